@@ -1,0 +1,22 @@
+"""fp64 CPU oracle for the per-owner Muon step (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP product path
+(``newton_schulz_06_amd``) never imports, links or calls it, and the two share
+no code: the only module both sides read is ``workloads`` (seeded synthetic
+inputs, none of the method's arithmetic).
+"""
+from .muon_ref import (  # noqa: F401
+    QUINTIC,
+    YOU_COEFFICIENTS,
+    DEFAULT_EPS,
+    coefficient_table,
+    momentum_update,
+    orient,
+    frobenius_normalize,
+    ns_iterate_left,
+    ns_iterate_right,
+    direct_newton_schulz,
+    muon_step,
+    round_to_bf16,
+)

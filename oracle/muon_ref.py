@@ -1,0 +1,199 @@
+"""Plain, slow, fp64 CPU oracle of the per-owner Muon step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this module;
+only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may use it.  It shares no code with the HIP library.
+
+What it computes, for each owned 2D matrix (sources are the DMuon
+documentation pages; readings of unstated points are marked READING):
+
+1. momentum (DMuon "API Reference", ``Muon``: the ``momentum`` argument and
+   the ``nesterov`` argument, whose lookahead input is the gradient plus
+   momentum times the buffer).
+   READING: the buffer recursion is ``buf <- mu*buf + g`` with no dampening,
+   and the Nesterov lookahead uses the buffer *after* this update.
+2. orientation (DMuon "API Reference", ``gram_newton_schulz_factors``:
+   NS acts on the normalized and possibly transposed view of G).
+   READING: transpose iff rows > cols; square matrices are not transposed.
+3. normalization (same section: the normalizer is the Frobenius norm of G
+   plus eps; ``direct_newton_schulz`` default eps = 1e-7).
+4. direct Newton-Schulz (DMuon "API Reference", ``direct_newton_schulz``:
+   X_{k+1} = a_k X + b_k (X X^T) X + c_k (X X^T)^2 X, one (a, b, c) per
+   step, the list length is the number of steps).
+   READING: the pages name but do not print the direct form's default
+   coefficients; the standard quintic (3.4445, -4.7750, 2.0315) is used at
+   every step.  YOU_COEFFICIENTS are printed on the same page and are the
+   second table used here.
+5. update (DMuon "HSDP Training (Multi-Node)", "What Happens Under the Hood":
+   the owner runs NS + momentum + weight decay + update; "API Reference",
+   ``Muon`` signature: lr=0.02, momentum=0.95, weight_decay=0.0).
+   READING: decoupled weight decay ``p <- p - lr*wd*p - lr*O`` on the
+   pre-update p, with no shape-dependent lr factor (none is printed).
+
+Every function works on numpy float64; inputs in float32 / bfloat16 are
+upcast exactly.  No blocking, fusion or reordering beyond the definitions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Standard quintic used when the pages leave the direct form's coefficients
+# unstated (READING above).
+QUINTIC = (3.4445, -4.7750, 2.0315)
+
+# DMuon "API Reference", YOU_COEFFICIENTS (5 per-step (a, b, c) triples).
+YOU_COEFFICIENTS = (
+    (4.0848, -6.8946, 2.927),
+    (3.9505, -6.3029, 2.6377),
+    (3.7418, -5.5913, 2.3037),
+    (2.8769, -3.1427, 1.2046),
+    (2.8366, -3.0525, 1.2012),
+)
+
+# DMuon "API Reference", direct_newton_schulz signature: eps=1e-07.
+DEFAULT_EPS = 1e-7
+
+
+def coefficient_table(coefficients=None, ns_steps: int = 5):
+    """Per-step (a, b, c) list.
+
+    DMuon "API Reference", ``direct_newton_schulz``: ``steps`` is used only
+    when no coefficient list is given; otherwise the list length is the step
+    count.  With no list, the quintic is repeated ``ns_steps`` times.
+    """
+    if coefficients is None:
+        return [tuple(float(v) for v in QUINTIC)] * int(ns_steps)
+    table = [tuple(float(v) for v in row) for row in coefficients]
+    for row in table:
+        if len(row) != 3:
+            raise ValueError("each coefficient row must be (a, b, c)")
+    return table
+
+
+def momentum_update(buf, grad, momentum: float, nesterov: bool):
+    """Momentum buffer update and NS input.
+
+    DMuon "API Reference", ``Muon`` › ``nesterov``: the NS input is
+    ``grad + mu * buf`` when Nesterov is on.  READING: ``buf`` is first
+    updated to ``mu*buf + grad``; without Nesterov the NS input is the
+    updated buffer itself.
+
+    Returns ``(new_buf, ns_input)`` in float64.
+    """
+    b = np.asarray(buf, dtype=np.float64)
+    g = np.asarray(grad, dtype=np.float64)
+    new_buf = momentum * b + g
+    if nesterov:
+        u = g + momentum * new_buf
+    else:
+        u = new_buf.copy()
+    return new_buf, u
+
+
+def orient(M):
+    """Return ``(X, transposed)``: X is M, or M^T when M has more rows than
+    columns (DMuon "API Reference", ``gram_newton_schulz_factors``: the
+    "possibly transposed view"; READING: transpose iff rows > cols)."""
+    M = np.asarray(M, dtype=np.float64)
+    if M.ndim != 2:
+        raise ValueError("Newton-Schulz needs a 2D matrix")
+    transposed = M.shape[0] > M.shape[1]
+    return (M.T if transposed else M), transposed
+
+
+def frobenius_normalize(X, eps: float = DEFAULT_EPS):
+    """X / (||X||_F + eps) (DMuon "API Reference",
+    ``gram_newton_schulz_factors`` › Returns: the normalizer is the norm of
+    G plus eps)."""
+    X = np.asarray(X, dtype=np.float64)
+    return X / (np.linalg.norm(X) + eps)
+
+
+def ns_iterate_left(X, coefficients):
+    """Direct NS on the oriented, normalized X (rows <= cols).
+
+    DMuon "API Reference", ``direct_newton_schulz``:
+    X <- a X + b (X X^T) X + c (X X^T)^2 X, written with A = X X^T and
+    B = b A + c A A as X <- a X + B X.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    for a, b, c in coefficients:
+        A = X @ X.T
+        B = b * A + c * (A @ A)
+        X = a * X + B @ X
+    return X
+
+
+def ns_iterate_right(X, coefficients):
+    """The same polynomial applied from the right:
+    X <- a X + X (b X^T X + c (X^T X)^2).
+
+    Equal to :func:`ns_iterate_left` in exact arithmetic (both are
+    a X + b X X^T X + c X X^T X X^T X); kept only so tests can check the
+    left form against an independent evaluation order.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    for a, b, c in coefficients:
+        S = X.T @ X
+        X = a * X + X @ (b * S + c * (S @ S))
+    return X
+
+
+def direct_newton_schulz(G, steps: int = 5, eps: float = DEFAULT_EPS,
+                         coefficients=None):
+    """Orthogonalize G: orient, normalize, iterate, undo the orientation.
+
+    DMuon "API Reference", ``direct_newton_schulz``: same shape as G.  The
+    result here is float64; callers round to their storage dtype.
+    """
+    table = coefficient_table(coefficients, steps)
+    X, transposed = orient(G)
+    X = frobenius_normalize(X, eps)
+    X = ns_iterate_left(X, table)
+    return X.T if transposed else X
+
+
+def muon_step(param, grad, buf, *, lr: float = 0.02, momentum: float = 0.95,
+              weight_decay: float = 0.0, nesterov: bool = True,
+              ns_steps: int = 5, coefficients=None, eps: float = DEFAULT_EPS):
+    """One Muon step on one owned matrix.
+
+    Momentum (see :func:`momentum_update`), NS of the momentum output
+    (:func:`direct_newton_schulz`), then the update
+    ``p <- p - lr*wd*p - lr*O`` (READING: decoupled weight decay on the
+    pre-update p, no shape factor).  Defaults follow the ``Muon`` signature
+    in DMuon "API Reference".
+
+    Returns ``(new_param, new_buf, O)``, all float64.
+    """
+    new_buf, u = momentum_update(buf, grad, momentum, nesterov)
+    O = direct_newton_schulz(u, steps=ns_steps, eps=eps,
+                             coefficients=coefficients)
+    p = np.asarray(param, dtype=np.float64)
+    new_param = p - lr * weight_decay * p - lr * O
+    return new_param, new_buf, O
+
+
+_BF16_DROP = 45  # fp64 keeps 52 explicit mantissa bits, bf16 keeps 7
+
+
+def round_to_bf16(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    Works on the float64 bit pattern (no detour through float32, so there is
+    no double rounding).  Valid for finite values inside bfloat16's normal
+    range; anything else raises, since no test here needs it.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.isfinite(x)
+    mag = np.abs(x)
+    if not finite.all():
+        raise ValueError("round_to_bf16: non-finite input")
+    nz = mag[mag != 0]
+    if nz.size and (nz.min() < 2.0 ** -126 or nz.max() >= 3.3e38):
+        raise ValueError("round_to_bf16: value outside bfloat16 normal range")
+    bits = x.view(np.uint64)
+    keep = (bits >> np.uint64(_BF16_DROP)) & np.uint64(1)
+    half = np.uint64((1 << (_BF16_DROP - 1)) - 1)
+    rounded = (bits + half + keep) & ~np.uint64((1 << _BF16_DROP) - 1)
+    return rounded.view(np.float64)
