@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-owner Muon step on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic
+gradients already resident in HBM: momentum (+ Nesterov), Newton-Schulz of
+every matrix (5 iterations of A = X X^T, B = bA + cA^2, X = aX + BX) and the
+lr-scaled update, all in libdmuon's HIP kernels.  The default workload is
+the 4-layer TinyMLP of DMuon's Quick Start (d=512, ff=2048: 12 matrices);
+``--config 3`` / ``--config 5`` run the Llama-8B projection and 70B-MLP
+batches, ``--config 4`` the 512-matrix NS-only batch.
+
+Prints ONE JSON line: NS TFLOP/s (algorithmic, symmetry-aware flops) as the
+value, ms per step, the dominant kernel's roofline (timed with HIP events
+on its stream inside the timed region) and the fp64 oracle's throughput on
+a bounded sample of the same workload on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Muon step ms & NS TFLOP/s (MFMA util %) per owned matrix batch, 1 GPU"
+# MI355X published dense MFMA peaks (TFLOP/s) and HBM3E bandwidth (GB/s).
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+GEMM_KINDS = ("syrk", "poly", "update_x")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def ns_flops(shapes, ns_steps):
+    """Algorithmic NS flops: per iteration p(p+1)q (upper-triangle X X^T),
+    p^2(p+1) (symmetric A A) and 2p^2q (B X)."""
+    tot = 0.0
+    for m, n in shapes:
+        p, q = float(min(m, n)), float(max(m, n))
+        tot += ns_steps * (p * (p + 1) * q + p * p * (p + 1) + 2 * p * p * q)
+    return tot
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the oracle's host timing (0 disables it)")
+    return ap.parse_args()
+
+
+def make_inputs(cfg, n_sets, device):
+    import torch
+    import workloads
+    from workloads.synth import powerlaw_basis_torch
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    shapes = cfg.shapes
+    params = [workloads.param_torch(m, n, cfg.cfg_id, i, device, dt[cfg.param_dtype])
+              for i, (m, n) in enumerate(shapes)]
+    bufs = [torch.zeros(m, n, dtype=torch.float32, device=device) for m, n in shapes]
+    bases = [None] * len(shapes)
+    if cfg.grad_kind == "powerlaw_t3":
+        for i, (m, n) in enumerate(shapes):
+            bases[i] = powerlaw_basis_torch(m, n, cfg.cfg_id, i, device)
+            log(f"basis {i + 1}/{len(shapes)} ready")
+    sets = []
+    for s in range(n_sets):
+        sets.append([workloads.grad_torch(cfg.grad_kind, m, n, cfg.cfg_id, s, i, device,
+                                          dt[cfg.grad_dtype], basis=bases[i])
+                     for i, (m, n) in enumerate(shapes)])
+        log(f"gradient set {s + 1}/{n_sets} ready")
+    del bases
+    torch.cuda.synchronize()
+    return params, bufs, sets
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in ("dmuon_kernels.hip", "dmuon_internal.h"):
+        with open(os.path.join(ROOT, "newton_schulz_06_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(kind, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    e = tab.get(f"{kind}@{workload}")
+    if not e or e.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, budget_s):
+    """The fp64 oracle as it stands, on the host, over the same recipe:
+    whole matrices of the workload in order until the budget is used."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()
+                       if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = None
+    flops = 0.0
+    done = []
+    t_total = 0.0
+    for i, (m, n) in enumerate(cfg.shapes):
+        g = workloads.grad_np(cfg.grad_kind, m, n, cfg.cfg_id, 0, i)
+        p = workloads.param_np(m, n, cfg.cfg_id, i)
+        buf = np.zeros((m, n))
+        t0 = time.perf_counter()
+        if cfg.ns_only:
+            oracle.direct_newton_schulz(g, steps=cfg.ns_steps)
+        else:
+            oracle.muon_step(p, g, buf, lr=cfg.lr, momentum=cfg.momentum,
+                             weight_decay=cfg.weight_decay, nesterov=cfg.nesterov,
+                             ns_steps=cfg.ns_steps)
+        t_total += time.perf_counter() - t0
+        flops += ns_flops([(m, n)], cfg.ns_steps)
+        done.append((m, n))
+        if t_total >= budget_s:
+            break
+    frac = len(done) / len(cfg.shapes)
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "NS TFLOP/s",
+        "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"{len(done)} of {len(cfg.shapes)} matrices of one step "
+                   f"({frac:.0%}), {t_total:.1f} s; numpy fp64 BLAS"),
+        "ms_per_step_estimate": t_total / frac * 1e3,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    import newton_schulz_06_amd as dm
+
+    cfg = workloads.CONFIGS[args.config]
+    steps = args.steps if args.steps is not None else (100 if args.config in (1, 2, 4) else 20)
+    warmup = args.warmup if args.warmup is not None else 10 if args.config in (1, 2, 4) else 3
+    device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
+    n_sets = 1 if cfg.ns_only else max(1, min(cfg.steps, steps + warmup))
+    log(f"config {cfg.cfg_id} ({cfg.name}): {len(cfg.shapes)} matrices, {n_sets} gradient sets")
+    params, bufs, sets = make_inputs(cfg, n_sets, device)
+    shapes = list(cfg.shapes)
+    flops_step = ns_flops(shapes, cfg.ns_steps)
+    arith = "f32" if cfg.ns_prec == "f32" else "bf16"
+
+    if cfg.ns_only:
+        outs = [torch.empty_like(g) for g in sets[0]]
+        call = dm.PreparedNs(sets[0], outs, ns_steps=cfg.ns_steps, prec=cfg.ns_prec)
+        run = lambda i: call()  # noqa: E731
+    else:
+        call = dm.PreparedMuonStep(params, bufs, sets, lr=cfg.lr, momentum=cfg.momentum,
+                                   weight_decay=cfg.weight_decay, nesterov=cfg.nesterov,
+                                   ns_steps=cfg.ns_steps, prec=cfg.ns_prec)
+        run = call
+
+    # Warm-up; the last warm-up step times every kernel kind once to find
+    # the dominant one.
+    for w in range(max(warmup - 1, 0)):
+        run(w % n_sets)
+    with dm.profile() as prof_all:
+        run((warmup - 1) % n_sets if warmup else 0)
+    torch.cuda.synchronize()
+    dominant = max(prof_all.rows, key=lambda k: prof_all.rows[k]["ms"])
+    log(f"warm-up done; per-kind ms of one step: "
+        + ", ".join(f"{k}={v['ms']:.3f}" for k, v in prof_all.rows.items())
+        + f"; dominant: {dominant}")
+
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with dm.profile(kinds=[dominant]) as prof:
+        e0.record(stream)
+        for s in range(steps):
+            run((warmup + s) % n_sets)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / steps
+    ns_tflops = flops_step / (ms_step * 1e-3) / 1e12
+    log(f"timed {steps} steps: {ms_step:.4f} ms/step (wall {wall * 1e3 / steps:.4f} ms/step), "
+        f"NS {ns_tflops:.1f} TFLOP/s")
+
+    row = prof.rows[dominant]
+    if dominant in GEMM_KINDS:
+        achieved = row["flops"] / row["ms"] / 1e9
+        peak = PEAK_TFLOPS[arith]
+        roof = {"bound": "mfma", "unit": "TFLOP/s"}
+    else:
+        achieved = row["bytes"] / row["ms"] / 1e6
+        peak = PEAK_HBM_GBS
+        roof = {"bound": "hbm", "unit": "GB/s"}
+    roof.update({"kernel": dominant, "achieved": round(achieved, 2), "peak": peak,
+                 "frac": round(achieved / peak, 4),
+                 "avg_launch_ms": round(row["ms"] / row["launches"], 5),
+                 "launches": row["launches"],
+                 "traffic": traffic_for(dominant, cfg.name)})
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the fp64 oracle on the host")
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(ns_tflops, 3),
+        "unit": "NS TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": arith,
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "matrices": len(shapes),
+            "shapes": sorted({f"{m}x{n}" for m, n in shapes}) if len(shapes) <= 32 else "512 small",
+            "ns_steps": cfg.ns_steps,
+            "ns_precision": cfg.ns_prec,
+            "param_dtype": cfg.param_dtype,
+            "grad_dtype": cfg.grad_dtype,
+            "nesterov": cfg.nesterov,
+            "ns_only": cfg.ns_only,
+            "gradients": cfg.grad_kind,
+            "parallelism": "1 GPU (owner-local batch)",
+        },
+        "ns_tflop_per_step": round(flops_step / 1e12, 6),
+        "ns_mfma_frac": round(ns_tflops / PEAK_TFLOPS[arith], 4),
+        "matrices_per_s": round(len(shapes) / (ms_step * 1e-3), 1),
+        "kernel_ms_one_step": {k: round(v["ms"], 4) for k, v in prof_all.rows.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * dmuon.h - C ABI of the MI355X (gfx950) per-owner Muon optimizer step.
+ *
+ * The library runs, on one GPU and batched over many owned 2D matrices, the
+ * part of DMuon's Muon optimizer that the owner rank executes (DMuon
+ * "HSDP Training (Multi-Node)", "What Happens Under the Hood": only the
+ * owner runs momentum, Newton-Schulz, weight decay and the update on the
+ * parameters it owns; DMuon "API Reference", Muon.step: momentum + NS +
+ * update on owned dedicated params).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Matrices are dense, row-major, leading dimension == n (no stride
+ *   argument).  Pointers are device pointers on the current HIP device,
+ *   aligned at least to their element size.
+ * - The caller owns every buffer (params, grads, momentum buffers, outputs,
+ *   workspace).  The library keeps no pointer after the enqueued work ends,
+ *   except a small per-device cache of launch tables keyed by the shapes and
+ *   pointers of a call (allocated on the first call with a new key, reused
+ *   afterwards).
+ * - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *   the default stream).  The workspace must stay alive until that work
+ *   completes.
+ * - Validation is synchronous and happens before anything is enqueued: on
+ *   any error no buffer is touched.  Errors are reported as a status code
+ *   plus a thread-local message (dmuon_last_error).  No C++ exception
+ *   crosses the ABI.  Faults inside kernels surface at the caller's next
+ *   synchronization, or as DMUON_E_HIP from a later call.
+ * - NaN and Inf propagate; nothing is clamped.  Results are bitwise
+ *   reproducible run to run for the same inputs (fixed reduction orders, no
+ *   floating-point atomics).
+ * - count == 0 is a valid no-op.
+ */
+#ifndef DMUON_H
+#define DMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DMUON_OK = 0,
+  DMUON_E_INVALID = 1,     /* bad argument (shape, dtype, pointer, alias) */
+  DMUON_E_UNSUPPORTED = 2, /* well-formed but outside the supported range */
+  DMUON_E_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
+  DMUON_E_HIP = 4          /* HIP runtime error while enqueueing */
+} dmuon_status_t;
+
+/* Element types of caller buffers. */
+typedef enum { DMUON_F32 = 0, DMUON_BF16 = 1 } dmuon_dtype_t;
+
+/*
+ * Newton-Schulz arithmetic.
+ *   DMUON_NS_F32        fp32 operands on fp32 MFMA, fp32 accumulate.
+ *   DMUON_NS_BF16       fp32 master copy of X; bf16 copies of X, A = X X^T
+ *                       and B = bA + cA^2 as MFMA operands; fp32 accumulate
+ *                       and fp32 epilogues.
+ *   DMUON_NS_BF16_SPLIT as DMUON_NS_BF16, with A and B carried as a bf16
+ *                       hi + lo pair (A^2 from three products, B X from
+ *                       two) for small or skinny matrices.
+ *   DMUON_NS_AUTO       per matrix: BF16_SPLIT when min(m, n) <= 1024,
+ *                       else BF16.
+ */
+typedef enum {
+  DMUON_NS_F32 = 0,
+  DMUON_NS_BF16 = 1,
+  DMUON_NS_BF16_SPLIT = 2,
+  DMUON_NS_AUTO = 3
+} dmuon_prec_t;
+
+/* One matrix: m rows, n columns, row-major, device pointer. */
+typedef struct {
+  int64_t m;
+  int64_t n;
+  void* ptr;
+} dmuon_mat_t;
+
+/* A batch of matrices of one element type; `mats` is a host array. */
+typedef struct {
+  const dmuon_mat_t* mats;
+  int32_t count;
+  int32_t dtype; /* dmuon_dtype_t */
+} dmuon_batch_t;
+
+/*
+ * Newton-Schulz configuration (DMuon "API Reference", direct_newton_schulz:
+ * per-step (a, b, c) coefficients whose list length is the number of
+ * iterations; eps is added to the Frobenius norm used to normalize).
+ *   coeffs    host array of 3 * ns_steps floats (a0, b0, c0, a1, ...), or
+ *             NULL for (3.4445, -4.7750, 2.0315) at every step.
+ *   ns_steps  1..16.
+ *   eps       >= 0 and finite (1e-7 in DMuon's signature).
+ *   prec      dmuon_prec_t.
+ */
+typedef struct {
+  const float* coeffs;
+  int32_t ns_steps;
+  float eps;
+  int32_t prec;
+} dmuon_ns_cfg_t;
+
+/*
+ * Workspace bytes needed by dmuon_ns_orthogonalize / dmuon_muon_step for a
+ * batch of these shapes.  Only the shapes, count and cfg->prec matter (the
+ * pointers of `g` are not read; they may be NULL).  Pure host computation.
+ */
+dmuon_status_t dmuon_ns_workspace_size(const dmuon_batch_t* g,
+                                       const dmuon_ns_cfg_t* cfg,
+                                       size_t* bytes);
+
+/*
+ * out[i] = NS(g[i]) for every matrix of the batch (DMuon "API Reference",
+ * direct_newton_schulz: G is transposed when it has more rows than columns,
+ * normalized by ||G||_F + eps, then X <- a X + b (X X^T) X + c (X X^T)^2 X
+ * per coefficient row; the result has G's shape and dtype).
+ *   g, out    same count, same shapes, same dtype.  out[i] may be exactly
+ *             g[i] (in place); any other overlap is rejected.
+ *   ws        device workspace of at least dmuon_ns_workspace_size bytes,
+ *             256-byte aligned.  Its contents on entry are ignored.
+ */
+dmuon_status_t dmuon_ns_orthogonalize(const dmuon_batch_t* g,
+                                      const dmuon_batch_t* out,
+                                      const dmuon_ns_cfg_t* cfg,
+                                      void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/*
+ * One Muon step on every owned matrix of the batch (DMuon "API Reference",
+ * Muon: lr, momentum, weight_decay, ns_steps, nesterov; the nesterov
+ * argument's lookahead feeds grad + momentum * buf to Newton-Schulz):
+ *   buf <- momentum * buf + grad
+ *   u   <- grad + momentum * buf      if nesterov, else buf
+ *   O   <- NS(u)                      as in dmuon_ns_orthogonalize
+ *   p   <- p - lr * weight_decay * p - lr * O
+ * params: F32 or BF16, updated in place (the new value is rounded to the
+ * param dtype, round-to-nearest-even).  grads: F32 or BF16, read only.
+ * bufs: F32, updated in place.  The three batches have the same count and
+ * per-index shapes; no two of the buffers overlap.
+ */
+dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params,
+                               const dmuon_batch_t* grads,
+                               const dmuon_batch_t* bufs,
+                               const dmuon_ns_cfg_t* cfg,
+                               float momentum, float lr, float weight_decay,
+                               int32_t nesterov,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Static string for a status code. */
+const char* dmuon_status_str(dmuon_status_t status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* dmuon_last_error(void);
+
+/* One-line description of the compiled kernels (cf. DMuon "API Reference",
+ * get_ns_backend: a one-line summary of the active NS kernel). */
+const char* dmuon_backend_info(void);
+
+/*
+ * Per-kernel timing (cf. DMuon "API Reference", Muon: record_step_profile
+ * records event timings of the optimizer phases).  Between
+ * dmuon_profile_begin(mask) and dmuon_profile_end(), every launch of a
+ * kernel kind selected by `mask` (bit k selects kind k of the list below;
+ * 0 selects all) made by this thread is bracketed by HIP events on the
+ * stream it is launched on.  dmuon_profile_end synchronizes those events and
+ * fills up to `max` rows of `out` (one per kind that ran), returning the
+ * number of rows, or -1 on error.  `flops` and `bytes` are the algorithmic
+ * work of those launches: symmetric-aware flops of the NS products
+ * (p(p+1)q for A = X X^T, p^2(p+1) for A A, 2p^2q for B X); for the
+ * element-wise kernels, the bytes the step must move at minimum.
+ * Kinds: 0 momentum, 1 input, 2 norm, 3 syrk, 4 poly, 5 update_x,
+ *        6 update_p, 7 output.
+ */
+typedef struct {
+  char name[24];
+  int32_t kind;
+  int32_t launches;
+  double ms;     /* summed event time over the launches */
+  double flops;  /* summed algorithmic flops */
+  double bytes;  /* summed algorithmic HBM bytes */
+} dmuon_profile_row_t;
+
+int32_t dmuon_profile_begin(uint32_t kind_mask);
+int32_t dmuon_profile_end(dmuon_profile_row_t* out, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMUON_H */

@@ -1,0 +1,306 @@
+"""Python binding of libdmuon, the MI355X (gfx950) per-owner Muon step.
+
+Argument marshalling only: the names mirror the C ABI in include/dmuon.h
+and every step of the computation runs in the library's HIP kernels.  There
+is no CPU fallback; if libdmuon.so is missing, the first call fails loudly.
+PyTorch is used for device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdmuon.so")
+
+DMUON_OK, DMUON_E_INVALID, DMUON_E_UNSUPPORTED, DMUON_E_WORKSPACE, DMUON_E_HIP = range(5)
+DMUON_F32, DMUON_BF16 = 0, 1
+PREC = {"f32": 0, "bf16": 1, "bf16_split": 2, "auto": 3}
+
+# Quintic used when no coefficient list is given.
+QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+class DmuonError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"dmuon status {status}: {message}")
+        self.status = status
+
+
+class DmuonValueError(DmuonError, ValueError):
+    pass
+
+
+class Mat(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("ptr", ctypes.c_void_p)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("mats", ctypes.POINTER(Mat)), ("count", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class NsCfg(ctypes.Structure):
+    _fields_ = [("coeffs", ctypes.POINTER(ctypes.c_float)), ("ns_steps", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("prec", ctypes.c_int32)]
+
+
+class ProfileRow(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 24), ("kind", ctypes.c_int32),
+                ("launches", ctypes.c_int32),
+                ("ms", ctypes.c_double), ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+
+
+EXPORTS = ("dmuon_ns_workspace_size", "dmuon_ns_orthogonalize", "dmuon_muon_step",
+           "dmuon_status_str", "dmuon_last_error", "dmuon_backend_info",
+           "dmuon_profile_begin", "dmuon_profile_end")
+
+_lib = None
+
+
+def lib():
+    """Loads libdmuon.so (built in-tree by newton_schulz_06_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m newton_schulz_06_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    st = ctypes.c_int
+    L.dmuon_ns_workspace_size.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(NsCfg),
+                                          ctypes.POINTER(ctypes.c_size_t)]
+    L.dmuon_ns_workspace_size.restype = st
+    L.dmuon_ns_orthogonalize.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(Batch),
+                                         ctypes.POINTER(NsCfg), ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]
+    L.dmuon_ns_orthogonalize.restype = st
+    L.dmuon_muon_step.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(Batch),
+                                  ctypes.POINTER(Batch), ctypes.POINTER(NsCfg),
+                                  ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]
+    L.dmuon_muon_step.restype = st
+    L.dmuon_status_str.argtypes = [ctypes.c_int]
+    L.dmuon_status_str.restype = ctypes.c_char_p
+    L.dmuon_last_error.argtypes = []
+    L.dmuon_last_error.restype = ctypes.c_char_p
+    L.dmuon_backend_info.argtypes = []
+    L.dmuon_backend_info.restype = ctypes.c_char_p
+    L.dmuon_profile_begin.argtypes = [ctypes.c_uint32]
+    L.dmuon_profile_begin.restype = ctypes.c_int32
+    L.dmuon_profile_end.argtypes = [ctypes.POINTER(ProfileRow), ctypes.c_int32]
+    L.dmuon_profile_end.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status == DMUON_OK:
+        return
+    msg = lib().dmuon_last_error().decode()
+    if status == DMUON_E_INVALID:
+        raise DmuonValueError(status, msg)
+    raise DmuonError(status, msg)
+
+
+# ------------------------------------------------------------ marshalling --
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return DMUON_F32
+    if t.dtype == torch.bfloat16:
+        return DMUON_BF16
+    raise DmuonValueError(DMUON_E_INVALID, f"unsupported dtype {t.dtype}")
+
+
+def make_batch(tensors):
+    """Batch descriptor over 2D contiguous device tensors of one dtype.
+    Returns (Batch, keepalive)."""
+    tensors = list(tensors)
+    arr = (Mat * max(1, len(tensors)))()
+    code = DMUON_F32
+    for i, t in enumerate(tensors):
+        if t.dim() != 2:
+            raise DmuonValueError(DMUON_E_INVALID, "every matrix must be 2D")
+        if not t.is_contiguous():
+            raise DmuonValueError(DMUON_E_INVALID, "every matrix must be contiguous")
+        c = _dtype_code(t)
+        if i == 0:
+            code = c
+        elif c != code:
+            raise DmuonValueError(DMUON_E_INVALID, "a batch holds one dtype")
+        arr[i] = Mat(int(t.shape[0]), int(t.shape[1]), int(t.data_ptr()))
+    return Batch(arr, len(tensors), code), arr
+
+
+def shape_batch(shapes, dtype=DMUON_BF16):
+    arr = (Mat * max(1, len(shapes)))()
+    for i, (m, n) in enumerate(shapes):
+        arr[i] = Mat(int(m), int(n), None)
+    return Batch(arr, len(shapes), dtype), arr
+
+
+def make_cfg(coefficients=None, ns_steps=5, eps=1e-7, prec="bf16"):
+    if isinstance(prec, str):
+        prec = PREC[prec]
+    keep = None
+    ptr = None
+    if coefficients is not None:
+        flat = [float(v) for row in coefficients for v in row]
+        if len(flat) != 3 * len(coefficients):
+            raise DmuonValueError(DMUON_E_INVALID, "coefficient rows must be (a, b, c)")
+        ns_steps = len(coefficients)
+        keep = (ctypes.c_float * len(flat))(*flat)
+        ptr = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
+    return NsCfg(ptr, int(ns_steps), float(eps), int(prec)), keep
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+# ------------------------------------------------------------------- API --
+
+def backend_info() -> str:
+    return lib().dmuon_backend_info().decode()
+
+
+def workspace_size(shapes, prec="bf16") -> int:
+    """dmuon_ns_workspace_size for a list of (m, n) shapes."""
+    b, keep = shape_batch(shapes)
+    cfg, ck = make_cfg(prec=prec)
+    out = ctypes.c_size_t(0)
+    _check(lib().dmuon_ns_workspace_size(ctypes.byref(b), ctypes.byref(cfg), ctypes.byref(out)))
+    return int(out.value)
+
+
+def alloc_workspace(shapes, prec="bf16", device="cuda"):
+    """Device workspace (a torch uint8 tensor) big enough for these shapes."""
+    import torch
+    return torch.empty(max(1, workspace_size(shapes, prec)), dtype=torch.uint8, device=device)
+
+
+def _ws(workspace, shapes, prec, device):
+    if workspace is None:
+        workspace = alloc_workspace(shapes, prec, device)
+    return workspace, ctypes.c_void_p(int(workspace.data_ptr())), int(workspace.numel())
+
+
+def ns_orthogonalize(gs, outs=None, *, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
+                     workspace=None, stream=None):
+    """dmuon_ns_orthogonalize: outs[i] = NS(gs[i]) in gs[i]'s dtype.
+    `outs` defaults to new tensors; passing `outs=gs` works in place."""
+    import torch
+    gs = list(gs)
+    if outs is None:
+        outs = [torch.empty_like(g) for g in gs]
+    outs = list(outs)
+    bg, kg = make_batch(gs)
+    bo, ko = make_batch(outs)
+    cfg, kc = make_cfg(coefficients, ns_steps, eps, prec)
+    device = gs[0].device if gs else "cuda"
+    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in gs], prec, device)
+    _check(lib().dmuon_ns_orthogonalize(ctypes.byref(bg), ctypes.byref(bo), ctypes.byref(cfg),
+                                        wptr, wbytes, _stream_handle(stream)))
+    return outs
+
+
+def muon_step(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_decay=0.0, nesterov=True,
+              coefficients=None, ns_steps=5, eps=1e-7, prec="bf16", workspace=None,
+              stream=None):
+    """dmuon_muon_step: in-place update of `params` and `bufs` (defaults as
+    in DMuon's Muon signature)."""
+    params, grads, bufs = list(params), list(grads), list(bufs)
+    bp, kp = make_batch(params)
+    bg, kg = make_batch(grads)
+    bb, kb = make_batch(bufs)
+    cfg, kc = make_cfg(coefficients, ns_steps, eps, prec)
+    device = grads[0].device if grads else "cuda"
+    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in grads], prec, device)
+    _check(lib().dmuon_muon_step(ctypes.byref(bp), ctypes.byref(bg), ctypes.byref(bb),
+                                 ctypes.byref(cfg), float(momentum), float(lr),
+                                 float(weight_decay), int(bool(nesterov)), wptr, wbytes,
+                                 _stream_handle(stream)))
+
+
+KINDS = ("momentum", "input", "norm", "syrk", "poly", "update_x", "update_p", "output")
+
+
+class profile:
+    """Context manager around dmuon_profile_begin / dmuon_profile_end.
+    ``kinds``: kernel names to time (default all).  After exit, ``rows``
+    maps kernel name -> dict(launches, ms, flops, bytes)."""
+
+    def __init__(self, kinds=None):
+        self.mask = 0
+        for k in kinds or ():
+            self.mask |= 1 << KINDS.index(k)
+
+    def __enter__(self):
+        self.rows = {}
+        lib().dmuon_profile_begin(self.mask)
+        return self
+
+    def __exit__(self, *exc):
+        out = (ProfileRow * 16)()
+        n = lib().dmuon_profile_end(out, 16)
+        if n < 0:
+            _check(DMUON_E_HIP)
+        for r in out[:n]:
+            self.rows[r.name.decode()] = dict(launches=r.launches, ms=r.ms, flops=r.flops,
+                                              bytes=r.bytes)
+        return False
+
+
+class PreparedMuonStep:
+    """dmuon_muon_step with the descriptors marshalled once, for repeated
+    calls on fixed buffers (one gradient batch per call, chosen by index)."""
+
+    def __init__(self, params, bufs, grad_sets, *, lr=0.02, momentum=0.95, weight_decay=0.0,
+                 nesterov=True, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
+                 workspace=None, stream=None):
+        self._keep = []
+        self.bp, k = make_batch(params); self._keep.append(k)
+        self.bb, k = make_batch(bufs); self._keep.append(k)
+        self.bgs = []
+        for gs in grad_sets:
+            b, k = make_batch(gs)
+            self.bgs.append(b)
+            self._keep.append(k)
+        self.cfg, k = make_cfg(coefficients, ns_steps, eps, prec); self._keep.append(k)
+        shapes = [tuple(p.shape) for p in params]
+        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, params[0].device)
+        self.stream = _stream_handle(stream)
+        self.scalars = (ctypes.c_float(momentum), ctypes.c_float(lr),
+                        ctypes.c_float(weight_decay), ctypes.c_int32(int(bool(nesterov))))
+        self.fn = lib().dmuon_muon_step
+
+    def __call__(self, i=0):
+        st = self.fn(ctypes.byref(self.bp), ctypes.byref(self.bgs[i]), ctypes.byref(self.bb),
+                     ctypes.byref(self.cfg), *self.scalars, self.wptr, self.wbytes, self.stream)
+        if st:
+            _check(st)
+
+
+class PreparedNs:
+    """dmuon_ns_orthogonalize with the descriptors marshalled once."""
+
+    def __init__(self, gs, outs, *, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
+                 workspace=None, stream=None):
+        self.bg, self._kg = make_batch(gs)
+        self.bo, self._ko = make_batch(outs)
+        self.cfg, self._kc = make_cfg(coefficients, ns_steps, eps, prec)
+        shapes = [tuple(g.shape) for g in gs]
+        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, gs[0].device)
+        self.stream = _stream_handle(stream)
+        self.fn = lib().dmuon_ns_orthogonalize
+
+    def __call__(self):
+        st = self.fn(ctypes.byref(self.bg), ctypes.byref(self.bo), ctypes.byref(self.cfg),
+                     self.wptr, self.wbytes, self.stream)
+        if st:
+            _check(st)

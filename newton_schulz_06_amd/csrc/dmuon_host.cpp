@@ -1,0 +1,707 @@
+// Host runtime of the C ABI declared in include/dmuon.h: argument
+// validation, workspace layout, per-device launch-table cache, the launch
+// sequence of one Muon step / one NS call, and optional event timing.
+#include "dmuon.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dmuon_internal.h"
+
+using namespace dmuon;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dmuon_status_t fail(dmuon_status_t st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+constexpr int kMaxSteps = 16;
+constexpr int64_t kMaxSide = int64_t(1) << 20;
+constexpr size_t kWsAlign = 256;
+constexpr int kSmallTile = 64;
+constexpr int kLargeTile = 128;
+// Matrices with min side up to this many rows use the 64-wide tile class.
+constexpr int kSmallTileMaxP = 512;
+// DMUON_NS_AUTO uses hi/lo split operands up to this min side: plain bf16
+// operands put iid-noise-like spectra of narrow matrices (e.g. 2048 x 512)
+// just past a 2e-2 relative error, while wider ones stay near 1e-2.
+constexpr int kAutoSplitMaxP = 1024;
+constexpr float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+size_t esize(int dtype) { return dtype == DMUON_F32 ? 4 : 2; }
+
+// Shape-derived geometry of one matrix in the workspace.
+struct Geom {
+  int64_t m, n, p, q, P, Q;
+  int tile, transposed, split;
+  size_t xm, xb, xt0, xt1, a32, aop, r3, bop;  // byte offsets in ws
+};
+
+struct Layout {
+  std::vector<Geom> g;
+  size_t partial_off = 0, scale_off = 0, total = 0;
+  int64_t in_tiles = 0;
+  int f32_ops = 0;
+};
+
+dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
+  Layout L;
+  L.f32_ops = (prec == DMUON_NS_F32);
+  const int n = b->count;
+  L.g.resize(n);
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    Geom& G = L.g[i];
+    G.m = b->mats[i].m;
+    G.n = b->mats[i].n;
+    G.transposed = G.m > G.n;
+    G.p = std::min(G.m, G.n);
+    G.q = std::max(G.m, G.n);
+    G.tile = G.p <= kSmallTileMaxP ? kSmallTile : kLargeTile;
+    G.P = round_up(G.p, G.tile);
+    G.Q = round_up(G.q, G.tile);
+    if (G.P * G.Q > INT32_MAX || G.Q * 3 > INT32_MAX)
+      return fail(DMUON_E_UNSUPPORTED, "matrix " + std::to_string(i) +
+                                           ": padded size exceeds 2^31 elements");
+    G.split = (prec == DMUON_NS_BF16_SPLIT) ||
+              (prec == DMUON_NS_AUTO && G.p <= kAutoSplitMaxP);
+    tiles += (G.P / EW_TILE) * (G.Q / EW_TILE);
+  }
+  if (tiles > INT32_MAX) return fail(DMUON_E_UNSUPPORTED, "batch too large (tile count)");
+  L.in_tiles = tiles;
+  size_t off = 0;
+  L.partial_off = off;
+  off = align_up(off + sizeof(float) * (size_t)tiles, kWsAlign);
+  L.scale_off = off;
+  off = align_up(off + sizeof(float) * 4 * (size_t)n, kWsAlign);
+  const size_t e = L.f32_ops ? 4 : 2;
+  for (int i = 0; i < n; ++i) {
+    Geom& G = L.g[i];
+    const size_t PQ = (size_t)G.P * G.Q, PP = (size_t)G.P * G.P;
+    auto take = [&](size_t bytes) {
+      const size_t o = off;
+      off = align_up(off + bytes, kWsAlign);
+      return o;
+    };
+    G.xm = take(4 * PQ);
+    G.xb = L.f32_ops ? 0 : take(2 * PQ);
+    G.xt0 = take(e * PQ);
+    G.xt1 = take(e * PQ);
+    G.a32 = take(4 * PP);
+    if (L.f32_ops) {
+      G.aop = G.a32;
+      G.r3 = 0;
+      G.bop = take(4 * PP);
+    } else if (G.split) {
+      G.aop = take(2 * 3 * PP);
+      G.r3 = take(2 * 3 * PP);
+      G.bop = take(2 * 2 * PP);
+    } else {
+      G.aop = take(2 * PP);
+      G.r3 = 0;
+      G.bop = take(2 * PP);
+    }
+  }
+  L.total = off;
+  *out = std::move(L);
+  return DMUON_OK;
+}
+
+// ------------------------------------------------------------ validation --
+
+dmuon_status_t check_batch(const dmuon_batch_t* b, const char* name, bool need_ptrs) {
+  if (!b) return fail(DMUON_E_INVALID, std::string(name) + ": null batch");
+  if (b->count < 0) return fail(DMUON_E_INVALID, std::string(name) + ": negative count");
+  if (b->count > 0 && !b->mats) return fail(DMUON_E_INVALID, std::string(name) + ": null mats");
+  if (b->dtype != DMUON_F32 && b->dtype != DMUON_BF16)
+    return fail(DMUON_E_INVALID, std::string(name) + ": unknown dtype");
+  for (int i = 0; i < b->count; ++i) {
+    const dmuon_mat_t& M = b->mats[i];
+    const std::string where = std::string(name) + "[" + std::to_string(i) + "]";
+    if (M.m < 1 || M.n < 1) return fail(DMUON_E_INVALID, where + ": empty or negative shape");
+    if (M.m > kMaxSide || M.n > kMaxSide)
+      return fail(DMUON_E_UNSUPPORTED, where + ": side longer than 2^20");
+    if (need_ptrs) {
+      if (!M.ptr) return fail(DMUON_E_INVALID, where + ": null pointer");
+      if (reinterpret_cast<uintptr_t>(M.ptr) % esize(b->dtype))
+        return fail(DMUON_E_INVALID, where + ": pointer not aligned to its element size");
+    }
+  }
+  return DMUON_OK;
+}
+
+dmuon_status_t check_cfg(const dmuon_ns_cfg_t* cfg) {
+  if (!cfg) return fail(DMUON_E_INVALID, "cfg: null");
+  if (cfg->ns_steps < 1 || cfg->ns_steps > kMaxSteps)
+    return fail(DMUON_E_INVALID, "cfg: ns_steps must be in [1, 16]");
+  if (!std::isfinite(cfg->eps) || cfg->eps < 0.f)
+    return fail(DMUON_E_INVALID, "cfg: eps must be finite and >= 0");
+  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_AUTO)
+    return fail(DMUON_E_INVALID, "cfg: unknown precision mode");
+  if (cfg->coeffs)
+    for (int i = 0; i < 3 * cfg->ns_steps; ++i)
+      if (!std::isfinite(cfg->coeffs[i]))
+        return fail(DMUON_E_INVALID, "cfg: non-finite coefficient");
+  return DMUON_OK;
+}
+
+dmuon_status_t same_shapes(const dmuon_batch_t* a, const dmuon_batch_t* b, const char* an,
+                           const char* bn) {
+  if (a->count != b->count)
+    return fail(DMUON_E_INVALID, std::string(an) + " and " + bn + ": counts differ");
+  for (int i = 0; i < a->count; ++i)
+    if (a->mats[i].m != b->mats[i].m || a->mats[i].n != b->mats[i].n)
+      return fail(DMUON_E_INVALID, std::string(an) + " and " + bn + ": shapes differ at index " +
+                                       std::to_string(i));
+  return DMUON_OK;
+}
+
+struct Span {
+  uintptr_t lo, hi;
+  int group, index;
+};
+
+// No two spans may overlap.
+dmuon_status_t check_disjoint(std::vector<Span> v, const char* const* names) {
+  std::sort(v.begin(), v.end(), [](const Span& x, const Span& y) { return x.lo < y.lo; });
+  size_t far = 0;  // span with the largest end so far
+  for (size_t i = 1; i < v.size(); ++i) {
+    if (v[i].lo < v[far].hi) {
+      char buf[160];
+      std::snprintf(buf, sizeof buf, "%s[%d] overlaps %s[%d]", names[v[i].group], v[i].index,
+                    names[v[far].group], v[far].index);
+      return fail(DMUON_E_INVALID, buf);
+    }
+    if (v[i].hi > v[far].hi) far = i;
+  }
+  return DMUON_OK;
+}
+
+void add_spans(std::vector<Span>& v, const dmuon_batch_t* b, int group) {
+  for (int i = 0; i < b->count; ++i) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(b->mats[i].ptr);
+    v.push_back({lo, lo + (uintptr_t)(b->mats[i].m * b->mats[i].n * esize(b->dtype)), group, i});
+  }
+}
+
+// ----------------------------------------------------------------- plans --
+
+struct GemmLaunch {
+  int kind, tile;
+  size_t off;  // byte offset of the task array in the device table
+  int ntasks, total;
+  double flops;
+};
+
+struct Plan {
+  std::vector<int64_t> key;
+  int device = -1;
+  void* dtab = nullptr;
+  int f32_ops = 0;
+  size_t in_off = 0, norm_off = 0, out_off = 0;
+  int nmat = 0, in_tiles = 0, out_tiles = 0;
+  double in_bytes = 0, out_bytes = 0, norm_bytes = 0;
+  std::vector<GemmLaunch> gemms;  // SYRK launches, then POLY, then UPDX
+  ~Plan() {
+    if (dtab) {
+      int cur = -1;
+      (void)hipGetDevice(&cur);
+      (void)hipSetDevice(device);
+      (void)hipDeviceSynchronize();
+      (void)hipFree(dtab);
+      (void)hipSetDevice(cur);
+    }
+  }
+};
+
+std::mutex g_plan_mu;
+// Most recently used last.  Never destroyed: freeing device memory from a
+// static destructor could run after the HIP runtime has shut down.
+std::vector<std::unique_ptr<Plan>>& g_plans = *new std::vector<std::unique_ptr<Plan>>();
+constexpr size_t kMaxPlans = 32;
+
+bool vec_ok(const void* p, int dtype, int64_t n) {
+  const size_t need = dtype == DMUON_F32 ? 16 : 8;
+  return p && reinterpret_cast<uintptr_t>(p) % need == 0 && n % 4 == 0;
+}
+
+// Builds the launch tables for one call shape and uploads them.
+dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_batch_t* dst,
+                          const dmuon_batch_t* bufs, bool ns_only, char* ws, int device,
+                          std::vector<int64_t> key, Plan** out) {
+  auto plan = std::make_unique<Plan>();
+  plan->key = std::move(key);
+  plan->device = device;
+  plan->f32_ops = L.f32_ops;
+  const int n = src->count;
+  plan->nmat = n;
+  float* partial = reinterpret_cast<float*>(ws + L.partial_off);
+  float* scale = reinterpret_cast<float*>(ws + L.scale_off);
+
+  std::vector<EwTask> tin(n), tout(n);
+  std::vector<NormTask> tnorm(n);
+  int in_begin = 0, out_begin = 0;
+  for (int i = 0; i < n; ++i) {
+    const Geom& G = L.g[i];
+    EwTask t{};
+    t.m = (int32_t)G.m;
+    t.n = (int32_t)G.n;
+    t.transposed = G.transposed;
+    t.in_dtype = src->dtype;
+    t.out_dtype = dst->dtype;
+    t.ldx = (int32_t)G.Q;
+    t.ldt = (int32_t)G.P;
+    t.f32_ops = L.f32_ops;
+    t.src = src->mats[i].ptr;
+    t.buf = bufs ? static_cast<float*>(bufs->mats[i].ptr) : nullptr;
+    t.dst = dst->mats[i].ptr;
+    t.xm = reinterpret_cast<float*>(ws + G.xm);
+    t.xb = L.f32_ops ? nullptr : reinterpret_cast<uint16_t*>(ws + G.xb);
+    t.xt = ws + G.xt0;
+    t.partial = partial;
+    t.scale = scale + 4 * i;
+    // input pass: padded oriented extents, mapped to the caller's layout
+    EwTask a = t;
+    a.rows = (int32_t)(G.transposed ? G.Q : G.P);
+    a.cols = (int32_t)(G.transposed ? G.P : G.Q);
+    a.tiles_c = a.cols / EW_TILE;
+    a.tile_begin = in_begin;
+    a.tile_count = (a.rows / EW_TILE) * a.tiles_c;
+    a.vec = vec_ok(t.src, src->dtype, G.n) && (!bufs || vec_ok(t.buf, DMUON_F32, G.n));
+    in_begin += a.tile_count;
+    tin[i] = a;
+    tnorm[i] = NormTask{a.tile_begin, a.tile_count, partial, scale + 4 * i};
+    // output pass: the caller's extents
+    EwTask o = t;
+    o.rows = (int32_t)G.m;
+    o.cols = (int32_t)G.n;
+    o.tiles_c = (int32_t)((G.n + EW_TILE - 1) / EW_TILE);
+    o.tile_begin = out_begin;
+    o.tile_count = (int32_t)((G.m + EW_TILE - 1) / EW_TILE) * o.tiles_c;
+    o.vec = vec_ok(t.dst, dst->dtype, G.n);
+    out_begin += o.tile_count;
+    tout[i] = o;
+    const double mn = (double)G.m * (double)G.n;
+    if (ns_only) {
+      plan->in_bytes += mn * esize(src->dtype);
+      plan->out_bytes += mn * esize(dst->dtype);
+    } else {
+      plan->in_bytes += mn * (esize(src->dtype) + 8.0);
+      plan->out_bytes += mn * 2.0 * esize(dst->dtype);
+    }
+    plan->norm_bytes += 4.0 * a.tile_count;
+  }
+  plan->in_tiles = in_begin;
+  plan->out_tiles = out_begin;
+
+  // GEMM tasks, grouped by (kind, tile class).
+  std::vector<GemmTask> gtasks;
+  const int kinds[3] = {KIND_SYRK, KIND_POLY, KIND_UPDX};
+  const int tiles[2] = {kSmallTile, kLargeTile};
+  std::vector<std::pair<size_t, size_t>> ranges;  // [begin, end) in gtasks per launch
+  for (int kind : kinds) {
+    for (int tile : tiles) {
+      const size_t begin = gtasks.size();
+      int acc = 0;
+      double flops = 0;
+      for (int i = 0; i < n; ++i) {
+        const Geom& G = L.g[i];
+        if (G.tile != tile) continue;
+        GemmTask t{};
+        const int P = (int)G.P, Q = (int)G.Q;
+        const int nt = P / tile;
+        const double p = (double)G.p, q = (double)G.q;
+        t.P = P;
+        t.split = G.split && !L.f32_ops;
+        t.scale = scale + 4 * i;
+        if (kind == KIND_SYRK) {
+          t.L = ws + (L.f32_ops ? G.xm : G.xb);
+          t.R0 = t.R1 = t.L;
+          t.ldl = t.ldr = Q;
+          t.K = t.kper = Q;
+          t.tiles_m = t.tiles_n = nt;
+          t.tri = 1;
+          t.tile_count = nt * (nt + 1) / 2;
+          t.fbuf = reinterpret_cast<float*>(ws + G.a32);
+          t.ld_f = P;
+          t.out0 = L.f32_ops ? nullptr : ws + G.aop;
+          t.out1 = t.split ? ws + G.r3 : nullptr;
+          t.ld0 = t.ld1 = t.split ? 3 * P : P;
+          flops += p * (p + 1) * q;
+        } else if (kind == KIND_POLY) {
+          t.L = ws + G.aop;
+          t.R0 = t.R1 = t.split ? ws + G.r3 : ws + G.aop;
+          t.ldl = t.ldr = t.split ? 3 * P : P;
+          t.K = t.kper = t.split ? 3 * P : P;
+          t.tiles_m = t.tiles_n = nt;
+          t.tri = 1;
+          t.tile_count = nt * (nt + 1) / 2;
+          t.fbuf = reinterpret_cast<float*>(ws + G.a32);
+          t.ld_f = P;
+          t.out0 = ws + G.bop;
+          t.ld0 = t.split ? 2 * P : P;
+          flops += p * p * (p + 1);
+        } else {
+          t.L = ws + G.bop;
+          t.R0 = ws + G.xt0;
+          t.R1 = ws + G.xt1;
+          t.ldl = t.split ? 2 * P : P;
+          t.ldr = P;
+          t.K = t.split ? 2 * P : P;
+          t.kper = P;
+          t.tiles_m = nt;
+          t.tiles_n = Q / tile;
+          t.tri = 0;
+          t.tile_count = t.tiles_m * t.tiles_n;
+          t.fbuf = reinterpret_cast<float*>(ws + G.xm);
+          t.ld_f = Q;
+          t.out0 = L.f32_ops ? nullptr : ws + G.xb;
+          t.ld0 = Q;
+          t.out1 = ws + G.xt0;
+          t.out2 = ws + G.xt1;
+          t.ld1 = P;
+          flops += 2.0 * p * p * q;
+        }
+        t.tile_begin = acc;
+        acc += t.tile_count;
+        gtasks.push_back(t);
+      }
+      if (gtasks.size() > begin) {
+        GemmLaunch gl{kind, tile, 0, (int)(gtasks.size() - begin), acc, flops};
+        plan->gemms.push_back(gl);
+        ranges.push_back({begin, gtasks.size()});
+      }
+    }
+  }
+
+  // One device allocation holds every table.
+  size_t off = 0;
+  auto place = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 64);
+    return o;
+  };
+  plan->in_off = place(sizeof(EwTask) * n);
+  plan->out_off = place(sizeof(EwTask) * n);
+  plan->norm_off = place(sizeof(NormTask) * n);
+  const size_t g_off = place(sizeof(GemmTask) * gtasks.size());
+  for (size_t k = 0; k < plan->gemms.size(); ++k)
+    plan->gemms[k].off = g_off + sizeof(GemmTask) * ranges[k].first;
+  std::vector<char> host(off);
+  std::memcpy(host.data() + plan->in_off, tin.data(), sizeof(EwTask) * n);
+  std::memcpy(host.data() + plan->out_off, tout.data(), sizeof(EwTask) * n);
+  std::memcpy(host.data() + plan->norm_off, tnorm.data(), sizeof(NormTask) * n);
+  if (!gtasks.empty())
+    std::memcpy(host.data() + g_off, gtasks.data(), sizeof(GemmTask) * gtasks.size());
+  hipError_t e = hipMalloc(&plan->dtab, off);
+  if (e != hipSuccess) {
+    plan->dtab = nullptr;
+    return fail(DMUON_E_HIP, std::string("hipMalloc(launch tables): ") + hipGetErrorString(e));
+  }
+  e = hipMemcpy(plan->dtab, host.data(), off, hipMemcpyHostToDevice);
+  if (e != hipSuccess)
+    return fail(DMUON_E_HIP, std::string("hipMemcpy(launch tables): ") + hipGetErrorString(e));
+  *out = plan.release();
+  return DMUON_OK;
+}
+
+// Looks up (or builds) the plan; caller holds g_plan_mu.
+dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_batch_t* dst,
+                        const dmuon_batch_t* bufs, bool ns_only, char* ws, Plan** out) {
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::vector<int64_t> key;
+  key.reserve(8 + 5 * (size_t)src->count);
+  key.push_back(device);
+  key.push_back(ns_only);
+  key.push_back(L.f32_ops);
+  key.push_back(src->dtype);
+  key.push_back(dst->dtype);
+  key.push_back((int64_t)reinterpret_cast<uintptr_t>(ws));
+  key.push_back(src->count);
+  for (int i = 0; i < src->count; ++i) {
+    key.push_back(src->mats[i].m);
+    key.push_back(src->mats[i].n);
+    key.push_back((int64_t)reinterpret_cast<uintptr_t>(src->mats[i].ptr));
+    key.push_back((int64_t)reinterpret_cast<uintptr_t>(dst->mats[i].ptr));
+    key.push_back(bufs ? (int64_t)reinterpret_cast<uintptr_t>(bufs->mats[i].ptr) : 0);
+    key.push_back(L.g[i].split);
+  }
+  for (size_t k = 0; k < g_plans.size(); ++k) {
+    if (g_plans[k]->key == key) {
+      std::unique_ptr<Plan> hit = std::move(g_plans[k]);
+      g_plans.erase(g_plans.begin() + (long)k);
+      g_plans.push_back(std::move(hit));
+      *out = g_plans.back().get();
+      return DMUON_OK;
+    }
+  }
+  Plan* p = nullptr;
+  dmuon_status_t st = build_plan(L, src, dst, bufs, ns_only, ws, device, std::move(key), &p);
+  if (st != DMUON_OK) return st;
+  if (g_plans.size() >= kMaxPlans) g_plans.erase(g_plans.begin());
+  g_plans.emplace_back(p);
+  *out = p;
+  return DMUON_OK;
+}
+
+// ------------------------------------------------------------- profiling --
+
+struct ProfRec {
+  int kind;
+  hipEvent_t e0, e1;
+  double flops, bytes;
+};
+
+struct Prof {
+  bool on = false;
+  uint32_t mask = 0;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+thread_local Prof g_prof;
+
+const char* kKindNames[KIND_COUNT] = {"momentum", "input", "norm", "syrk",
+                                      "poly", "update_x", "update_p", "output"};
+
+template <class F>
+hipError_t timed(int kind, double flops, double bytes, hipStream_t s, F&& launch) {
+  if (!g_prof.on || !(g_prof.mask & (1u << kind))) return launch();
+  hipEvent_t e0 = g_prof.get(), e1 = g_prof.get();
+  if (e0) (void)hipEventRecord(e0, s);
+  const hipError_t err = launch();
+  if (e1) (void)hipEventRecord(e1, s);
+  if (e0 && e1) g_prof.recs.push_back({kind, e0, e1, flops, bytes});
+  return err;
+}
+
+dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, float momentum,
+                   int nesterov, float lr, float decay, hipStream_t s) {
+  const char* tab = static_cast<const char*>(plan.dtab);
+  auto check = [](hipError_t e, const char* what) -> dmuon_status_t {
+    if (e == hipSuccess) return DMUON_OK;
+    return fail(DMUON_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  };
+  const EwTask* tin = reinterpret_cast<const EwTask*>(tab + plan.in_off);
+  const EwTask* tout = reinterpret_cast<const EwTask*>(tab + plan.out_off);
+  const NormTask* tnorm = reinterpret_cast<const NormTask*>(tab + plan.norm_off);
+  dmuon_status_t st = check(
+      timed(ns_only ? KIND_INPUT : KIND_MOMENTUM, 0, plan.in_bytes, s,
+            [&] { return launch_momentum(tin, plan.nmat, plan.in_tiles, momentum, nesterov,
+                                         ns_only, s); }),
+      "momentum/input launch");
+  if (st) return st;
+  st = check(timed(KIND_NORM, 0, plan.norm_bytes, s,
+                   [&] { return launch_norm(tnorm, plan.nmat, cfg->eps, s); }),
+             "norm launch");
+  if (st) return st;
+  for (int it = 0; it < cfg->ns_steps; ++it) {
+    const float* c = cfg->coeffs ? cfg->coeffs + 3 * it : kQuintic;
+    for (const GemmLaunch& gl : plan.gemms) {
+      const GemmTask* tasks = reinterpret_cast<const GemmTask*>(tab + gl.off);
+      st = check(timed(gl.kind, gl.flops, 0, s,
+                       [&] {
+                         return launch_gemm(gl.kind, gl.tile, plan.f32_ops, tasks, gl.ntasks,
+                                            gl.total, it, c[0], c[1], c[2], s);
+                       }),
+                 "NS product launch");
+      if (st) return st;
+    }
+  }
+  return check(timed(ns_only ? KIND_OUTPUT : KIND_UPDATE, 0, plan.out_bytes, s,
+                     [&] {
+                       return launch_update(tout, plan.nmat, plan.out_tiles, lr, decay, ns_only,
+                                            s);
+                     }),
+               "update/output launch");
+}
+
+dmuon_status_t check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+  if (L.total == 0) return DMUON_OK;
+  if (!ws) return fail(DMUON_E_WORKSPACE, "workspace: null pointer");
+  if (reinterpret_cast<uintptr_t>(ws) % kWsAlign)
+    return fail(DMUON_E_WORKSPACE, "workspace: pointer not 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(DMUON_E_WORKSPACE, "workspace: " + std::to_string(ws_bytes) + " bytes given, " +
+                                       std::to_string(L.total) + " needed");
+  return DMUON_OK;
+}
+
+}  // namespace
+
+// ================================================================== C ABI ==
+
+extern "C" {
+
+dmuon_status_t dmuon_ns_workspace_size(const dmuon_batch_t* g, const dmuon_ns_cfg_t* cfg,
+                                       size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DMUON_E_INVALID, "bytes: null");
+  dmuon_status_t st = check_batch(g, "g", false);
+  if (st) return st;
+  if (!cfg) return fail(DMUON_E_INVALID, "cfg: null");
+  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_AUTO)
+    return fail(DMUON_E_INVALID, "cfg: unknown precision mode");
+  Layout L;
+  st = make_layout(g, cfg->prec, &L);
+  if (st) return st;
+  *bytes = g->count ? L.total : 0;
+  return DMUON_OK;
+}
+
+dmuon_status_t dmuon_ns_orthogonalize(const dmuon_batch_t* g, const dmuon_batch_t* out,
+                                      const dmuon_ns_cfg_t* cfg, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  g_last_error.clear();
+  dmuon_status_t st = check_batch(g, "g", true);
+  if (st) return st;
+  if ((st = check_batch(out, "out", true))) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = same_shapes(g, out, "g", "out"))) return st;
+  if (g->dtype != out->dtype) return fail(DMUON_E_INVALID, "out dtype must equal g dtype");
+  if (g->count == 0) return DMUON_OK;
+  Layout L;
+  if ((st = make_layout(g, cfg->prec, &L))) return st;
+  if ((st = check_ws(L, ws, ws_bytes))) return st;
+  // out[i] may be exactly g[i]; nothing else may overlap.
+  std::vector<Span> spans;
+  add_spans(spans, g, 0);
+  for (int i = 0; i < out->count; ++i)
+    if (out->mats[i].ptr != g->mats[i].ptr) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(out->mats[i].ptr);
+      spans.push_back({lo, lo + (uintptr_t)(out->mats[i].m * out->mats[i].n * esize(out->dtype)),
+                       1, i});
+    }
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(ws);
+  spans.push_back({wlo, wlo + L.total, 2, 0});
+  static const char* const names[] = {"g", "out", "ws"};
+  if ((st = check_disjoint(spans, names))) return st;
+
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  Plan* plan = nullptr;
+  if ((st = get_plan(L, g, out, nullptr, true, static_cast<char*>(ws), &plan))) return st;
+  return run(*plan, cfg, true, 0.f, 0, 0.f, 1.f, static_cast<hipStream_t>(stream));
+}
+
+dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t* grads,
+                               const dmuon_batch_t* bufs, const dmuon_ns_cfg_t* cfg,
+                               float momentum, float lr, float weight_decay, int32_t nesterov,
+                               void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  dmuon_status_t st = check_batch(params, "params", true);
+  if (st) return st;
+  if ((st = check_batch(grads, "grads", true))) return st;
+  if ((st = check_batch(bufs, "bufs", true))) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = same_shapes(params, grads, "params", "grads"))) return st;
+  if ((st = same_shapes(params, bufs, "params", "bufs"))) return st;
+  if (bufs->dtype != DMUON_F32) return fail(DMUON_E_INVALID, "bufs must be F32");
+  if (!std::isfinite(momentum) || !std::isfinite(lr) || !std::isfinite(weight_decay))
+    return fail(DMUON_E_INVALID, "momentum, lr and weight_decay must be finite");
+  if (params->count == 0) return DMUON_OK;
+  Layout L;
+  if ((st = make_layout(grads, cfg->prec, &L))) return st;
+  if ((st = check_ws(L, ws, ws_bytes))) return st;
+  std::vector<Span> spans;
+  add_spans(spans, params, 0);
+  add_spans(spans, grads, 1);
+  add_spans(spans, bufs, 2);
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(ws);
+  spans.push_back({wlo, wlo + L.total, 3, 0});
+  static const char* const names[] = {"params", "grads", "bufs", "ws"};
+  if ((st = check_disjoint(spans, names))) return st;
+
+  // decoupled weight decay on the pre-update parameter
+  const float decay = (float)(1.0 - (double)lr * (double)weight_decay);
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  Plan* plan = nullptr;
+  if ((st = get_plan(L, grads, params, bufs, false, static_cast<char*>(ws), &plan))) return st;
+  return run(*plan, cfg, false, momentum, nesterov ? 1 : 0, lr, decay,
+             static_cast<hipStream_t>(stream));
+}
+
+const char* dmuon_status_str(dmuon_status_t s) {
+  switch (s) {
+    case DMUON_OK: return "ok";
+    case DMUON_E_INVALID: return "invalid argument";
+    case DMUON_E_UNSUPPORTED: return "unsupported";
+    case DMUON_E_WORKSPACE: return "workspace";
+    case DMUON_E_HIP: return "hip error";
+  }
+  return "unknown status";
+}
+
+const char* dmuon_last_error(void) { return g_last_error.c_str(); }
+
+const char* dmuon_backend_info(void) {
+  return "direct NS (SYRK + symmetric poly + update-X) . gfx950 MFMA "
+         "bf16 32x32x16 / fp32 32x32x2 . tiles 64,128 . fp32 master X";
+}
+
+int32_t dmuon_profile_begin(uint32_t kind_mask) {
+  for (ProfRec& r : g_prof.recs) {
+    g_prof.pool.push_back(r.e0);
+    g_prof.pool.push_back(r.e1);
+  }
+  g_prof.recs.clear();
+  g_prof.mask = kind_mask ? kind_mask : 0xffffffffu;
+  g_prof.on = true;
+  return 0;
+}
+
+int32_t dmuon_profile_end(dmuon_profile_row_t* out, int32_t max) {
+  g_prof.on = false;
+  dmuon_profile_row_t rows[KIND_COUNT];
+  std::memset(rows, 0, sizeof rows);
+  int32_t status = 0;
+  for (ProfRec& r : g_prof.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.e1) != hipSuccess || hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess)
+      status = -1;
+    dmuon_profile_row_t& row = rows[r.kind];
+    row.launches += 1;
+    row.ms += ms;
+    row.flops += r.flops;
+    row.bytes += r.bytes;
+    g_prof.pool.push_back(r.e0);
+    g_prof.pool.push_back(r.e1);
+  }
+  g_prof.recs.clear();
+  if (status) return fail(DMUON_E_HIP, "profile: event query failed"), -1;
+  int32_t k = 0;
+  for (int kind = 0; kind < KIND_COUNT; ++kind) {
+    if (!rows[kind].launches) continue;
+    if (out && k < max) {
+      out[k] = rows[kind];
+      out[k].kind = kind;
+      std::snprintf(out[k].name, sizeof out[k].name, "%s", kKindNames[kind]);
+    }
+    ++k;
+  }
+  return out ? std::min(k, max) : k;
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal launch descriptors shared by the host runtime and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace dmuon {
+
+// Kernel kinds, used for profiling rows and launch bookkeeping.
+enum Kind : int {
+  KIND_MOMENTUM = 0,  // momentum (+ Nesterov), orientation, sum of squares
+  KIND_INPUT,         // NS-only input pass: orientation, sum of squares
+  KIND_NORM,          // per-matrix norm finalize -> 1/(||u|| + eps)
+  KIND_SYRK,          // A = X X^T (upper tiles, mirrored write)
+  KIND_POLY,          // B = b A + c A A^T (upper tiles, mirrored write)
+  KIND_UPDX,          // X <- a X + B X
+  KIND_UPDATE,        // p <- p (1 - lr wd) - lr O
+  KIND_OUTPUT,        // out <- O in the caller's dtype
+  KIND_COUNT
+};
+
+// Element-wise tile size (original-layout tiles of EW_TILE x EW_TILE).
+constexpr int EW_TILE = 64;
+constexpr int EW_THREADS = 256;
+
+// One matrix of an element-wise launch.  Tiles cover `rows` x `cols` in
+// the caller's layout; for the input passes these are the padded extents of
+// the oriented workspace mapped back to the caller's layout.
+struct EwTask {
+  int32_t m, n;            // caller's shape
+  int32_t rows, cols;      // extent covered by this launch's tiles
+  int32_t tiles_c;         // tiles along cols
+  int32_t tile_begin;      // first global tile of this task
+  int32_t tile_count;      // tiles of this task
+  int32_t transposed;      // m > n: the oriented X is the transpose
+  int32_t in_dtype;        // dtype of `src` (grad / input G)
+  int32_t out_dtype;       // dtype of `dst` (param / output)
+  int32_t ldx;             // row stride of xm / xb (padded q)
+  int32_t ldt;             // row stride of xt (padded p)
+  int32_t f32_ops;         // 1: xt holds fp32 (NS in fp32), 0: bf16
+  int32_t vec;             // 1: caller buffers allow 16-byte (4-element) access
+  const void* src;         // grad (step) or G (NS only)
+  float* buf;              // momentum buffer (step) or null
+  void* dst;               // param (update) or output (NS only)
+  float* xm;               // fp32 master X, P x Q
+  uint16_t* xb;            // bf16 X, P x Q (null when f32_ops)
+  void* xt;                // X^T, Q x P (bf16 or fp32)
+  float* partial;          // per-tile sums of squares (indexed by global tile)
+  float* scale;            // per-matrix scalars: [0]=1/(s+eps) [1]=its square
+};
+
+// One matrix of a grouped NT-GEMM launch: C = L * R^T over K, tile T x T.
+// L is (tiles_m*T) x K row-major with stride ldl; R is (tiles_n*T) x K with
+// stride ldr and column index taken modulo kper (for hi/lo split operands
+// that reuse one R for two K segments).
+struct GemmTask {
+  const void* L;
+  const void* R0;          // R on even NS iterations
+  const void* R1;          // R on odd NS iterations
+  int32_t ldl, ldr, K, kper;
+  int32_t tiles_m, tiles_n, tile_begin, tile_count;
+  int32_t tri;             // 1: upper-triangle tiles only (+ mirrored write)
+  int32_t split;           // 1: bf16 hi/lo operand layout in the epilogue
+  int32_t P;               // padded p (segment offset of split layouts)
+  int32_t ld_f;            // stride of fbuf
+  float* fbuf;             // SYRK: A (out)  POLY: A (in)  UPDX: X master
+  void* out0;              // SYRK: A operand / L3  POLY: B operand  UPDX: Xb
+  void* out1;              // SYRK: R3            UPDX: X^T (even iter)
+  void* out2;              // UPDX: X^T (odd iter)
+  int32_t ld0, ld1;
+  const float* scale;      // per-matrix scalars (see EwTask::scale)
+};
+
+struct NormTask {
+  int32_t tile_begin, tile_count;
+  const float* partial;
+  float* scale;
+};
+
+// Launch helpers implemented in dmuon_kernels.hip.
+hipError_t launch_momentum(const EwTask* tasks, int ntasks, int total_tiles,
+                           float momentum, int nesterov, int ns_only,
+                           hipStream_t s);
+hipError_t launch_norm(const NormTask* tasks, int ntasks, float eps,
+                       hipStream_t s);
+// kind in {KIND_SYRK, KIND_POLY, KIND_UPDX}; tile in {64, 128}
+hipError_t launch_gemm(int kind, int tile, int f32_ops,
+                       const GemmTask* tasks, int ntasks, int total_tiles,
+                       int iter, float a, float b, float c, hipStream_t s);
+hipError_t launch_update(const EwTask* tasks, int ntasks, int total_tiles,
+                         float lr, float decay, int ns_only, hipStream_t s);
+
+}  // namespace dmuon

@@ -1,0 +1,682 @@
+// gfx950 (CDNA4) kernels of the per-owner Muon step.
+//
+// Data layout in the workspace, per matrix (p = min(m, n), q = max(m, n),
+// P and Q padded up to the GEMM tile; every pad element is kept at zero):
+//   xm    fp32 master copy of the oriented X, P x Q row-major
+//   xb    bf16 copy of X (the SYRK operand), P x Q           [bf16 modes]
+//   xt    X^T, Q x P, two buffers used in turn (the B X operand)
+//   a32   fp32 A = X X^T, P x P
+//   aop   A as MFMA operand: bf16 P x P, or hi/lo layouts   [bf16 modes]
+//   bop   B = bA + cA^2 as MFMA operand (fp32 / bf16 / hi-lo)
+// With every operand stored K-contiguous, all three products of one NS
+// iteration are "NT" products C = L R^T and share one MFMA main loop.
+#include <type_traits>
+
+#include "dmuon_internal.h"
+
+namespace dmuon {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float from_bf16(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+__device__ __forceinline__ float load1(const void* base, int dtype, size_t i) {
+  return dtype == 0 ? static_cast<const float*>(base)[i]
+                    : from_bf16(static_cast<const uint16_t*>(base)[i]);
+}
+
+__device__ __forceinline__ void store1(void* base, int dtype, size_t i, float v) {
+  if (dtype == 0)
+    static_cast<float*>(base)[i] = v;
+  else
+    static_cast<uint16_t*>(base)[i] = to_bf16(v);
+}
+
+__device__ __forceinline__ f32x4 load4(const void* base, int dtype, size_t i) {
+  f32x4 r;
+  if (dtype == 0) {
+    r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i);
+  } else {
+    uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
+    r[0] = __uint_as_float(w.x << 16);
+    r[1] = __uint_as_float(w.x & 0xffff0000u);
+    r[2] = __uint_as_float(w.y << 16);
+    r[3] = __uint_as_float(w.y & 0xffff0000u);
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  uint2 w;
+  w.x = (uint32_t)to_bf16(a) | ((uint32_t)to_bf16(b) << 16);
+  w.y = (uint32_t)to_bf16(c) | ((uint32_t)to_bf16(d) << 16);
+  return w;
+}
+
+__device__ __forceinline__ void store4(void* base, int dtype, size_t i, f32x4 v) {
+  if (dtype == 0)
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + i) = v;
+  else
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + i) =
+        pack_bf16x4(v[0], v[1], v[2], v[3]);
+}
+
+// Last task whose tile_begin <= tile (tasks are sorted by tile_begin).
+template <class Task>
+__device__ __forceinline__ int find_task(const Task* tasks, int ntasks, int tile) {
+  int lo = 0, hi = ntasks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tasks[mid].tile_begin <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// --------------------------------------------------------------------------
+// Wavefront sum: DPP within each row of 16 lanes, then cross-row shuffles.
+// Every lane ends with the same value, summed in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// --------------------------------------------------------------------------
+// Momentum / input pass.  One 64 x 64 tile of the caller's layout per block:
+//   buf <- mu*buf + g ; u <- nesterov ? g + mu*buf : buf   (or u <- G)
+// u is written to the oriented workspace in both layouts (X and X^T, the
+// transposed one through LDS), pads are written as zeros, and the tile's
+// sum of u^2 goes to partial[tile].
+__global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
+    const EwTask* __restrict__ tasks, int ntasks, int total_tiles, float mu,
+    int nesterov, int ns_only) {
+  __shared__ float tile[EW_TILE][EW_TILE + 1];
+  __shared__ float wsum[EW_THREADS / 64];
+  const int gt = blockIdx.x;
+  if (gt >= total_tiles) return;
+  const EwTask& T = tasks[find_task(tasks, ntasks, gt)];
+  const int lt = gt - T.tile_begin;
+  const int r0 = (lt / T.tiles_c) * EW_TILE;
+  const int c0 = (lt % T.tiles_c) * EW_TILE;
+  const int tid = threadIdx.x;
+  const int cx = (tid & 15) * 4;
+  const int ry = tid >> 4;
+  const bool f32ops = T.f32_ops != 0;
+  float ss = 0.f;
+
+  for (int k = 0; k < EW_TILE / 16; ++k) {
+    const int r = ry + 16 * k;
+    const int gr = r0 + r;
+    const int gc = c0 + cx;
+    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+    if (gr < T.m && gc < T.n) {
+      const size_t idx = (size_t)gr * T.n + gc;
+      if (T.vec && gc + 3 < T.n) {
+        const f32x4 g = load4(T.src, T.in_dtype, idx);
+        if (ns_only) {
+          u = g;
+        } else {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(T.buf + idx);
+          f32x4 bn;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bn[e] = fmaf(mu, b[e], g[e]);
+            u[e] = nesterov ? fmaf(mu, bn[e], g[e]) : bn[e];
+          }
+          *reinterpret_cast<f32x4*>(T.buf + idx) = bn;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (gc + e < T.n) {
+            const float g = load1(T.src, T.in_dtype, idx + e);
+            if (ns_only) {
+              u[e] = g;
+            } else {
+              const float bn = fmaf(mu, T.buf[idx + e], g);
+              T.buf[idx + e] = bn;
+              u[e] = nesterov ? fmaf(mu, bn, g) : bn;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss = fmaf(u[e], u[e], ss);
+      tile[r][cx + e] = u[e];
+    }
+    // Same-layout copy: X itself for a wide matrix, X^T for a tall one.
+    if (!T.transposed) {
+      const size_t o = (size_t)gr * T.ldx + gc;
+      *reinterpret_cast<f32x4*>(T.xm + o) = u;
+      if (!f32ops)
+        *reinterpret_cast<uint2*>(T.xb + o) = pack_bf16x4(u[0], u[1], u[2], u[3]);
+    } else {
+      const size_t o = (size_t)gr * T.ldt + gc;
+      if (f32ops)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(T.xt) + o) = u;
+      else
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(T.xt) + o) =
+            pack_bf16x4(u[0], u[1], u[2], u[3]);
+    }
+  }
+  __syncthreads();
+  // Transposed copy: X^T for a wide matrix, X (and its bf16 copy) for a tall one.
+  for (int k = 0; k < EW_TILE / 16; ++k) {
+    const int oc = ry + 16 * k;  // column of the tile = row of the output
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = tile[cx + e][oc];
+    const int orow = c0 + oc;
+    const int ocol = r0 + cx;
+    if (!T.transposed) {
+      const size_t o = (size_t)orow * T.ldt + ocol;
+      if (f32ops)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(T.xt) + o) = v;
+      else
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(T.xt) + o) =
+            pack_bf16x4(v[0], v[1], v[2], v[3]);
+    } else {
+      const size_t o = (size_t)orow * T.ldx + ocol;
+      *reinterpret_cast<f32x4*>(T.xm + o) = v;
+      if (!f32ops)
+        *reinterpret_cast<uint2*>(T.xb + o) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  // Block sum of squares, fixed order.
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < EW_THREADS / 64; ++w) s += wsum[w];
+    T.partial[gt] = s;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Norm finalize: one block per matrix sums its tiles' partials in fp64 in a
+// fixed order and stores 1/(||u||_F + eps) and its square.
+__global__ __launch_bounds__(256) void norm_kernel(const NormTask* __restrict__ tasks,
+                                                   float eps) {
+  __shared__ double wpart[4];
+  const NormTask& T = tasks[blockIdx.x];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < T.tile_count; i += 256)
+    acc += (double)T.partial[T.tile_begin + i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) wpart[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double tot = (wpart[0] + wpart[1]) + (wpart[2] + wpart[3]);
+    const double s = sqrt(tot);
+    const double inv = 1.0 / (s + (double)eps);
+    T.scale[0] = (float)inv;
+    T.scale[1] = (float)(inv * inv);
+    T.scale[2] = (float)s;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Grouped NT GEMM on MFMA: C (T x T tile) = L[tm] * R[tn]^T over K, then a
+// kind-specific epilogue.  256 threads = 4 waves in a 2 x 2 grid, each wave
+// owns (T/2) x (T/2) = NT x NT blocks of 32 x 32 MFMA output.  K advances
+// 128 bytes per stage (64 bf16 or 32 fp32) through double-buffered LDS rows
+// padded by 16 bytes so that the 16-byte operand reads are conflict free.
+
+// Workgroups are handed to the 8 XCDs round robin; give each XCD one
+// contiguous range of the tile order so its L2 sees neighbouring tiles.
+__device__ __forceinline__ int xcd_remap(int b, int grid) {
+  return (b & 7) * (grid >> 3) + (b >> 3);
+}
+
+constexpr int GROUP = 8;  // tile rows per group of the full-product order
+
+// Upper-triangle tile order in 8 x 8 super-tiles (row-major over the
+// super-tiles, row-major inside), so concurrently running tiles share
+// operand panels.
+__device__ __forceinline__ void tri_decode(int t, int nt, int& tm, int& tn) {
+  const int ns = (nt + GROUP - 1) / GROUP;
+  for (int si = 0; si < ns; ++si) {
+    const int rows = min(GROUP, nt - si * GROUP);
+    for (int sj = si; sj < ns; ++sj) {
+      const int cols = min(GROUP, nt - sj * GROUP);
+      const int cnt = (si == sj) ? rows * (rows + 1) / 2 : rows * cols;
+      if (t < cnt) {
+        if (si == sj) {
+          int r = 0;
+          while (t >= rows - r) { t -= rows - r; ++r; }
+          tm = si * GROUP + r;
+          tn = si * GROUP + r + t;
+        } else {
+          tm = si * GROUP + t / cols;
+          tn = sj * GROUP + t % cols;
+        }
+        return;
+      }
+      t -= cnt;
+    }
+  }
+  tm = tn = 0;  // not reached for t < nt(nt+1)/2
+}
+
+__device__ __forceinline__ void full_decode(int t, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  const int group = t / (GROUP * tiles_n);
+  const int first = group * GROUP;
+  const int gsz = min(GROUP, tiles_m - first);
+  const int w = t - group * GROUP * tiles_n;
+  tm = first + w % gsz;
+  tn = w / gsz;
+}
+
+template <int KIND, int T, bool F32>
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmTask* __restrict__ tasks,
+                                                   int ntasks, int total_tiles, int iter,
+                                                   float ca, float cb, float cc) {
+  using E = typename std::conditional<F32, float, uint16_t>::type;
+  constexpr int ESZ = sizeof(E);
+  constexpr int BK = 128 / ESZ;           // K elements per stage
+  constexpr int VEC = 16 / ESZ;           // elements per 16-byte chunk
+  constexpr int STRIDE = BK + VEC;        // LDS row stride in elements
+  constexpr int WT = T / 2;               // wave tile
+  constexpr int NT = WT / 32;             // 32x32 MFMA blocks per wave side
+  constexpr int LOADS = T * 8 / 256;      // 16-byte chunks per thread per operand
+  __shared__ __attribute__((aligned(16))) E lds[2][2][T * STRIDE];
+
+  const int vb = xcd_remap(blockIdx.x, gridDim.x);
+  if (vb >= total_tiles) return;
+  const GemmTask& G = tasks[find_task(tasks, ntasks, vb)];
+  const int lt = vb - G.tile_begin;
+  int tm, tn;
+  if (G.tri)
+    tri_decode(lt, G.tiles_m, tm, tn);
+  else
+    full_decode(lt, G.tiles_m, G.tiles_n, tm, tn);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = (wave >> 1) * WT;
+  const int wc = (wave & 1) * WT;
+
+  const E* __restrict__ Lp = static_cast<const E*>(G.L) + (size_t)tm * T * G.ldl;
+  const E* __restrict__ Rp =
+      static_cast<const E*>((iter & 1) ? G.R1 : G.R0) + (size_t)tn * T * G.ldr;
+  const int ldl = G.ldl, ldr = G.ldr, kper = G.kper;
+  const int nk = G.K / BK;
+
+  uint4 regL[LOADS], regR[LOADS];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+    const int kr = k0 % kper;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 3;
+      const int col = (c & 7) * VEC;
+      regL[i] = *reinterpret_cast<const uint4*>(Lp + (size_t)row * ldl + k0 + col);
+      regR[i] = *reinterpret_cast<const uint4*>(Rp + (size_t)row * ldr + kr + col);
+    }
+  };
+  auto sstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 3;
+      const int col = (c & 7) * VEC;
+      *reinterpret_cast<uint4*>(&lds[st][0][row * STRIDE + col]) = regL[i];
+      *reinterpret_cast<uint4*>(&lds[st][1][row * STRIDE + col]) = regR[i];
+    }
+  };
+
+  f32x16 acc[NT][NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](int st) {
+    const E* sL = lds[st][0];
+    const E* sR = lds[st][1];
+    const int lrow = lane & 31;
+    const int khalf = lane >> 5;
+    if constexpr (!F32) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8 a[NT], b[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          a[t] = *reinterpret_cast<const bf16x8*>(
+              &sL[(wr + t * 32 + lrow) * STRIDE + ks * 16 + khalf * 8]);
+          b[t] = *reinterpret_cast<const bf16x8*>(
+              &sR[(wc + t * 32 + lrow) * STRIDE + ks * 16 + khalf * 8]);
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    } else {
+      // fp32: each lane reads 4 consecutive k; instruction t of a group
+      // takes element t, so lane half h covers k = 8*ks + 4*h + t.
+#pragma unroll
+      for (int ks = 0; ks < BK / 8; ++ks) {
+        f32x4 a[NT], b[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          a[t] = *reinterpret_cast<const f32x4*>(
+              &sL[(wr + t * 32 + lrow) * STRIDE + ks * 8 + khalf * 4]);
+          b[t] = *reinterpret_cast<const f32x4*>(
+              &sR[(wc + t * 32 + lrow) * STRIDE + ks * 8 + khalf * 4]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    compute(st);
+    if (kt + 1 < nk) sstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue.  32x32 MFMA output: lane l, register r holds row
+  // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its block.
+  const int row_base = tm * T + wr + 4 * (lane >> 5);
+  const int col_base = tn * T + wc + (lane & 31);
+  const bool mirror = G.tri && (tm != tn);
+  float s = 1.f;
+  if (KIND == KIND_SYRK && iter == 0) s = G.scale[1];
+  if (KIND == KIND_UPDX && iter == 0) s = G.scale[0];
+  const int P = G.P;
+
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int gi = row_base + i * 32 + 8 * g;  // rows gi .. gi+3
+        const int gj = col_base + j * 32;
+        f32x4 v;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) v[rr] = acc[i][j][4 * g + rr];
+
+        if constexpr (KIND == KIND_SYRK) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) v[rr] *= s;
+          float* A = G.fbuf;
+          const int ldf = G.ld_f;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) A[(size_t)(gi + rr) * ldf + gj] = v[rr];
+          if (mirror) *reinterpret_cast<f32x4*>(A + (size_t)gj * ldf + gi) = v;
+          if constexpr (!F32) {
+            uint16_t* o0 = static_cast<uint16_t*>(G.out0);
+            const int ld0 = G.ld0;
+            if (!G.split) {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) o0[(size_t)(gi + rr) * ld0 + gj] = to_bf16(v[rr]);
+              if (mirror)
+                *reinterpret_cast<uint2*>(o0 + (size_t)gj * ld0 + gi) =
+                    pack_bf16x4(v[0], v[1], v[2], v[3]);
+            } else {
+              // L3 = [hi | hi | lo], R3 = [hi | lo | hi] along K (3P), so
+              // L3 R3^T = hi hi^T + hi lo^T + lo hi^T.
+              uint16_t* o1 = static_cast<uint16_t*>(G.out1);
+              const int ld1 = G.ld1;
+              f32x4 hi, lo;
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                hi[rr] = from_bf16(to_bf16(v[rr]));
+                lo[rr] = v[rr] - hi[rr];
+              }
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const size_t rL = (size_t)(gi + rr) * ld0 + gj;
+                const size_t rR = (size_t)(gi + rr) * ld1 + gj;
+                const uint16_t h = to_bf16(hi[rr]), l = to_bf16(lo[rr]);
+                o0[rL] = h; o0[rL + P] = h; o0[rL + 2 * P] = l;
+                o1[rR] = h; o1[rR + P] = l; o1[rR + 2 * P] = h;
+              }
+              if (mirror) {
+                const uint2 h4 = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+                const uint2 l4 = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+                const size_t mL = (size_t)gj * ld0 + gi;
+                const size_t mR = (size_t)gj * ld1 + gi;
+                *reinterpret_cast<uint2*>(o0 + mL) = h4;
+                *reinterpret_cast<uint2*>(o0 + mL + P) = h4;
+                *reinterpret_cast<uint2*>(o0 + mL + 2 * P) = l4;
+                *reinterpret_cast<uint2*>(o1 + mR) = h4;
+                *reinterpret_cast<uint2*>(o1 + mR + P) = l4;
+                *reinterpret_cast<uint2*>(o1 + mR + 2 * P) = h4;
+              }
+            }
+          }
+        } else if constexpr (KIND == KIND_POLY) {
+          const float* A = G.fbuf;
+          const int ldf = G.ld_f;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(cb, A[(size_t)(gi + rr) * ldf + gj], cc * v[rr]);
+          if constexpr (F32) {
+            float* o0 = static_cast<float*>(G.out0);
+            const int ld0 = G.ld0;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) o0[(size_t)(gi + rr) * ld0 + gj] = v[rr];
+            if (mirror) *reinterpret_cast<f32x4*>(o0 + (size_t)gj * ld0 + gi) = v;
+          } else {
+            uint16_t* o0 = static_cast<uint16_t*>(G.out0);
+            const int ld0 = G.ld0;
+            if (!G.split) {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) o0[(size_t)(gi + rr) * ld0 + gj] = to_bf16(v[rr]);
+              if (mirror)
+                *reinterpret_cast<uint2*>(o0 + (size_t)gj * ld0 + gi) =
+                    pack_bf16x4(v[0], v[1], v[2], v[3]);
+            } else {
+              // [hi | lo] along K (2P); the B X product pairs both halves
+              // with the same X^T.
+              f32x4 hi, lo;
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                hi[rr] = from_bf16(to_bf16(v[rr]));
+                lo[rr] = v[rr] - hi[rr];
+              }
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const size_t o = (size_t)(gi + rr) * ld0 + gj;
+                o0[o] = to_bf16(hi[rr]);
+                o0[o + P] = to_bf16(lo[rr]);
+              }
+              if (mirror) {
+                const size_t o = (size_t)gj * ld0 + gi;
+                *reinterpret_cast<uint2*>(o0 + o) = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+                *reinterpret_cast<uint2*>(o0 + o + P) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+              }
+            }
+          }
+        } else {  // KIND_UPDX: X <- s * (a X + B X_raw), s = 1/(||u||+eps) on iter 0
+          float* X = G.fbuf;
+          const int ldf = G.ld_f;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const size_t o = (size_t)(gi + rr) * ldf + gj;
+            v[rr] = s * fmaf(ca, X[o], v[rr]);
+            X[o] = v[rr];
+          }
+          void* xt_next = (iter & 1) ? G.out1 : G.out2;
+          const int ld1 = G.ld1;
+          if constexpr (F32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(xt_next) + (size_t)gj * ld1 + gi) = v;
+          } else {
+            uint16_t* xb = static_cast<uint16_t*>(G.out0);
+            const int ld0 = G.ld0;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) xb[(size_t)(gi + rr) * ld0 + gj] = to_bf16(v[rr]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(xt_next) + (size_t)gj * ld1 + gi) =
+                pack_bf16x4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+}
+
+// --------------------------------------------------------------------------
+// Update / output pass over 64 x 64 tiles of the caller's layout.
+//   O[r][c] = X[r][c] (wide) or X[c][r] (tall, staged through LDS)
+//   update:  p <- p * decay - lr * O      output: out <- O
+__global__ __launch_bounds__(EW_THREADS) void update_kernel(
+    const EwTask* __restrict__ tasks, int ntasks, int total_tiles, float lr,
+    float decay, int ns_only) {
+  __shared__ float tile[EW_TILE][EW_TILE + 1];
+  const int gt = blockIdx.x;
+  if (gt >= total_tiles) return;
+  const EwTask& T = tasks[find_task(tasks, ntasks, gt)];
+  const int lt = gt - T.tile_begin;
+  const int r0 = (lt / T.tiles_c) * EW_TILE;
+  const int c0 = (lt % T.tiles_c) * EW_TILE;
+  const int tid = threadIdx.x;
+  const int cx = (tid & 15) * 4;
+  const int ry = tid >> 4;
+
+  if (T.transposed) {
+    // X rows c0.., columns r0..: always inside the padded P x Q buffer.
+    for (int k = 0; k < EW_TILE / 16; ++k) {
+      const int xr = ry + 16 * k;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(T.xm + (size_t)(c0 + xr) * T.ldx + r0 + cx);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[xr][cx + e] = v[e];
+    }
+    __syncthreads();
+  }
+  for (int k = 0; k < EW_TILE / 16; ++k) {
+    const int r = ry + 16 * k;
+    const int gr = r0 + r;
+    const int gc = c0 + cx;
+    if (gr >= T.m || gc >= T.n) continue;
+    f32x4 o;
+    if (T.transposed) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = tile[cx + e][r];
+    } else {
+      o = *reinterpret_cast<const f32x4*>(T.xm + (size_t)gr * T.ldx + gc);
+    }
+    const size_t idx = (size_t)gr * T.n + gc;
+    if (T.vec && gc + 3 < T.n) {
+      f32x4 outv;
+      if (ns_only) {
+        outv = o;
+      } else {
+        const f32x4 p = load4(T.dst, T.out_dtype, idx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) outv[e] = fmaf(-lr, o[e], p[e] * decay);
+      }
+      store4(T.dst, T.out_dtype, idx, outv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (gc + e < T.n) {
+          float val = o[e];
+          if (!ns_only) val = fmaf(-lr, o[e], load1(T.dst, T.out_dtype, idx + e) * decay);
+          store1(T.dst, T.out_dtype, idx + e, val);
+        }
+      }
+    }
+  }
+}
+
+template <int KIND, int T, bool F32>
+hipError_t launch_gemm_t(const GemmTask* tasks, int ntasks, int total_tiles, int iter, float a,
+                         float b, float c, hipStream_t s) {
+  const int grid = (total_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_kernel<KIND, T, F32>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
+                     total_tiles, iter, a, b, c);
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_gemm_k(int tile, int f32_ops, const GemmTask* tasks, int ntasks,
+                         int total_tiles, int iter, float a, float b, float c, hipStream_t s) {
+  if (tile == 64)
+    return f32_ops ? launch_gemm_t<KIND, 64, true>(tasks, ntasks, total_tiles, iter, a, b, c, s)
+                   : launch_gemm_t<KIND, 64, false>(tasks, ntasks, total_tiles, iter, a, b, c, s);
+  if (tile == 128)
+    return f32_ops ? launch_gemm_t<KIND, 128, true>(tasks, ntasks, total_tiles, iter, a, b, c, s)
+                   : launch_gemm_t<KIND, 128, false>(tasks, ntasks, total_tiles, iter, a, b, c, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_momentum(const EwTask* tasks, int ntasks, int total_tiles, float momentum,
+                           int nesterov, int ns_only, hipStream_t s) {
+  hipLaunchKernelGGL(momentum_kernel, dim3(total_tiles), dim3(EW_THREADS), 0, s, tasks, ntasks,
+                     total_tiles, momentum, nesterov, ns_only);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const NormTask* tasks, int ntasks, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(norm_kernel, dim3(ntasks), dim3(256), 0, s, tasks, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int kind, int tile, int f32_ops, const GemmTask* tasks, int ntasks,
+                       int total_tiles, int iter, float a, float b, float c, hipStream_t s) {
+  switch (kind) {
+    case KIND_SYRK:
+      return launch_gemm_k<KIND_SYRK>(tile, f32_ops, tasks, ntasks, total_tiles, iter, a, b, c, s);
+    case KIND_POLY:
+      return launch_gemm_k<KIND_POLY>(tile, f32_ops, tasks, ntasks, total_tiles, iter, a, b, c, s);
+    case KIND_UPDX:
+      return launch_gemm_k<KIND_UPDX>(tile, f32_ops, tasks, ntasks, total_tiles, iter, a, b, c, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_update(const EwTask* tasks, int ntasks, int total_tiles, float lr, float decay,
+                         int ns_only, hipStream_t s) {
+  hipLaunchKernelGGL(update_kernel, dim3(total_tiles), dim3(EW_THREADS), 0, s, tasks, ntasks,
+                     total_tiles, lr, decay, ns_only);
+  return hipGetLastError();
+}
+
+}  // namespace dmuon

@@ -1,0 +1,161 @@
+"""GPU parity of dmuon_ns_orthogonalize against the fp64 oracle.
+
+Single-term coefficient tables isolate the kernels: (1, 0, 0) returns the
+normalized, oriented input (input pass + norm + output pass); (0, 1, 0)
+gives X X^T X (SYRK + update-X); (0, 0, 1) gives (X X^T)^2 X (adds the
+symmetric polynomial product).  Full tables are then checked at the
+tolerances of the method: fp32 NS relative Frobenius <= 1e-4; bf16 NS
+relative Frobenius and max singular-value deviation <= 2e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import exact64, rel_frobenius, sigma_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import newton_schulz_06_amd as dm  # noqa: E402
+
+# Shapes spanning several 64/128 tiles, ragged tails, both orientations.
+SHAPES = [(64, 64), (100, 300), (300, 100), (33, 33), (1, 7), (7, 1), (257, 700),
+          (700, 257), (520, 1100), (129, 129)]
+
+
+def _gen(shape, seed, kind="gauss"):
+    return workloads.grad_np(kind, shape[0], shape[1], 90, seed, 0)
+
+
+def _run_ns(gs_np, dtype, prec, coefficients=None, ns_steps=5):
+    gs = [to_dev(g, dtype) for g in gs_np]
+    outs = dm.ns_orthogonalize(gs, coefficients=coefficients, ns_steps=ns_steps, prec=prec)
+    torch.cuda.synchronize()
+    return [exact64(g) for g in gs], [exact64(o) for o in outs]
+
+
+UNIT_TABLES = {"identity": [(1.0, 0.0, 0.0)], "syrk": [(0.0, 1.0, 0.0)],
+               "poly": [(0.0, 0.0, 1.0)], "mixed2": [(1.5, -0.5, 0.25), (0.5, 1.0, -0.5)]}
+
+
+@pytest.mark.parametrize("prec,dtype,tol", [("f32", "f32", 2e-6), ("bf16", "f32", 1.5e-2),
+                                            ("bf16", "bf16", 1.5e-2),
+                                            ("bf16_split", "bf16", 1.5e-2)])
+@pytest.mark.parametrize("table", sorted(UNIT_TABLES))
+def test_single_term_tables(table, prec, dtype, tol):
+    coeffs = UNIT_TABLES[table]
+    gs_np = [_gen(s, i) for i, s in enumerate(SHAPES)]
+    gin, outs = _run_ns(gs_np, dtype, prec, coefficients=coeffs)
+    for s, g, o in zip(SHAPES, gin, outs):
+        want = oracle.direct_newton_schulz(g, coefficients=coeffs)
+        err = rel_frobenius(o, want)
+        # the identity table only rounds the normalized input
+        lim = 2e-6 if (table == "identity" and dtype == "f32") else (
+            1e-2 if table == "identity" else tol)
+        assert err <= lim, (table, prec, dtype, s, err)
+
+
+@pytest.mark.parametrize("coef", ["quintic", "you"])
+def test_ns_f32_matches_oracle(coef):
+    table = None if coef == "quintic" else oracle.YOU_COEFFICIENTS
+    gs_np = [_gen(s, 10 + i) for i, s in enumerate(SHAPES)]
+    gin, outs = _run_ns(gs_np, "f32", "f32", coefficients=table)
+    for s, g, o in zip(SHAPES, gin, outs):
+        want = oracle.direct_newton_schulz(g, coefficients=table)
+        assert rel_frobenius(o, want) <= 1e-4, (s, rel_frobenius(o, want))
+
+
+@pytest.mark.parametrize("prec", ["bf16_split", "auto"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ns_bf16_matches_oracle(prec, dtype):
+    """iid Gaussian inputs (the hardest spectra for bf16 operands) with hi/lo
+    split operands, which the automatic mode picks for min side <= 1024."""
+    gs_np = [_gen(s, 20 + i) for i, s in enumerate(SHAPES)]
+    gin, outs = _run_ns(gs_np, dtype, prec)
+    for s, g, o in zip(SHAPES, gin, outs):
+        want = oracle.direct_newton_schulz(g)
+        e = rel_frobenius(o, want)
+        d = sigma_dev(o, want)
+        assert e <= 2e-2 and d <= 2e-2, (s, prec, dtype, e, d)
+
+
+@pytest.mark.parametrize("prec", ["bf16", "auto"])
+def test_ns_plain_bf16_large_gaussian(prec):
+    """Plain bf16 operands (what the automatic mode uses above 1024) on an
+    iid Gaussian 1100 x 4400 and its transpose."""
+    gs_np = [_gen((1100, 4400), 60), _gen((4400, 1100), 61)]
+    gin, outs = _run_ns(gs_np, "bf16", prec)
+    for g, o in zip(gin, outs):
+        want = oracle.direct_newton_schulz(g)
+        e = rel_frobenius(o, want)
+        d = sigma_dev(o, want)
+        assert e <= 2e-2 and d <= 2e-2, (g.shape, prec, e, d)
+
+
+def test_ns_c4_packed_batch():
+    """512 small matrices (sides log-uniform in [32, 1024], multiples of 32)
+    in one call, per-matrix tolerance, automatic precision."""
+    cfg = workloads.CONFIGS[4]
+    gs_np = [workloads.grad_np(cfg.grad_kind, m, n, 4, 0, i) for i, (m, n) in enumerate(cfg.shapes)]
+    gin, outs = _run_ns(gs_np, "bf16", "auto")
+    worst_e = worst_d = 0.0
+    for i, (g, o) in enumerate(zip(gin, outs)):
+        want = oracle.direct_newton_schulz(g)
+        e = rel_frobenius(o, want)
+        worst_e = max(worst_e, e)
+        if min(g.shape) <= 256 or i % 8 == 0:
+            worst_d = max(worst_d, sigma_dev(o, want))
+        assert e <= 2e-2, (i, g.shape, e)
+    assert worst_d <= 2e-2, worst_d
+    print(f"c4: worst relF {worst_e:.3e}, worst sigma dev {worst_d:.3e}")
+
+
+@pytest.mark.parametrize("kind,shape", [("lowrank", (1024, 3584)), ("lowrank", (3584, 1024)),
+                                        ("powerlaw_t3", (3584, 1024)),
+                                        ("powerlaw_t3", (1024, 3584))])
+def test_ns_structured_gradients_bf16(kind, shape):
+    """Scaled-down stand-ins of the Llama-8B (low rank + noise) and 70B MLP
+    (power law + Student-t) gradients, bf16 storage, bf16 NS."""
+    g = workloads.grad_np(kind, shape[0], shape[1], 91, 0, 0)
+    gin, outs = _run_ns([g], "bf16", "bf16")
+    want = oracle.direct_newton_schulz(gin[0])
+    e = rel_frobenius(outs[0], want)
+    d = sigma_dev(outs[0], want)
+    assert e <= 2e-2 and d <= 2e-2, (kind, shape, e, d)
+
+
+def test_ns_deterministic_and_in_place():
+    gs_np = [_gen(s, 40 + i) for i, s in enumerate(SHAPES)]
+    gs = [to_dev(g, "bf16") for g in gs_np]
+    a = dm.ns_orthogonalize(gs, prec="bf16")
+    b = dm.ns_orthogonalize(gs, prec="bf16")
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    inp = [g.clone() for g in gs]
+    dm.ns_orthogonalize(inp, outs=inp, prec="bf16")
+    torch.cuda.synchronize()
+    for x, y in zip(a, inp):
+        assert torch.equal(x, y)
+
+
+def test_ns_zero_and_nan():
+    z = torch.zeros(40, 70, device="cuda")
+    n = torch.randn(40, 70, device="cuda")
+    n[3, 5] = float("nan")
+    out = dm.ns_orthogonalize([z, n], prec="f32")
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[0]).item() == 0
+    assert torch.isnan(out[1]).any().item()
+
+
+def test_ns_tiny_shapes():
+    for shape in [(1, 1), (1, 2), (2, 1), (3, 3)]:
+        g = _gen(shape, 50)
+        gin, outs = _run_ns([g], "f32", "f32")
+        want = oracle.direct_newton_schulz(gin[0])
+        assert rel_frobenius(outs[0], want) <= 1e-5, shape

@@ -97,13 +97,13 @@ CONFIGS = {
     1: Config(1, "tinymlp_d256_ff1024_fp32", _tinymlp(256, 1024, 1),
               "f32", "f32", "f32", 1, "gauss"),
     2: Config(2, "tinymlp_d512_ff2048_x4", _tinymlp(512, 2048, 4),
-              "f32", "f32", "bf16", 20, "gauss"),
+              "f32", "f32", "auto", 20, "gauss"),
     3: Config(3, "llama8b_proj_x4", _llama8b(4),
-              "bf16", "bf16", "bf16", 10, "lowrank"),
+              "bf16", "bf16", "auto", 10, "lowrank"),
     4: Config(4, "packed_small_512", c4_shapes(),
               "bf16", "bf16", "auto", 1, "gauss_lognormal", ns_only=True),
     5: Config(5, "llama70b_mlp", ((28672, 8192),) * 4 + ((8192, 28672),) * 2,
-              "bf16", "bf16", "bf16", 3, "powerlaw_t3", nesterov=True),
+              "bf16", "bf16", "auto", 3, "powerlaw_t3", nesterov=True),
 }
 
 
