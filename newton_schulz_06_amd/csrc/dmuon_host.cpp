@@ -28,10 +28,15 @@ dmuon_status_t fail(dmuon_status_t st, const std::string& msg) {
 constexpr int kMaxSteps = 16;
 constexpr int64_t kMaxSide = int64_t(1) << 20;
 constexpr size_t kWsAlign = 256;
-constexpr int kSmallTile = 64;
-constexpr int kLargeTile = 128;
-// Matrices with min side up to this many rows use the 64-wide tile class.
-constexpr int kSmallTileMaxP = 512;
+// GEMM tile classes (square T x T output tiles).  bf16 operands: 64 for
+// min side <= 128, 128 up to 512, 256 above.  fp32 operands: 64 up to 512,
+// 128 above.
+constexpr int kTiles[3] = {64, 128, 256};
+
+int tile_class(int64_t p, bool f32_ops) {
+  if (f32_ops) return p <= 512 ? 64 : 128;
+  return p <= 128 ? 64 : (p <= 512 ? 128 : 256);
+}
 // DMUON_NS_AUTO uses hi/lo split operands up to this min side: plain bf16
 // operands put iid-noise-like spectra of narrow matrices (e.g. 2048 x 512)
 // just past a 2e-2 relative error, while wider ones stay near 1e-2.
@@ -69,7 +74,7 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
     G.transposed = G.m > G.n;
     G.p = std::min(G.m, G.n);
     G.q = std::max(G.m, G.n);
-    G.tile = G.p <= kSmallTileMaxP ? kSmallTile : kLargeTile;
+    G.tile = tile_class(G.p, L.f32_ops);
     G.P = round_up(G.p, G.tile);
     G.Q = round_up(G.q, G.tile);
     if (G.P * G.Q > INT32_MAX || G.Q * 3 > INT32_MAX)
@@ -309,10 +314,9 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   // GEMM tasks, grouped by (kind, tile class).
   std::vector<GemmTask> gtasks;
   const int kinds[3] = {KIND_SYRK, KIND_POLY, KIND_UPDX};
-  const int tiles[2] = {kSmallTile, kLargeTile};
   std::vector<std::pair<size_t, size_t>> ranges;  // [begin, end) in gtasks per launch
   for (int kind : kinds) {
-    for (int tile : tiles) {
+    for (int tile : kTiles) {
       const size_t begin = gtasks.size();
       int acc = 0;
       double flops = 0;

@@ -295,133 +295,13 @@ __device__ __forceinline__ void full_decode(int t, int tiles_m, int tiles_n, int
   tn = w / gsz;
 }
 
-template <int KIND, int T, bool F32>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmTask* __restrict__ tasks,
-                                                   int ntasks, int total_tiles, int iter,
-                                                   float ca, float cb, float cc) {
-  using E = typename std::conditional<F32, float, uint16_t>::type;
-  constexpr int ESZ = sizeof(E);
-  constexpr int BK = 128 / ESZ;           // K elements per stage
-  constexpr int VEC = 16 / ESZ;           // elements per 16-byte chunk
-  constexpr int STRIDE = BK + VEC;        // LDS row stride in elements
-  constexpr int WT = T / 2;               // wave tile
-  constexpr int NT = WT / 32;             // 32x32 MFMA blocks per wave side
-  constexpr int LOADS = T * 8 / 256;      // 16-byte chunks per thread per operand
-  __shared__ __attribute__((aligned(16))) E lds[2][2][T * STRIDE];
-
-  const int vb = xcd_remap(blockIdx.x, gridDim.x);
-  if (vb >= total_tiles) return;
-  const GemmTask& G = tasks[find_task(tasks, ntasks, vb)];
-  const int lt = vb - G.tile_begin;
-  int tm, tn;
-  if (G.tri)
-    tri_decode(lt, G.tiles_m, tm, tn);
-  else
-    full_decode(lt, G.tiles_m, G.tiles_n, tm, tn);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wr = (wave >> 1) * WT;
-  const int wc = (wave & 1) * WT;
-
-  const E* __restrict__ Lp = static_cast<const E*>(G.L) + (size_t)tm * T * G.ldl;
-  const E* __restrict__ Rp =
-      static_cast<const E*>((iter & 1) ? G.R1 : G.R0) + (size_t)tn * T * G.ldr;
-  const int ldl = G.ldl, ldr = G.ldr, kper = G.kper;
-  const int nk = G.K / BK;
-
-  uint4 regL[LOADS], regR[LOADS];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-    const int kr = k0 % kper;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3;
-      const int col = (c & 7) * VEC;
-      regL[i] = *reinterpret_cast<const uint4*>(Lp + (size_t)row * ldl + k0 + col);
-      regR[i] = *reinterpret_cast<const uint4*>(Rp + (size_t)row * ldr + kr + col);
-    }
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3;
-      const int col = (c & 7) * VEC;
-      *reinterpret_cast<uint4*>(&lds[st][0][row * STRIDE + col]) = regL[i];
-      *reinterpret_cast<uint4*>(&lds[st][1][row * STRIDE + col]) = regR[i];
-    }
-  };
-
-  f32x16 acc[NT][NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  auto compute = [&](int st) {
-    const E* sL = lds[st][0];
-    const E* sR = lds[st][1];
-    const int lrow = lane & 31;
-    const int khalf = lane >> 5;
-    if constexpr (!F32) {
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8 a[NT], b[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          a[t] = *reinterpret_cast<const bf16x8*>(
-              &sL[(wr + t * 32 + lrow) * STRIDE + ks * 16 + khalf * 8]);
-          b[t] = *reinterpret_cast<const bf16x8*>(
-              &sR[(wc + t * 32 + lrow) * STRIDE + ks * 16 + khalf * 8]);
-        }
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    } else {
-      // fp32: each lane reads 4 consecutive k; instruction t of a group
-      // takes element t, so lane half h covers k = 8*ks + 4*h + t.
-#pragma unroll
-      for (int ks = 0; ks < BK / 8; ++ks) {
-        f32x4 a[NT], b[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          a[t] = *reinterpret_cast<const f32x4*>(
-              &sL[(wr + t * 32 + lrow) * STRIDE + ks * 8 + khalf * 4]);
-          b[t] = *reinterpret_cast<const f32x4*>(
-              &sR[(wc + t * 32 + lrow) * STRIDE + ks * 8 + khalf * 4]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
-      }
-    }
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    compute(st);
-    if (kt + 1 < nk) sstore(st ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue.  32x32 MFMA output: lane l, register r holds row
-  // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its block.
+// Kind-specific epilogue of one T x T output tile.  32x32 MFMA output
+// layout: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4 and column
+// l%32 of its block.
+template <int KIND, int T, bool F32, int NT>
+__device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm, int tn,
+                                         int wr, int wc, int lane, int iter, float ca, float cb,
+                                         float cc) {
   const int row_base = tm * T + wr + 4 * (lane >> 5);
   const int col_base = tn * T + wc + (lane & 31);
   const bool mirror = G.tri && (tm != tn);
@@ -559,6 +439,269 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmTask* __restrict__ 
       }
 }
 
+template <int KIND, int T, bool F32>
+__global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restrict__ tasks,
+                                                   int ntasks, int total_tiles, int iter,
+                                                   float ca, float cb, float cc) {
+  using E = typename std::conditional<F32, float, uint16_t>::type;
+  constexpr int ESZ = sizeof(E);
+  constexpr int BK = 128 / ESZ;           // K elements per stage
+  constexpr int VEC = 16 / ESZ;           // elements per 16-byte chunk
+  constexpr int STRIDE = BK + VEC;        // LDS row stride in elements
+  constexpr int WT = T / 2;               // wave tile
+  constexpr int NT = WT / 32;             // 32x32 MFMA blocks per wave side
+  constexpr int LOADS = T * 8 / 256;      // 16-byte chunks per thread per operand
+  __shared__ __attribute__((aligned(16))) E lds[2][2][T * STRIDE];
+
+  const int vb = xcd_remap(blockIdx.x, gridDim.x);
+  if (vb >= total_tiles) return;
+  const GemmTask& G = tasks[find_task(tasks, ntasks, vb)];
+  const int lt = vb - G.tile_begin;
+  int tm, tn;
+  if (G.tri)
+    tri_decode(lt, G.tiles_m, tm, tn);
+  else
+    full_decode(lt, G.tiles_m, G.tiles_n, tm, tn);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = (wave >> 1) * WT;
+  const int wc = (wave & 1) * WT;
+
+  const E* __restrict__ Lp = static_cast<const E*>(G.L) + (size_t)tm * T * G.ldl;
+  const E* __restrict__ Rp =
+      static_cast<const E*>((iter & 1) ? G.R1 : G.R0) + (size_t)tn * T * G.ldr;
+  const int ldl = G.ldl, ldr = G.ldr, kper = G.kper;
+  const int nk = G.K / BK;
+
+  uint4 regL[LOADS], regR[LOADS];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+    const int kr = k0 % kper;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 3;
+      const int col = (c & 7) * VEC;
+      regL[i] = *reinterpret_cast<const uint4*>(Lp + (size_t)row * ldl + k0 + col);
+      regR[i] = *reinterpret_cast<const uint4*>(Rp + (size_t)row * ldr + kr + col);
+    }
+  };
+  auto sstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 3;
+      const int col = (c & 7) * VEC;
+      *reinterpret_cast<uint4*>(&lds[st][0][row * STRIDE + col]) = regL[i];
+      *reinterpret_cast<uint4*>(&lds[st][1][row * STRIDE + col]) = regR[i];
+    }
+  };
+
+  f32x16 acc[NT][NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](int st) {
+    const E* sL = lds[st][0];
+    const E* sR = lds[st][1];
+    const int lrow = lane & 31;
+    const int khalf = lane >> 5;
+    if constexpr (!F32) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8 a[NT], b[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          a[t] = *reinterpret_cast<const bf16x8*>(
+              &sL[(wr + t * 32 + lrow) * STRIDE + ks * 16 + khalf * 8]);
+          b[t] = *reinterpret_cast<const bf16x8*>(
+              &sR[(wc + t * 32 + lrow) * STRIDE + ks * 16 + khalf * 8]);
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    } else {
+      // fp32: each lane reads 4 consecutive k; instruction t of a group
+      // takes element t, so lane half h covers k = 8*ks + 4*h + t.
+#pragma unroll
+      for (int ks = 0; ks < BK / 8; ++ks) {
+        f32x4 a[NT], b[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          a[t] = *reinterpret_cast<const f32x4*>(
+              &sL[(wr + t * 32 + lrow) * STRIDE + ks * 8 + khalf * 4]);
+          b[t] = *reinterpret_cast<const f32x4*>(
+              &sR[(wc + t * 32 + lrow) * STRIDE + ks * 8 + khalf * 4]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    compute(st);
+    if (kt + 1 < nk) sstore(st ^ 1);
+    __syncthreads();
+  }
+
+  epilogue<KIND, T, F32, NT>(G, acc, tm, tn, wr, wc, lane, iter, ca, cb, cc);
+}
+
+// bf16 main loop fed by direct global->LDS loads (global_load_lds_dwordx4):
+// STAGES buffers of K = 32 per stage (64-byte rows) are kept in flight, so
+// each K-step's loads were issued STAGES-1 steps before they are consumed.
+// Rows are stored without padding; the 16-byte chunk of k-slot `kc` of row
+// r lives at slot kc ^ swz(r), which makes the 16-byte operand reads of 16
+// consecutive rows hit distinct bank groups (and 8 rows for 32 banks).
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// 16 bytes per lane from global memory straight into LDS at the wave-uniform
+// base `lds` (lane l lands at lds + 16*l).  Kept out of the kernel templates:
+// the host compilation pass cannot type-check this builtin, and inside a
+// kernel body that silently drops the kernel's host-side launch stub.
+__device__ void lds_dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at no-wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int KIND, int T>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restrict__ tasks,
+                                                        int ntasks, int total_tiles, int iter,
+                                                        float ca, float cb, float cc) {
+  constexpr int STAGES = 4;
+  constexpr int BK = 32;                  // bf16 per row per stage (64 bytes)
+  constexpr int WT = T / 2;               // wave tile (2 x 2 waves)
+  constexpr int NT = WT / 32;             // 32x32 MFMA blocks per wave side
+  constexpr int LPW = T / 64;             // 1 KB load instructions per wave per operand
+  constexpr int LOADS = 2 * LPW;          // loads per thread per stage
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES][2][T * BK];
+
+  const int vb = xcd_remap(blockIdx.x, gridDim.x);
+  if (vb >= total_tiles) return;
+  const GemmTask& G = tasks[find_task(tasks, ntasks, vb)];
+  const int lt = vb - G.tile_begin;
+  int tm, tn;
+  if (G.tri)
+    tri_decode(lt, G.tiles_m, tm, tn);
+  else
+    full_decode(lt, G.tiles_m, G.tiles_n, tm, tn);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = (wave >> 1) * WT;
+  const int wc = (wave & 1) * WT;
+  const int nk = G.K / BK;
+  const int kper = G.kper;
+
+  // Per-lane global source of each load instruction: chunk c of the stage
+  // (row c/4, slot c%4) holds global k-chunk slot ^ swz(row).
+  const uint16_t* srcL[LPW];
+  const uint16_t* srcR[LPW];
+  {
+    const uint16_t* Lp = static_cast<const uint16_t*>(G.L) + (size_t)tm * T * G.ldl;
+    const uint16_t* Rp =
+        static_cast<const uint16_t*>((iter & 1) ? G.R1 : G.R0) + (size_t)tn * T * G.ldr;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int c = (wave * LPW + i) * 64 + lane;
+      const int row = c >> 2;
+      const int kc = (c & 3) ^ swz(row);
+      srcL[i] = Lp + (size_t)row * G.ldl + kc * 8;
+      srcR[i] = Rp + (size_t)row * G.ldr + kc * 8;
+    }
+  }
+  auto issue = [&](int kt) {
+    const int st = kt % STAGES;
+    const int k0 = kt * BK;
+    const int kr = k0 % kper;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      lds_dma16(srcL[i] + k0, &lds[st][0][(wave * LPW + i) * 512]);
+      lds_dma16(srcR[i] + kr, &lds[st][1][(wave * LPW + i) * 512]);
+    }
+  };
+
+  f32x16 acc[NT][NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Operand read offsets (elements) inside a stage buffer, per k-substep.
+  int offA[2][NT], offB[2][NT];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int kc = ks * 2 + (lane >> 5);
+      const int ra = wr + t * 32 + (lane & 31);
+      const int rb = wc + t * 32 + (lane & 31);
+      offA[ks][t] = ra * BK + 8 * (kc ^ swz(ra));
+      offB[ks][t] = rb * BK + 8 * (kc ^ swz(rb));
+    }
+
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt must have landed: allow the younger stages to stay in flight.
+    const int younger = min(nk - 1 - kt, STAGES - 2);
+    if (younger >= 2) wait_vmcnt<2 * LOADS>();
+    else if (younger == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    const uint16_t* sa = lds[kt % STAGES][0];
+    const uint16_t* sb = lds[kt % STAGES][1];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[NT], b[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        a[t] = *reinterpret_cast<const bf16x8*>(sa + offA[ks][t]);
+        b[t] = *reinterpret_cast<const bf16x8*>(sb + offB[ks][t]);
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  epilogue<KIND, T, false, NT>(G, acc, tm, tn, wr, wc, lane, iter, ca, cb, cc);
+}
+
 // --------------------------------------------------------------------------
 // Update / output pass over 64 x 64 tiles of the caller's layout.
 //   O[r][c] = X[r][c] (wide) or X[c][r] (tall, staged through LDS)
@@ -623,11 +766,20 @@ __global__ __launch_bounds__(EW_THREADS) void update_kernel(
   }
 }
 
-template <int KIND, int T, bool F32>
-hipError_t launch_gemm_t(const GemmTask* tasks, int ntasks, int total_tiles, int iter, float a,
-                         float b, float c, hipStream_t s) {
+template <int KIND, int T>
+hipError_t launch_gemm_f32(const GemmTask* tasks, int ntasks, int total_tiles, int iter, float a,
+                           float b, float c, hipStream_t s) {
   const int grid = (total_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_kernel<KIND, T, F32>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
+  hipLaunchKernelGGL((gemm_reg_kernel<KIND, T, true>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
+                     total_tiles, iter, a, b, c);
+  return hipGetLastError();
+}
+
+template <int KIND, int T>
+hipError_t launch_gemm_bf16(const GemmTask* tasks, int ntasks, int total_tiles, int iter, float a,
+                            float b, float c, hipStream_t s) {
+  const int grid = (total_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_bf16_kernel<KIND, T>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
                      total_tiles, iter, a, b, c);
   return hipGetLastError();
 }
@@ -635,12 +787,14 @@ hipError_t launch_gemm_t(const GemmTask* tasks, int ntasks, int total_tiles, int
 template <int KIND>
 hipError_t launch_gemm_k(int tile, int f32_ops, const GemmTask* tasks, int ntasks,
                          int total_tiles, int iter, float a, float b, float c, hipStream_t s) {
-  if (tile == 64)
-    return f32_ops ? launch_gemm_t<KIND, 64, true>(tasks, ntasks, total_tiles, iter, a, b, c, s)
-                   : launch_gemm_t<KIND, 64, false>(tasks, ntasks, total_tiles, iter, a, b, c, s);
-  if (tile == 128)
-    return f32_ops ? launch_gemm_t<KIND, 128, true>(tasks, ntasks, total_tiles, iter, a, b, c, s)
-                   : launch_gemm_t<KIND, 128, false>(tasks, ntasks, total_tiles, iter, a, b, c, s);
+  if (f32_ops) {
+    if (tile == 64) return launch_gemm_f32<KIND, 64>(tasks, ntasks, total_tiles, iter, a, b, c, s);
+    if (tile == 128) return launch_gemm_f32<KIND, 128>(tasks, ntasks, total_tiles, iter, a, b, c, s);
+    return hipErrorInvalidValue;
+  }
+  if (tile == 64) return launch_gemm_bf16<KIND, 64>(tasks, ntasks, total_tiles, iter, a, b, c, s);
+  if (tile == 128) return launch_gemm_bf16<KIND, 128>(tasks, ntasks, total_tiles, iter, a, b, c, s);
+  if (tile == 256) return launch_gemm_bf16<KIND, 256>(tasks, ntasks, total_tiles, iter, a, b, c, s);
   return hipErrorInvalidValue;
 }
 

@@ -59,7 +59,10 @@ def _expected_ws(shapes, prec):
     per = []
     for m, n in shapes:
         p, q = min(m, n), max(m, n)
-        t = 64 if p <= 512 else 128
+        if prec == "f32":
+            t = 64 if p <= 512 else 128
+        else:
+            t = 64 if p <= 128 else (128 if p <= 512 else 256)
         P, Q = _pad(p, t), _pad(q, t)
         tiles += (P // 64) * (Q // 64)
         split = prec == "bf16_split" or (prec == "auto" and p <= 1024)
