@@ -47,11 +47,22 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 size_t esize(int dtype) { return dtype == DMUON_F32 ? 4 : 2; }
 
+// Row stride (elements) for a workspace matrix with `n` columns of `esz`
+// bytes: rounded up to an odd multiple of 256 bytes, so that consecutive
+// rows start in different L2 channels (the NS shapes are multiples of large
+// powers of two; unpadded, all rows of a tile would share one channel).
+int64_t ld_for(int64_t n, int64_t esz) {
+  int64_t units = (n * esz + 255) / 256;
+  if (units % 2 == 0) ++units;
+  return units * 256 / esz;
+}
+
 // Shape-derived geometry of one matrix in the workspace.
 struct Geom {
   int64_t m, n, p, q, P, Q;
   int tile, transposed, split;
-  size_t xm, xb, xt0, xt1, a32, aop, r3, bop;  // byte offsets in ws
+  int64_t ld_xm, ld_xb, ld_xt, ld_a32, ld_aop, ld_bop;  // row strides (elements)
+  size_t xm, xb, xt0, xt1, a32, aop, r3, bop;          // byte offsets in ws
 };
 
 struct Layout {
@@ -77,7 +88,8 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
     G.tile = tile_class(G.p, L.f32_ops);
     G.P = round_up(G.p, G.tile);
     G.Q = round_up(G.q, G.tile);
-    if (G.P * G.Q > INT32_MAX || G.Q * 3 > INT32_MAX)
+    if (G.P * ld_for(G.Q, 4) > INT32_MAX || G.Q * ld_for(G.P, 4) > INT32_MAX ||
+        G.P * ld_for(3 * G.P, 2) > INT32_MAX)
       return fail(DMUON_E_UNSUPPORTED, "matrix " + std::to_string(i) +
                                            ": padded size exceeds 2^31 elements");
     G.split = (prec == DMUON_NS_BF16_SPLIT) ||
@@ -91,32 +103,42 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
   off = align_up(off + sizeof(float) * (size_t)tiles, kWsAlign);
   L.scale_off = off;
   off = align_up(off + sizeof(float) * 4 * (size_t)n, kWsAlign);
-  const size_t e = L.f32_ops ? 4 : 2;
+  const int64_t e = L.f32_ops ? 4 : 2;
   for (int i = 0; i < n; ++i) {
     Geom& G = L.g[i];
-    const size_t PQ = (size_t)G.P * G.Q, PP = (size_t)G.P * G.P;
     auto take = [&](size_t bytes) {
       const size_t o = off;
       off = align_up(off + bytes, kWsAlign);
       return o;
     };
-    G.xm = take(4 * PQ);
-    G.xb = L.f32_ops ? 0 : take(2 * PQ);
-    G.xt0 = take(e * PQ);
-    G.xt1 = take(e * PQ);
-    G.a32 = take(4 * PP);
+    const size_t P = (size_t)G.P, Q = (size_t)G.Q;
+    G.ld_xm = ld_for(G.Q, 4);
+    G.ld_xb = ld_for(G.Q, 2);
+    G.ld_xt = ld_for(G.P, e);
+    G.ld_a32 = ld_for(G.P, 4);
+    G.xm = take(4 * P * G.ld_xm);
+    G.xb = L.f32_ops ? 0 : take(2 * P * G.ld_xb);
+    G.xt0 = take(e * Q * G.ld_xt);
+    G.xt1 = take(e * Q * G.ld_xt);
+    G.a32 = take(4 * P * G.ld_a32);
     if (L.f32_ops) {
       G.aop = G.a32;
+      G.ld_aop = G.ld_a32;
       G.r3 = 0;
-      G.bop = take(4 * PP);
+      G.ld_bop = ld_for(G.P, 4);
+      G.bop = take(4 * P * G.ld_bop);
     } else if (G.split) {
-      G.aop = take(2 * 3 * PP);
-      G.r3 = take(2 * 3 * PP);
-      G.bop = take(2 * 2 * PP);
+      G.ld_aop = ld_for(3 * G.P, 2);
+      G.aop = take(2 * P * G.ld_aop);
+      G.r3 = take(2 * P * G.ld_aop);
+      G.ld_bop = ld_for(2 * G.P, 2);
+      G.bop = take(2 * P * G.ld_bop);
     } else {
-      G.aop = take(2 * PP);
+      G.ld_aop = ld_for(G.P, 2);
+      G.aop = take(2 * P * G.ld_aop);
       G.r3 = 0;
-      G.bop = take(2 * PP);
+      G.ld_bop = ld_for(G.P, 2);
+      G.bop = take(2 * P * G.ld_bop);
     }
   }
   L.total = off;
@@ -266,8 +288,9 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
     t.transposed = G.transposed;
     t.in_dtype = src->dtype;
     t.out_dtype = dst->dtype;
-    t.ldx = (int32_t)G.Q;
-    t.ldt = (int32_t)G.P;
+    t.ldx = (int32_t)G.ld_xm;
+    t.ldxb = (int32_t)G.ld_xb;
+    t.ldt = (int32_t)G.ld_xt;
     t.f32_ops = L.f32_ops;
     t.src = src->mats[i].ptr;
     t.buf = bufs ? static_cast<float*>(bufs->mats[i].ptr) : nullptr;
@@ -333,36 +356,36 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
         if (kind == KIND_SYRK) {
           t.L = ws + (L.f32_ops ? G.xm : G.xb);
           t.R0 = t.R1 = t.L;
-          t.ldl = t.ldr = Q;
+          t.ldl = t.ldr = (int32_t)(L.f32_ops ? G.ld_xm : G.ld_xb);
           t.K = t.kper = Q;
           t.tiles_m = t.tiles_n = nt;
           t.tri = 1;
           t.tile_count = nt * (nt + 1) / 2;
           t.fbuf = reinterpret_cast<float*>(ws + G.a32);
-          t.ld_f = P;
+          t.ld_f = (int32_t)G.ld_a32;
           t.out0 = L.f32_ops ? nullptr : ws + G.aop;
           t.out1 = t.split ? ws + G.r3 : nullptr;
-          t.ld0 = t.ld1 = t.split ? 3 * P : P;
+          t.ld0 = t.ld1 = (int32_t)G.ld_aop;
           flops += p * (p + 1) * q;
         } else if (kind == KIND_POLY) {
           t.L = ws + G.aop;
           t.R0 = t.R1 = t.split ? ws + G.r3 : ws + G.aop;
-          t.ldl = t.ldr = t.split ? 3 * P : P;
+          t.ldl = t.ldr = (int32_t)G.ld_aop;
           t.K = t.kper = t.split ? 3 * P : P;
           t.tiles_m = t.tiles_n = nt;
           t.tri = 1;
           t.tile_count = nt * (nt + 1) / 2;
           t.fbuf = reinterpret_cast<float*>(ws + G.a32);
-          t.ld_f = P;
+          t.ld_f = (int32_t)G.ld_a32;
           t.out0 = ws + G.bop;
-          t.ld0 = t.split ? 2 * P : P;
+          t.ld0 = (int32_t)G.ld_bop;
           flops += p * p * (p + 1);
         } else {
           t.L = ws + G.bop;
           t.R0 = ws + G.xt0;
           t.R1 = ws + G.xt1;
-          t.ldl = t.split ? 2 * P : P;
-          t.ldr = P;
+          t.ldl = (int32_t)G.ld_bop;
+          t.ldr = (int32_t)G.ld_xt;
           t.K = t.split ? 2 * P : P;
           t.kper = P;
           t.tiles_m = nt;
@@ -370,12 +393,12 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.tri = 0;
           t.tile_count = t.tiles_m * t.tiles_n;
           t.fbuf = reinterpret_cast<float*>(ws + G.xm);
-          t.ld_f = Q;
+          t.ld_f = (int32_t)G.ld_xm;
           t.out0 = L.f32_ops ? nullptr : ws + G.xb;
-          t.ld0 = Q;
+          t.ld0 = (int32_t)G.ld_xb;
           t.out1 = ws + G.xt0;
           t.out2 = ws + G.xt1;
-          t.ld1 = P;
+          t.ld1 = (int32_t)G.ld_xt;
           flops += 2.0 * p * p * q;
         }
         t.tile_begin = acc;

@@ -37,10 +37,12 @@ struct EwTask {
   int32_t transposed;      // m > n: the oriented X is the transpose
   int32_t in_dtype;        // dtype of `src` (grad / input G)
   int32_t out_dtype;       // dtype of `dst` (param / output)
-  int32_t ldx;             // row stride of xm / xb (padded q)
-  int32_t ldt;             // row stride of xt (padded p)
+  int32_t ldx;             // row stride of xm (elements)
+  int32_t ldxb;            // row stride of xb (elements)
+  int32_t ldt;             // row stride of xt (elements)
   int32_t f32_ops;         // 1: xt holds fp32 (NS in fp32), 0: bf16
   int32_t vec;             // 1: caller buffers allow 16-byte (4-element) access
+  int32_t pad_;
   const void* src;         // grad (step) or G (NS only)
   float* buf;              // momentum buffer (step) or null
   void* dst;               // param (update) or output (NS only)

@@ -170,10 +170,10 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
     }
     // Same-layout copy: X itself for a wide matrix, X^T for a tall one.
     if (!T.transposed) {
-      const size_t o = (size_t)gr * T.ldx + gc;
-      *reinterpret_cast<f32x4*>(T.xm + o) = u;
+      *reinterpret_cast<f32x4*>(T.xm + (size_t)gr * T.ldx + gc) = u;
       if (!f32ops)
-        *reinterpret_cast<uint2*>(T.xb + o) = pack_bf16x4(u[0], u[1], u[2], u[3]);
+        *reinterpret_cast<uint2*>(T.xb + (size_t)gr * T.ldxb + gc) =
+            pack_bf16x4(u[0], u[1], u[2], u[3]);
     } else {
       const size_t o = (size_t)gr * T.ldt + gc;
       if (f32ops)
@@ -200,10 +200,10 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(T.xt) + o) =
             pack_bf16x4(v[0], v[1], v[2], v[3]);
     } else {
-      const size_t o = (size_t)orow * T.ldx + ocol;
-      *reinterpret_cast<f32x4*>(T.xm + o) = v;
+      *reinterpret_cast<f32x4*>(T.xm + (size_t)orow * T.ldx + ocol) = v;
       if (!f32ops)
-        *reinterpret_cast<uint2*>(T.xb + o) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<uint2*>(T.xb + (size_t)orow * T.ldxb + ocol) =
+            pack_bf16x4(v[0], v[1], v[2], v[3]);
     }
   }
   // Block sum of squares, fixed order.
@@ -301,7 +301,9 @@ __device__ __forceinline__ void full_decode(int t, int tiles_m, int tiles_n, int
 template <int KIND, int T, bool F32, int NT>
 __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm, int tn,
                                          int wr, int wc, int lane, int iter, float ca, float cb,
-                                         float cc) {
+                                         float cc, uint16_t* stage) {
+  constexpr bool kStageXT = (KIND == KIND_UPDX) && !F32;
+  if constexpr (kStageXT) __syncthreads();  // main-loop LDS reads are done
   const int row_base = tm * T + wr + 4 * (lane >> 5);
   const int col_base = tn * T + wc + (lane & 31);
   const bool mirror = G.tri && (tm != tn);
@@ -432,11 +434,33 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
             const int ld0 = G.ld0;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) xb[(size_t)(gi + rr) * ld0 + gj] = to_bf16(v[rr]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(xt_next) + (size_t)gj * ld1 + gi) =
-                pack_bf16x4(v[0], v[1], v[2], v[3]);
+            // X^T goes through LDS (transposed, 8-byte groups XOR-swizzled)
+            // so that it leaves the tile as full rows.
+            const int il = gi - tm * T, jl = gj - tn * T;
+            const int x = 4 * (jl & (T / 4 - 1));
+            *reinterpret_cast<uint2*>(stage + jl * T + (il ^ x)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+            (void)xt_next;
+            (void)ld1;
           }
         }
       }
+  if constexpr (kStageXT) {
+    __syncthreads();
+    uint16_t* xt = static_cast<uint16_t*>((iter & 1) ? G.out1 : G.out2);
+    const int ld1 = G.ld1;
+    constexpr int CPR = T / 8;            // 16-byte chunks per row
+    constexpr int RPP = 256 / CPR;        // rows per pass of the block
+    const int tid = threadIdx.x;
+    const int c = tid % CPR;
+#pragma unroll 4
+    for (int jl = tid / CPR; jl < T; jl += RPP) {
+      const int x = 4 * (jl & (T / 4 - 1));
+      const int pos = (8 * c) ^ x;
+      uint4 w = *reinterpret_cast<const uint4*>(stage + jl * T + (pos & ~7));
+      if (pos & 4) { const uint32_t a = w.x, b = w.y; w.x = w.z; w.y = w.w; w.z = a; w.w = b; }
+      *reinterpret_cast<uint4*>(xt + (size_t)(tn * T + jl) * ld1 + tm * T + 8 * c) = w;
+    }
+  }
 }
 
 template <int KIND, int T, bool F32>
@@ -564,7 +588,7 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
     __syncthreads();
   }
 
-  epilogue<KIND, T, F32, NT>(G, acc, tm, tn, wr, wc, lane, iter, ca, cb, cc);
+  epilogue<KIND, T, F32, NT>(G, acc, tm, tn, wr, wc, lane, iter, ca, cb, cc, nullptr);
 }
 
 // bf16 main loop fed by direct global->LDS loads (global_load_lds_dwordx4):
@@ -699,7 +723,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
     }
   }
 
-  epilogue<KIND, T, false, NT>(G, acc, tm, tn, wr, wc, lane, iter, ca, cb, cc);
+  epilogue<KIND, T, false, NT>(G, acc, tm, tn, wr, wc, lane, iter, ca, cb, cc, &lds[0][0][0]);
 }
 
 // --------------------------------------------------------------------------

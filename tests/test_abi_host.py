@@ -50,10 +50,18 @@ def _pad(x, t):
     return (x + t - 1) // t * t
 
 
+def _ld(n, esz):
+    """Row stride: an odd multiple of 256 bytes."""
+    u = -(-n * esz // 256)
+    if u % 2 == 0:
+        u += 1
+    return u * 256 // esz
+
+
 def _expected_ws(shapes, prec):
     """Workspace rule: partials + scales, then per matrix X master, bf16 X,
     two X^T buffers, fp32 A and the operand copies of A and B, each rounded
-    to 256 bytes."""
+    to 256 bytes, rows padded to odd multiples of 256 bytes."""
     a = lambda x: _pad(x, 256)  # noqa: E731
     tiles = 0
     per = []
@@ -67,11 +75,15 @@ def _expected_ws(shapes, prec):
         tiles += (P // 64) * (Q // 64)
         split = prec == "bf16_split" or (prec == "auto" and p <= 1024)
         if prec == "f32":
-            per.append(a(4 * P * Q) + 2 * a(4 * P * Q) + a(4 * P * P) + a(4 * P * P))
+            per.append(a(4 * P * _ld(Q, 4)) + 2 * a(4 * Q * _ld(P, 4)) + a(4 * P * _ld(P, 4))
+                       + a(4 * P * _ld(P, 4)))
         else:
-            aop = 2 * a(6 * P * P) if split else a(2 * P * P)
-            bop = a(4 * P * P) if split else a(2 * P * P)
-            per.append(a(4 * P * Q) + a(2 * P * Q) + 2 * a(2 * P * Q) + a(4 * P * P) + aop + bop)
+            base = a(4 * P * _ld(Q, 4)) + a(2 * P * _ld(Q, 2)) + 2 * a(2 * Q * _ld(P, 2)) \
+                + a(4 * P * _ld(P, 4))
+            if split:
+                per.append(base + 2 * a(2 * P * _ld(3 * P, 2)) + a(2 * P * _ld(2 * P, 2)))
+            else:
+                per.append(base + a(2 * P * _ld(P, 2)) + a(2 * P * _ld(P, 2)))
     return a(4 * tiles) + a(16 * len(shapes)) + sum(per)
 
 
