@@ -33,24 +33,46 @@ __device__ __forceinline__ float from_bf16(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }
 
+// Global-memory accessors.  Device pointers reach the kernels through task
+// tables, where the compiler cannot prove their address space; without an
+// explicit global (address space 1) access it emits flat instructions,
+// which also wait on the LDS counter.
+#define GMEM __attribute__((address_space(1)))
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float ld_f32(const float* p) { return *(const GMEM float*)p; }
+__device__ __forceinline__ void st_f32(float* p, float v) { *(GMEM float*)p = v; }
+__device__ __forceinline__ f32x4 ld_f32x4(const float* p) { return *(const GMEM f32x4*)p; }
+__device__ __forceinline__ void st_f32x4(float* p, f32x4 v) { *(GMEM f32x4*)p = v; }
+__device__ __forceinline__ uint16_t ld_u16(const uint16_t* p) { return *(const GMEM uint16_t*)p; }
+__device__ __forceinline__ void st_u16(uint16_t* p, uint16_t v) { *(GMEM uint16_t*)p = v; }
+__device__ __forceinline__ u32x2 ld_u32x2(const uint16_t* p) { return *(const GMEM u32x2*)p; }
+__device__ __forceinline__ void st_u32x2(uint16_t* p, u32x2 v) { *(GMEM u32x2*)p = v; }
+__device__ __forceinline__ void st_u32x4(uint16_t* p, u32x4 v) { *(GMEM u32x4*)p = v; }
+__device__ __forceinline__ uint4 ld_u128(const void* p) {
+  const u32x4 w = *(const GMEM u32x4*)p;
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 __device__ __forceinline__ float load1(const void* base, int dtype, size_t i) {
-  return dtype == 0 ? static_cast<const float*>(base)[i]
-                    : from_bf16(static_cast<const uint16_t*>(base)[i]);
+  return dtype == 0 ? ld_f32(static_cast<const float*>(base) + i)
+                    : from_bf16(ld_u16(static_cast<const uint16_t*>(base) + i));
 }
 
 __device__ __forceinline__ void store1(void* base, int dtype, size_t i, float v) {
   if (dtype == 0)
-    static_cast<float*>(base)[i] = v;
+    st_f32(static_cast<float*>(base) + i, v);
   else
-    static_cast<uint16_t*>(base)[i] = to_bf16(v);
+    st_u16(static_cast<uint16_t*>(base) + i, to_bf16(v));
 }
 
 __device__ __forceinline__ f32x4 load4(const void* base, int dtype, size_t i) {
   f32x4 r;
   if (dtype == 0) {
-    r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i);
+    r = ld_f32x4(static_cast<const float*>(base) + i);
   } else {
-    uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
+    const u32x2 w = ld_u32x2(static_cast<const uint16_t*>(base) + i);
     r[0] = __uint_as_float(w.x << 16);
     r[1] = __uint_as_float(w.x & 0xffff0000u);
     r[2] = __uint_as_float(w.y << 16);
@@ -59,8 +81,8 @@ __device__ __forceinline__ f32x4 load4(const void* base, int dtype, size_t i) {
   return r;
 }
 
-__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
-  uint2 w;
+__device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d) {
+  u32x2 w;
   w.x = (uint32_t)to_bf16(a) | ((uint32_t)to_bf16(b) << 16);
   w.y = (uint32_t)to_bf16(c) | ((uint32_t)to_bf16(d) << 16);
   return w;
@@ -68,10 +90,9 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
 
 __device__ __forceinline__ void store4(void* base, int dtype, size_t i, f32x4 v) {
   if (dtype == 0)
-    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + i) = v;
+    st_f32x4(static_cast<float*>(base) + i, v);
   else
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + i) =
-        pack_bf16x4(v[0], v[1], v[2], v[3]);
+    st_u32x2(static_cast<uint16_t*>(base) + i, pack_bf16x4(v[0], v[1], v[2], v[3]));
 }
 
 // Last task whose tile_begin <= tile (tasks are sorted by tile_begin).
@@ -138,14 +159,14 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
         if (ns_only) {
           u = g;
         } else {
-          const f32x4 b = *reinterpret_cast<const f32x4*>(T.buf + idx);
+          const f32x4 b = ld_f32x4(T.buf + idx);
           f32x4 bn;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             bn[e] = fmaf(mu, b[e], g[e]);
             u[e] = nesterov ? fmaf(mu, bn[e], g[e]) : bn[e];
           }
-          *reinterpret_cast<f32x4*>(T.buf + idx) = bn;
+          st_f32x4(T.buf + idx, bn);
         }
       } else {
 #pragma unroll
@@ -155,8 +176,8 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
             if (ns_only) {
               u[e] = g;
             } else {
-              const float bn = fmaf(mu, T.buf[idx + e], g);
-              T.buf[idx + e] = bn;
+              const float bn = fmaf(mu, ld_f32(T.buf + idx + e), g);
+              st_f32(T.buf + idx + e, bn);
               u[e] = nesterov ? fmaf(mu, bn, g) : bn;
             }
           }
@@ -170,17 +191,15 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
     }
     // Same-layout copy: X itself for a wide matrix, X^T for a tall one.
     if (!T.transposed) {
-      *reinterpret_cast<f32x4*>(T.xm + (size_t)gr * T.ldx + gc) = u;
+      st_f32x4(T.xm + (size_t)gr * T.ldx + gc, u);
       if (!f32ops)
-        *reinterpret_cast<uint2*>(T.xb + (size_t)gr * T.ldxb + gc) =
-            pack_bf16x4(u[0], u[1], u[2], u[3]);
+        st_u32x2(T.xb + (size_t)gr * T.ldxb + gc, pack_bf16x4(u[0], u[1], u[2], u[3]));
     } else {
       const size_t o = (size_t)gr * T.ldt + gc;
       if (f32ops)
-        *reinterpret_cast<f32x4*>(static_cast<float*>(T.xt) + o) = u;
+        st_f32x4(static_cast<float*>(T.xt) + o, u);
       else
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(T.xt) + o) =
-            pack_bf16x4(u[0], u[1], u[2], u[3]);
+        st_u32x2(static_cast<uint16_t*>(T.xt) + o, pack_bf16x4(u[0], u[1], u[2], u[3]));
     }
   }
   __syncthreads();
@@ -195,15 +214,13 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
     if (!T.transposed) {
       const size_t o = (size_t)orow * T.ldt + ocol;
       if (f32ops)
-        *reinterpret_cast<f32x4*>(static_cast<float*>(T.xt) + o) = v;
+        st_f32x4(static_cast<float*>(T.xt) + o, v);
       else
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(T.xt) + o) =
-            pack_bf16x4(v[0], v[1], v[2], v[3]);
+        st_u32x2(static_cast<uint16_t*>(T.xt) + o, pack_bf16x4(v[0], v[1], v[2], v[3]));
     } else {
-      *reinterpret_cast<f32x4*>(T.xm + (size_t)orow * T.ldx + ocol) = v;
+      st_f32x4(T.xm + (size_t)orow * T.ldx + ocol, v);
       if (!f32ops)
-        *reinterpret_cast<uint2*>(T.xb + (size_t)orow * T.ldxb + ocol) =
-            pack_bf16x4(v[0], v[1], v[2], v[3]);
+        st_u32x2(T.xb + (size_t)orow * T.ldxb + ocol, pack_bf16x4(v[0], v[1], v[2], v[3]));
     }
   }
   // Block sum of squares, fixed order.
@@ -214,7 +231,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < EW_THREADS / 64; ++w) s += wsum[w];
-    T.partial[gt] = s;
+    st_f32(T.partial + gt, s);
   }
 }
 
@@ -227,7 +244,7 @@ __global__ __launch_bounds__(256) void norm_kernel(const NormTask* __restrict__ 
   const NormTask& T = tasks[blockIdx.x];
   double acc = 0.0;
   for (int i = threadIdx.x; i < T.tile_count; i += 256)
-    acc += (double)T.partial[T.tile_begin + i];
+    acc += (double)ld_f32(T.partial + T.tile_begin + i);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if ((threadIdx.x & 63) == 0) wpart[threadIdx.x >> 6] = acc;
@@ -236,9 +253,9 @@ __global__ __launch_bounds__(256) void norm_kernel(const NormTask* __restrict__ 
     const double tot = (wpart[0] + wpart[1]) + (wpart[2] + wpart[3]);
     const double s = sqrt(tot);
     const double inv = 1.0 / (s + (double)eps);
-    T.scale[0] = (float)inv;
-    T.scale[1] = (float)(inv * inv);
-    T.scale[2] = (float)s;
+    st_f32(T.scale + 0, (float)inv);
+    st_f32(T.scale + 1, (float)(inv * inv));
+    st_f32(T.scale + 2, (float)s);
   }
 }
 
@@ -330,17 +347,16 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
           float* A = G.fbuf;
           const int ldf = G.ld_f;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) A[(size_t)(gi + rr) * ldf + gj] = v[rr];
-          if (mirror) *reinterpret_cast<f32x4*>(A + (size_t)gj * ldf + gi) = v;
+          for (int rr = 0; rr < 4; ++rr) st_f32(A + (size_t)(gi + rr) * ldf + gj, v[rr]);
+          if (mirror) st_f32x4(A + (size_t)gj * ldf + gi, v);
           if constexpr (!F32) {
             uint16_t* o0 = static_cast<uint16_t*>(G.out0);
             const int ld0 = G.ld0;
             if (!G.split) {
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) o0[(size_t)(gi + rr) * ld0 + gj] = to_bf16(v[rr]);
+              for (int rr = 0; rr < 4; ++rr) st_u16(o0 + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
               if (mirror)
-                *reinterpret_cast<uint2*>(o0 + (size_t)gj * ld0 + gi) =
-                    pack_bf16x4(v[0], v[1], v[2], v[3]);
+                st_u32x2(o0 + (size_t)gj * ld0 + gi, pack_bf16x4(v[0], v[1], v[2], v[3]));
             } else {
               // L3 = [hi | hi | lo], R3 = [hi | lo | hi] along K (3P), so
               // L3 R3^T = hi hi^T + hi lo^T + lo hi^T.
@@ -357,20 +373,20 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
                 const size_t rL = (size_t)(gi + rr) * ld0 + gj;
                 const size_t rR = (size_t)(gi + rr) * ld1 + gj;
                 const uint16_t h = to_bf16(hi[rr]), l = to_bf16(lo[rr]);
-                o0[rL] = h; o0[rL + P] = h; o0[rL + 2 * P] = l;
-                o1[rR] = h; o1[rR + P] = l; o1[rR + 2 * P] = h;
+                st_u16(o0 + rL, h); st_u16(o0 + rL + P, h); st_u16(o0 + rL + 2 * P, l);
+                st_u16(o1 + rR, h); st_u16(o1 + rR + P, l); st_u16(o1 + rR + 2 * P, h);
               }
               if (mirror) {
-                const uint2 h4 = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
-                const uint2 l4 = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+                const u32x2 h4 = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+                const u32x2 l4 = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
                 const size_t mL = (size_t)gj * ld0 + gi;
                 const size_t mR = (size_t)gj * ld1 + gi;
-                *reinterpret_cast<uint2*>(o0 + mL) = h4;
-                *reinterpret_cast<uint2*>(o0 + mL + P) = h4;
-                *reinterpret_cast<uint2*>(o0 + mL + 2 * P) = l4;
-                *reinterpret_cast<uint2*>(o1 + mR) = h4;
-                *reinterpret_cast<uint2*>(o1 + mR + P) = l4;
-                *reinterpret_cast<uint2*>(o1 + mR + 2 * P) = h4;
+                st_u32x2(o0 + mL, h4);
+                st_u32x2(o0 + mL + P, h4);
+                st_u32x2(o0 + mL + 2 * P, l4);
+                st_u32x2(o1 + mR, h4);
+                st_u32x2(o1 + mR + P, l4);
+                st_u32x2(o1 + mR + 2 * P, h4);
               }
             }
           }
@@ -378,22 +394,21 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
           const float* A = G.fbuf;
           const int ldf = G.ld_f;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(cb, A[(size_t)(gi + rr) * ldf + gj], cc * v[rr]);
+          for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(cb, ld_f32(A + (size_t)(gi + rr) * ldf + gj), cc * v[rr]);
           if constexpr (F32) {
             float* o0 = static_cast<float*>(G.out0);
             const int ld0 = G.ld0;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) o0[(size_t)(gi + rr) * ld0 + gj] = v[rr];
-            if (mirror) *reinterpret_cast<f32x4*>(o0 + (size_t)gj * ld0 + gi) = v;
+            for (int rr = 0; rr < 4; ++rr) st_f32(o0 + (size_t)(gi + rr) * ld0 + gj, v[rr]);
+            if (mirror) st_f32x4(o0 + (size_t)gj * ld0 + gi, v);
           } else {
             uint16_t* o0 = static_cast<uint16_t*>(G.out0);
             const int ld0 = G.ld0;
             if (!G.split) {
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) o0[(size_t)(gi + rr) * ld0 + gj] = to_bf16(v[rr]);
+              for (int rr = 0; rr < 4; ++rr) st_u16(o0 + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
               if (mirror)
-                *reinterpret_cast<uint2*>(o0 + (size_t)gj * ld0 + gi) =
-                    pack_bf16x4(v[0], v[1], v[2], v[3]);
+                st_u32x2(o0 + (size_t)gj * ld0 + gi, pack_bf16x4(v[0], v[1], v[2], v[3]));
             } else {
               // [hi | lo] along K (2P); the B X product pairs both halves
               // with the same X^T.
@@ -406,13 +421,13 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) {
                 const size_t o = (size_t)(gi + rr) * ld0 + gj;
-                o0[o] = to_bf16(hi[rr]);
-                o0[o + P] = to_bf16(lo[rr]);
+                st_u16(o0 + o, to_bf16(hi[rr]));
+                st_u16(o0 + o + P, to_bf16(lo[rr]));
               }
               if (mirror) {
                 const size_t o = (size_t)gj * ld0 + gi;
-                *reinterpret_cast<uint2*>(o0 + o) = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
-                *reinterpret_cast<uint2*>(o0 + o + P) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+                st_u32x2(o0 + o, pack_bf16x4(hi[0], hi[1], hi[2], hi[3]));
+                st_u32x2(o0 + o + P, pack_bf16x4(lo[0], lo[1], lo[2], lo[3]));
               }
             }
           }
@@ -422,23 +437,23 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const size_t o = (size_t)(gi + rr) * ldf + gj;
-            v[rr] = s * fmaf(ca, X[o], v[rr]);
-            X[o] = v[rr];
+            v[rr] = s * fmaf(ca, ld_f32(X + o), v[rr]);
+            st_f32(X + o, v[rr]);
           }
           void* xt_next = (iter & 1) ? G.out1 : G.out2;
           const int ld1 = G.ld1;
           if constexpr (F32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(xt_next) + (size_t)gj * ld1 + gi) = v;
+            st_f32x4(static_cast<float*>(xt_next) + (size_t)gj * ld1 + gi, v);
           } else {
             uint16_t* xb = static_cast<uint16_t*>(G.out0);
             const int ld0 = G.ld0;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) xb[(size_t)(gi + rr) * ld0 + gj] = to_bf16(v[rr]);
+            for (int rr = 0; rr < 4; ++rr) st_u16(xb + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
             // X^T goes through LDS (transposed, 8-byte groups XOR-swizzled)
             // so that it leaves the tile as full rows.
             const int il = gi - tm * T, jl = gj - tn * T;
             const int x = 4 * (jl & (T / 4 - 1));
-            *reinterpret_cast<uint2*>(stage + jl * T + (il ^ x)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<u32x2*>(stage + jl * T + (il ^ x)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
             (void)xt_next;
             (void)ld1;
           }
@@ -456,9 +471,9 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
     for (int jl = tid / CPR; jl < T; jl += RPP) {
       const int x = 4 * (jl & (T / 4 - 1));
       const int pos = (8 * c) ^ x;
-      uint4 w = *reinterpret_cast<const uint4*>(stage + jl * T + (pos & ~7));
+      u32x4 w = *reinterpret_cast<const u32x4*>(stage + jl * T + (pos & ~7));
       if (pos & 4) { const uint32_t a = w.x, b = w.y; w.x = w.z; w.y = w.w; w.z = a; w.w = b; }
-      *reinterpret_cast<uint4*>(xt + (size_t)(tn * T + jl) * ld1 + tm * T + 8 * c) = w;
+      st_u32x4(xt + (size_t)(tn * T + jl) * ld1 + tm * T + 8 * c, w);
     }
   }
 }
@@ -508,8 +523,8 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
       const int c = tid + 256 * i;
       const int row = c >> 3;
       const int col = (c & 7) * VEC;
-      regL[i] = *reinterpret_cast<const uint4*>(Lp + (size_t)row * ldl + k0 + col);
-      regR[i] = *reinterpret_cast<const uint4*>(Rp + (size_t)row * ldr + kr + col);
+      regL[i] = ld_u128(Lp + (size_t)row * ldl + k0 + col);
+      regR[i] = ld_u128(Rp + (size_t)row * ldr + kr + col);
     }
   };
   auto sstore = [&](int st) {
@@ -748,7 +763,7 @@ __global__ __launch_bounds__(EW_THREADS) void update_kernel(
     // X rows c0.., columns r0..: always inside the padded P x Q buffer.
     for (int k = 0; k < EW_TILE / 16; ++k) {
       const int xr = ry + 16 * k;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(T.xm + (size_t)(c0 + xr) * T.ldx + r0 + cx);
+      const f32x4 v = ld_f32x4(T.xm + (size_t)(c0 + xr) * T.ldx + r0 + cx);
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[xr][cx + e] = v[e];
     }
@@ -764,7 +779,7 @@ __global__ __launch_bounds__(EW_THREADS) void update_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = tile[cx + e][r];
     } else {
-      o = *reinterpret_cast<const f32x4*>(T.xm + (size_t)gr * T.ldx + gc);
+      o = ld_f32x4(T.xm + (size_t)gr * T.ldx + gc);
     }
     const size_t idx = (size_t)gr * T.n + gc;
     if (T.vec && gc + 3 < T.n) {
