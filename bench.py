@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's host timing (0 disables it)")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="run one plain device copy of this many MiB first (a "
+                         "known-size reference for rocprofv3 byte counters)")
     return ap.parse_args()
 
 
@@ -162,6 +165,13 @@ def main():
     warmup = args.warmup if args.warmup is not None else 10 if args.config in (1, 2, 4) else 3
     device = torch.device("cuda", 0)
     torch.cuda.set_device(device)
+    if args.calib_copy:
+        n = args.calib_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=device)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     n_sets = 1 if cfg.ns_only else max(1, min(cfg.steps, steps + warmup))
     log(f"config {cfg.cfg_id} ({cfg.name}): {len(cfg.shapes)} matrices, {n_sets} gradient sets")
     params, bufs, sets = make_inputs(cfg, n_sets, device)
