@@ -12,8 +12,8 @@ documentation pages; readings of unstated points are marked READING):
    momentum times the buffer).
    READING: the buffer recursion is ``buf <- mu*buf + g`` with no dampening,
    and the Nesterov lookahead uses the buffer *after* this update.
-2. orientation (DMuon "API Reference", ``gram_newton_schulz_factors``:
-   NS acts on the normalized and possibly transposed view of G).
+2. orientation (DMuon "API Reference", ``gram_newton_schulz_factors``: NS
+   may operate on the transpose of the normalized G).
    READING: transpose iff rows > cols; square matrices are not transposed.
 3. normalization (same section: the normalizer is the Frobenius norm of G
    plus eps; ``direct_newton_schulz`` default eps = 1e-7).
@@ -92,8 +92,8 @@ def momentum_update(buf, grad, momentum: float, nesterov: bool):
 
 def orient(M):
     """Return ``(X, transposed)``: X is M, or M^T when M has more rows than
-    columns (DMuon "API Reference", ``gram_newton_schulz_factors``: the
-    "possibly transposed view"; READING: transpose iff rows > cols)."""
+    columns (DMuon "API Reference", ``gram_newton_schulz_factors``: NS may
+    act on the transposed matrix; READING: transpose iff rows > cols)."""
     M = np.asarray(M, dtype=np.float64)
     if M.ndim != 2:
         raise ValueError("Newton-Schulz needs a 2D matrix")
