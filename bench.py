@@ -87,7 +87,7 @@ def make_inputs(cfg, n_sets, device):
 
 def kernel_sha():
     h = hashlib.sha256()
-    for f in ("dmuon_kernels.hip", "dmuon_internal.h"):
+    for f in ("dmuon_kernels.hip", "dmuon_internal.h", "dmuon_host.cpp"):
         with open(os.path.join(ROOT, "newton_schulz_06_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

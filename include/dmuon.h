@@ -54,21 +54,24 @@ typedef enum { DMUON_F32 = 0, DMUON_BF16 = 1 } dmuon_dtype_t;
 
 /*
  * Newton-Schulz arithmetic.
- *   DMUON_NS_F32        fp32 operands on fp32 MFMA, fp32 accumulate.
- *   DMUON_NS_BF16       fp32 master copy of X; bf16 copies of X, A = X X^T
- *                       and B = bA + cA^2 as MFMA operands; fp32 accumulate
- *                       and fp32 epilogues.
- *   DMUON_NS_BF16_SPLIT as DMUON_NS_BF16, with A and B carried as a bf16
- *                       hi + lo pair (A^2 from three products, B X from
- *                       two) for small or skinny matrices.
- *   DMUON_NS_AUTO       per matrix: BF16_SPLIT when min(m, n) <= 1024,
- *                       else BF16.
+ *   DMUON_NS_F32          fp32 operands on fp32 MFMA, fp32 accumulate.
+ *   DMUON_NS_BF16         fp32 master copy of X; bf16 copies of X, A = X X^T
+ *                         and B = bA + cA^2 as MFMA operands; fp32
+ *                         accumulate and fp32 epilogues.
+ *   DMUON_NS_BF16_SPLIT   as DMUON_NS_BF16, with A and B carried as bf16
+ *                         hi + lo pairs (A^2 from three products, B X from
+ *                         two).
+ *   DMUON_NS_BF16_SPLIT_A as DMUON_NS_BF16 with only A split (A^2 from three
+ *                         products, B X from one).
+ *   DMUON_NS_AUTO         per matrix by p = min(m, n): BF16_SPLIT for
+ *                         p <= 128, BF16_SPLIT_A for p <= 1024, else BF16.
  */
 typedef enum {
   DMUON_NS_F32 = 0,
   DMUON_NS_BF16 = 1,
   DMUON_NS_BF16_SPLIT = 2,
-  DMUON_NS_AUTO = 3
+  DMUON_NS_AUTO = 3,
+  DMUON_NS_BF16_SPLIT_A = 4
 } dmuon_prec_t;
 
 /* One matrix: m rows, n columns, row-major, device pointer. */

@@ -28,24 +28,32 @@ dmuon_status_t fail(dmuon_status_t st, const std::string& msg) {
 constexpr int kMaxSteps = 16;
 constexpr int64_t kMaxSide = int64_t(1) << 20;
 constexpr size_t kWsAlign = 256;
-// GEMM tile classes (square T x T output tiles).  bf16 operands: 64 for
-// min side <= 128, 128 up to 512, 256 above.  fp32 operands: 64 up to 512,
-// 128 above.
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+size_t esize(int dtype) { return dtype == DMUON_F32 ? 4 : 2; }
+
+// GEMM tile classes (square T x T output tiles).  bf16 operands: the
+// largest of 256 (min side >= 1024) / 128 (>= 768) whose padding of the
+// min side stays within 1/8, else 64 -- small matrices are latency-bound and
+// want many small tiles.  fp32 operands: 64 up to 512, 128 above.
 constexpr int kTiles[3] = {64, 128, 256};
 
 int tile_class(int64_t p, bool f32_ops) {
   if (f32_ops) return p <= 512 ? 64 : 128;
-  return p <= 128 ? 64 : (p <= 512 ? 128 : 256);
+  auto fits = [p](int64_t t) { return round_up(p, t) * 8 <= p * 9; };
+  if (p >= 1024 && fits(256)) return 256;
+  if (p >= 768 && fits(128)) return 128;
+  return 64;
 }
-// DMUON_NS_AUTO uses hi/lo split operands up to this min side: plain bf16
-// operands put iid-noise-like spectra of narrow matrices (e.g. 2048 x 512)
-// just past a 2e-2 relative error, while wider ones stay near 1e-2.
-constexpr int kAutoSplitMaxP = 1024;
+// DMUON_NS_AUTO: hi/lo A and B up to this min side, hi/lo A only up to the
+// next.  With plain bf16 operands iid-noise-like spectra of narrow matrices
+// (e.g. 2048 x 512) land just past a 2e-2 relative error; splitting A (the
+// A^2 product) brings them to ~1.3e-2, and the smallest sides (<= 128)
+// need B split as well.
+constexpr int kAutoSplitMaxP = 128;
+constexpr int kAutoSplitAMaxP = 1024;
 constexpr float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
 
-size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
-size_t esize(int dtype) { return dtype == DMUON_F32 ? 4 : 2; }
 
 // Row stride (elements) for a workspace matrix with `n` columns of `esz`
 // bytes: rounded up to an odd multiple of 256 bytes, so that consecutive
@@ -60,7 +68,7 @@ int64_t ld_for(int64_t n, int64_t esz) {
 // Shape-derived geometry of one matrix in the workspace.
 struct Geom {
   int64_t m, n, p, q, P, Q;
-  int tile, transposed, split;
+  int tile, transposed, split_a, split_b;
   int64_t ld_xm, ld_xb, ld_xt, ld_a32, ld_aop, ld_bop;  // row strides (elements)
   size_t xm, xb, xt0, xt1, a32, aop, r3, bop;          // byte offsets in ws
 };
@@ -85,15 +93,18 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
     G.transposed = G.m > G.n;
     G.p = std::min(G.m, G.n);
     G.q = std::max(G.m, G.n);
-    G.tile = tile_class(G.p, L.f32_ops);
+    G.tile = tile_class(G.p, L.f32_ops != 0);
     G.P = round_up(G.p, G.tile);
     G.Q = round_up(G.q, G.tile);
     if (G.P * ld_for(G.Q, 4) > INT32_MAX || G.Q * ld_for(G.P, 4) > INT32_MAX ||
         G.P * ld_for(3 * G.P, 2) > INT32_MAX)
       return fail(DMUON_E_UNSUPPORTED, "matrix " + std::to_string(i) +
                                            ": padded size exceeds 2^31 elements");
-    G.split = (prec == DMUON_NS_BF16_SPLIT) ||
-              (prec == DMUON_NS_AUTO && G.p <= kAutoSplitMaxP);
+    const bool auto_ab = prec == DMUON_NS_AUTO && G.p <= kAutoSplitMaxP;
+    const bool auto_a = prec == DMUON_NS_AUTO && G.p <= kAutoSplitAMaxP;
+    G.split_b = !L.f32_ops && (prec == DMUON_NS_BF16_SPLIT || auto_ab);
+    G.split_a = !L.f32_ops && (prec == DMUON_NS_BF16_SPLIT || prec == DMUON_NS_BF16_SPLIT_A ||
+                               auto_a);
     tiles += (G.P / EW_TILE) * (G.Q / EW_TILE);
   }
   if (tiles > INT32_MAX) return fail(DMUON_E_UNSUPPORTED, "batch too large (tile count)");
@@ -127,17 +138,11 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
       G.r3 = 0;
       G.ld_bop = ld_for(G.P, 4);
       G.bop = take(4 * P * G.ld_bop);
-    } else if (G.split) {
-      G.ld_aop = ld_for(3 * G.P, 2);
-      G.aop = take(2 * P * G.ld_aop);
-      G.r3 = take(2 * P * G.ld_aop);
-      G.ld_bop = ld_for(2 * G.P, 2);
-      G.bop = take(2 * P * G.ld_bop);
     } else {
-      G.ld_aop = ld_for(G.P, 2);
+      G.ld_aop = ld_for(G.split_a ? 3 * G.P : G.P, 2);
       G.aop = take(2 * P * G.ld_aop);
-      G.r3 = 0;
-      G.ld_bop = ld_for(G.P, 2);
+      G.r3 = G.split_a ? take(2 * P * G.ld_aop) : 0;
+      G.ld_bop = ld_for(G.split_b ? 2 * G.P : G.P, 2);
       G.bop = take(2 * P * G.ld_bop);
     }
   }
@@ -175,7 +180,7 @@ dmuon_status_t check_cfg(const dmuon_ns_cfg_t* cfg) {
     return fail(DMUON_E_INVALID, "cfg: ns_steps must be in [1, 16]");
   if (!std::isfinite(cfg->eps) || cfg->eps < 0.f)
     return fail(DMUON_E_INVALID, "cfg: eps must be finite and >= 0");
-  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_AUTO)
+  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_BF16_SPLIT_A)
     return fail(DMUON_E_INVALID, "cfg: unknown precision mode");
   if (cfg->coeffs)
     for (int i = 0; i < 3 * cfg->ns_steps; ++i)
@@ -351,7 +356,6 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
         const int nt = P / tile;
         const double p = (double)G.p, q = (double)G.q;
         t.P = P;
-        t.split = G.split && !L.f32_ops;
         t.scale = scale + 4 * i;
         if (kind == KIND_SYRK) {
           t.L = ws + (L.f32_ops ? G.xm : G.xb);
@@ -363,15 +367,17 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.tile_count = nt * (nt + 1) / 2;
           t.fbuf = reinterpret_cast<float*>(ws + G.a32);
           t.ld_f = (int32_t)G.ld_a32;
+          t.split = G.split_a;  // writes A as [hi|hi|lo] / [hi|lo|hi]
           t.out0 = L.f32_ops ? nullptr : ws + G.aop;
           t.out1 = t.split ? ws + G.r3 : nullptr;
           t.ld0 = t.ld1 = (int32_t)G.ld_aop;
           flops += p * (p + 1) * q;
         } else if (kind == KIND_POLY) {
+          t.split = G.split_b;  // writes B as [hi|lo]
           t.L = ws + G.aop;
-          t.R0 = t.R1 = t.split ? ws + G.r3 : ws + G.aop;
+          t.R0 = t.R1 = G.split_a ? ws + G.r3 : ws + G.aop;
           t.ldl = t.ldr = (int32_t)G.ld_aop;
-          t.K = t.kper = t.split ? 3 * P : P;
+          t.K = t.kper = G.split_a ? 3 * P : P;
           t.tiles_m = t.tiles_n = nt;
           t.tri = 1;
           t.tile_count = nt * (nt + 1) / 2;
@@ -386,7 +392,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.R1 = ws + G.xt1;
           t.ldl = (int32_t)G.ld_bop;
           t.ldr = (int32_t)G.ld_xt;
-          t.K = t.split ? 2 * P : P;
+          t.K = G.split_b ? 2 * P : P;
           t.kper = P;
           t.tiles_m = nt;
           t.tiles_n = Q / tile;
@@ -465,7 +471,7 @@ dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_b
     key.push_back((int64_t)reinterpret_cast<uintptr_t>(src->mats[i].ptr));
     key.push_back((int64_t)reinterpret_cast<uintptr_t>(dst->mats[i].ptr));
     key.push_back(bufs ? (int64_t)reinterpret_cast<uintptr_t>(bufs->mats[i].ptr) : 0);
-    key.push_back(L.g[i].split);
+    key.push_back(L.g[i].split_a + 2 * L.g[i].split_b);
   }
   for (size_t k = 0; k < g_plans.size(); ++k) {
     if (g_plans[k]->key == key) {
@@ -590,7 +596,7 @@ dmuon_status_t dmuon_ns_workspace_size(const dmuon_batch_t* g, const dmuon_ns_cf
   dmuon_status_t st = check_batch(g, "g", false);
   if (st) return st;
   if (!cfg) return fail(DMUON_E_INVALID, "cfg: null");
-  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_AUTO)
+  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_BF16_SPLIT_A)
     return fail(DMUON_E_INVALID, "cfg: unknown precision mode");
   Layout L;
   st = make_layout(g, cfg->prec, &L);

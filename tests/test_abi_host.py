@@ -58,6 +58,20 @@ def _ld(n, esz):
     return u * 256 // esz
 
 
+def _tile(p, prec):
+    if prec == "f32":
+        return 64 if p <= 512 else 128
+
+    def fits(t):
+        return _pad(p, t) * 8 <= p * 9
+
+    if p >= 1024 and fits(256):
+        return 256
+    if p >= 768 and fits(128):
+        return 128
+    return 64
+
+
 def _expected_ws(shapes, prec):
     """Workspace rule: partials + scales, then per matrix X master, bf16 X,
     two X^T buffers, fp32 A and the operand copies of A and B, each rounded
@@ -67,29 +81,28 @@ def _expected_ws(shapes, prec):
     per = []
     for m, n in shapes:
         p, q = min(m, n), max(m, n)
-        if prec == "f32":
-            t = 64 if p <= 512 else 128
-        else:
-            t = 64 if p <= 128 else (128 if p <= 512 else 256)
+        t = _tile(p, prec)
         P, Q = _pad(p, t), _pad(q, t)
         tiles += (P // 64) * (Q // 64)
-        split = prec == "bf16_split" or (prec == "auto" and p <= 1024)
+        split_b = prec == "bf16_split" or (prec == "auto" and p <= 128)
+        split_a = prec in ("bf16_split", "bf16_split_a") or (prec == "auto" and p <= 1024)
         if prec == "f32":
             per.append(a(4 * P * _ld(Q, 4)) + 2 * a(4 * Q * _ld(P, 4)) + a(4 * P * _ld(P, 4))
                        + a(4 * P * _ld(P, 4)))
         else:
             base = a(4 * P * _ld(Q, 4)) + a(2 * P * _ld(Q, 2)) + 2 * a(2 * Q * _ld(P, 2)) \
                 + a(4 * P * _ld(P, 4))
-            if split:
-                per.append(base + 2 * a(2 * P * _ld(3 * P, 2)) + a(2 * P * _ld(2 * P, 2)))
-            else:
-                per.append(base + a(2 * P * _ld(P, 2)) + a(2 * P * _ld(P, 2)))
+            aop = a(2 * P * _ld(3 * P if split_a else P, 2))
+            base += aop * (2 if split_a else 1)
+            base += a(2 * P * _ld(2 * P if split_b else P, 2))
+            per.append(base)
     return a(4 * tiles) + a(16 * len(shapes)) + sum(per)
 
 
-@pytest.mark.parametrize("prec", ["f32", "bf16", "bf16_split", "auto"])
+@pytest.mark.parametrize("prec", ["f32", "bf16", "bf16_split", "auto", "bf16_split_a"])
 def test_workspace_size(prec):
-    shapes = [(1024, 256), (256, 1024), (100, 37), (4096, 14336), (32, 480)]
+    shapes = [(1024, 256), (256, 1024), (100, 37), (4096, 14336), (32, 480), (544, 800),
+              (900, 960), (8192, 28672)]
     assert dm.workspace_size(shapes, prec) == _expected_ws(shapes, prec)
     assert dm.workspace_size([], prec) == 0
 

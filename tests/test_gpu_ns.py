@@ -83,6 +83,20 @@ def test_ns_bf16_matches_oracle(prec, dtype):
         assert e <= 2e-2 and d <= 2e-2, (s, prec, dtype, e, d)
 
 
+@pytest.mark.parametrize("prec", ["bf16_split_a", "auto"])
+def test_ns_split_a_mid_gaussian(prec):
+    """hi/lo A with plain bf16 B (the automatic mode for 128 < min side <=
+    1024) on iid Gaussians, the hardest spectra for bf16 operands."""
+    shapes = [(257, 700), (700, 257), (520, 1100), (2048, 512), (512, 512), (160, 640)]
+    gs_np = [_gen(s, 70 + i) for i, s in enumerate(shapes)]
+    gin, outs = _run_ns(gs_np, "bf16", prec)
+    for s, g, o in zip(shapes, gin, outs):
+        want = oracle.direct_newton_schulz(g)
+        e = rel_frobenius(o, want)
+        d = sigma_dev(o, want)
+        assert e <= 2e-2 and d <= 2e-2, (s, prec, e, d)
+
+
 @pytest.mark.parametrize("prec", ["bf16", "auto"])
 def test_ns_plain_bf16_large_gaussian(prec):
     """Plain bf16 operands (what the automatic mode uses above 1024) on an
