@@ -173,8 +173,9 @@ const char* dmuon_backend_info(void);
  * work of those launches: symmetric-aware flops of the NS products
  * (p(p+1)q for A = X X^T, p^2(p+1) for A A, 2p^2q for B X); for the
  * element-wise kernels, the bytes the step must move at minimum.
- * Kinds: 0 momentum, 1 input, 2 norm, 3 syrk, 4 poly, 5 update_x,
- *        6 update_p, 7 output.
+ * Kinds: 0 momentum, 1 input, 2 norm, 3 syrk, 4 poly, 5 update_x.  The
+ * last update_x launch of a call also applies the parameter update (or
+ * writes the NS output), so there is no separate update kind.
  */
 typedef struct {
   char name[24];

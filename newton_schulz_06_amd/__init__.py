@@ -227,7 +227,7 @@ def muon_step(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_decay=0.0, 
                                  _stream_handle(stream)))
 
 
-KINDS = ("momentum", "input", "norm", "syrk", "poly", "update_x", "update_p", "output")
+KINDS = ("momentum", "input", "norm", "syrk", "poly", "update_x")
 
 
 class profile:

@@ -242,9 +242,9 @@ struct Plan {
   int device = -1;
   void* dtab = nullptr;
   int f32_ops = 0;
-  size_t in_off = 0, norm_off = 0, out_off = 0;
-  int nmat = 0, in_tiles = 0, out_tiles = 0;
-  double in_bytes = 0, out_bytes = 0, norm_bytes = 0;
+  size_t in_off = 0, norm_off = 0;
+  int nmat = 0, in_tiles = 0;
+  double in_bytes = 0, norm_bytes = 0;
   std::vector<GemmLaunch> gemms;  // SYRK launches, then POLY, then UPDX
   ~Plan() {
     if (dtab) {
@@ -282,9 +282,9 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   float* partial = reinterpret_cast<float*>(ws + L.partial_off);
   float* scale = reinterpret_cast<float*>(ws + L.scale_off);
 
-  std::vector<EwTask> tin(n), tout(n);
+  std::vector<EwTask> tin(n);
   std::vector<NormTask> tnorm(n);
-  int in_begin = 0, out_begin = 0;
+  int in_begin = 0;
   for (int i = 0; i < n; ++i) {
     const Geom& G = L.g[i];
     EwTask t{};
@@ -292,14 +292,12 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
     t.n = (int32_t)G.n;
     t.transposed = G.transposed;
     t.in_dtype = src->dtype;
-    t.out_dtype = dst->dtype;
     t.ldx = (int32_t)G.ld_xm;
     t.ldxb = (int32_t)G.ld_xb;
     t.ldt = (int32_t)G.ld_xt;
     t.f32_ops = L.f32_ops;
     t.src = src->mats[i].ptr;
     t.buf = bufs ? static_cast<float*>(bufs->mats[i].ptr) : nullptr;
-    t.dst = dst->mats[i].ptr;
     t.xm = reinterpret_cast<float*>(ws + G.xm);
     t.xb = L.f32_ops ? nullptr : reinterpret_cast<uint16_t*>(ws + G.xb);
     t.xt = ws + G.xt0;
@@ -316,28 +314,11 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
     in_begin += a.tile_count;
     tin[i] = a;
     tnorm[i] = NormTask{a.tile_begin, a.tile_count, partial, scale + 4 * i};
-    // output pass: the caller's extents
-    EwTask o = t;
-    o.rows = (int32_t)G.m;
-    o.cols = (int32_t)G.n;
-    o.tiles_c = (int32_t)((G.n + EW_TILE - 1) / EW_TILE);
-    o.tile_begin = out_begin;
-    o.tile_count = (int32_t)((G.m + EW_TILE - 1) / EW_TILE) * o.tiles_c;
-    o.vec = vec_ok(t.dst, dst->dtype, G.n);
-    out_begin += o.tile_count;
-    tout[i] = o;
     const double mn = (double)G.m * (double)G.n;
-    if (ns_only) {
-      plan->in_bytes += mn * esize(src->dtype);
-      plan->out_bytes += mn * esize(dst->dtype);
-    } else {
-      plan->in_bytes += mn * (esize(src->dtype) + 8.0);
-      plan->out_bytes += mn * 2.0 * esize(dst->dtype);
-    }
+    plan->in_bytes += ns_only ? mn * esize(src->dtype) : mn * (esize(src->dtype) + 8.0);
     plan->norm_bytes += 4.0 * a.tile_count;
   }
   plan->in_tiles = in_begin;
-  plan->out_tiles = out_begin;
 
   // GEMM tasks, grouped by (kind, tile class).
   std::vector<GemmTask> gtasks;
@@ -405,6 +386,12 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.out1 = ws + G.xt0;
           t.out2 = ws + G.xt1;
           t.ld1 = (int32_t)G.ld_xt;
+          t.dst = dst->mats[i].ptr;
+          t.pv = (int32_t)G.p;
+          t.qv = (int32_t)G.q;
+          t.dst_trans = G.transposed;
+          t.dst_dtype = dst->dtype;
+          t.dst_vec = G.transposed && vec_ok(t.dst, dst->dtype, G.p);
           flops += 2.0 * p * p * q;
         }
         t.tile_begin = acc;
@@ -427,14 +414,12 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
     return o;
   };
   plan->in_off = place(sizeof(EwTask) * n);
-  plan->out_off = place(sizeof(EwTask) * n);
   plan->norm_off = place(sizeof(NormTask) * n);
   const size_t g_off = place(sizeof(GemmTask) * gtasks.size());
   for (size_t k = 0; k < plan->gemms.size(); ++k)
     plan->gemms[k].off = g_off + sizeof(GemmTask) * ranges[k].first;
   std::vector<char> host(off);
   std::memcpy(host.data() + plan->in_off, tin.data(), sizeof(EwTask) * n);
-  std::memcpy(host.data() + plan->out_off, tout.data(), sizeof(EwTask) * n);
   std::memcpy(host.data() + plan->norm_off, tnorm.data(), sizeof(NormTask) * n);
   if (!gtasks.empty())
     std::memcpy(host.data() + g_off, gtasks.data(), sizeof(GemmTask) * gtasks.size());
@@ -517,8 +502,7 @@ struct Prof {
 };
 thread_local Prof g_prof;
 
-const char* kKindNames[KIND_COUNT] = {"momentum", "input", "norm", "syrk",
-                                      "poly", "update_x", "update_p", "output"};
+const char* kKindNames[KIND_COUNT] = {"momentum", "input", "norm", "syrk", "poly", "update_x"};
 
 template <class F>
 hipError_t timed(int kind, double flops, double bytes, hipStream_t s, F&& launch) {
@@ -539,7 +523,6 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
     return fail(DMUON_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
   };
   const EwTask* tin = reinterpret_cast<const EwTask*>(tab + plan.in_off);
-  const EwTask* tout = reinterpret_cast<const EwTask*>(tab + plan.out_off);
   const NormTask* tnorm = reinterpret_cast<const NormTask*>(tab + plan.norm_off);
   dmuon_status_t st = check(
       timed(ns_only ? KIND_INPUT : KIND_MOMENTUM, 0, plan.in_bytes, s,
@@ -553,23 +536,29 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
   if (st) return st;
   for (int it = 0; it < cfg->ns_steps; ++it) {
     const float* c = cfg->coeffs ? cfg->coeffs + 3 * it : kQuintic;
+    IterArgs args{};
+    args.iter = it;
+    args.a = c[0];
+    args.b = c[1];
+    args.c = c[2];
+    // The last X update writes the caller's param (or output) directly.
+    if (it == cfg->ns_steps - 1) {
+      args.fin = ns_only ? FIN_OUTPUT : FIN_UPDATE;
+      args.lr = lr;
+      args.decay = decay;
+    }
     for (const GemmLaunch& gl : plan.gemms) {
       const GemmTask* tasks = reinterpret_cast<const GemmTask*>(tab + gl.off);
       st = check(timed(gl.kind, gl.flops, 0, s,
                        [&] {
                          return launch_gemm(gl.kind, gl.tile, plan.f32_ops, tasks, gl.ntasks,
-                                            gl.total, it, c[0], c[1], c[2], s);
+                                            gl.total, args, s);
                        }),
                  "NS product launch");
       if (st) return st;
     }
   }
-  return check(timed(ns_only ? KIND_OUTPUT : KIND_UPDATE, 0, plan.out_bytes, s,
-                     [&] {
-                       return launch_update(tout, plan.nmat, plan.out_tiles, lr, decay, ns_only,
-                                            s);
-                     }),
-               "update/output launch");
+  return DMUON_OK;
 }
 
 dmuon_status_t check_ws(const Layout& L, void* ws, size_t ws_bytes) {
@@ -691,7 +680,8 @@ const char* dmuon_last_error(void) { return g_last_error.c_str(); }
 
 const char* dmuon_backend_info(void) {
   return "direct NS (SYRK + symmetric poly + update-X) . gfx950 MFMA "
-         "bf16 32x32x16 / fp32 32x32x2 . tiles 64,128 . fp32 master X";
+         "bf16 32x32x16 (tiles 64/128/256) / fp32 32x32x2 (tiles 64/128) . fp32 master X . "
+         "update fused into the last X product";
 }
 
 int32_t dmuon_profile_begin(uint32_t kind_mask) {

@@ -15,9 +15,9 @@ enum Kind : int {
   KIND_NORM,          // per-matrix norm finalize -> 1/(||u|| + eps)
   KIND_SYRK,          // A = X X^T (upper tiles, mirrored write)
   KIND_POLY,          // B = b A + c A A^T (upper tiles, mirrored write)
-  KIND_UPDX,          // X <- a X + B X
-  KIND_UPDATE,        // p <- p (1 - lr wd) - lr O
-  KIND_OUTPUT,        // out <- O in the caller's dtype
+  KIND_UPDX,          // X <- a X + B X; on the last iteration the result
+                      // goes straight to the caller: p <- p (1 - lr wd) - lr O
+                      // (step) or out <- O (NS only)
   KIND_COUNT
 };
 
@@ -36,16 +36,13 @@ struct EwTask {
   int32_t tile_count;      // tiles of this task
   int32_t transposed;      // m > n: the oriented X is the transpose
   int32_t in_dtype;        // dtype of `src` (grad / input G)
-  int32_t out_dtype;       // dtype of `dst` (param / output)
   int32_t ldx;             // row stride of xm (elements)
   int32_t ldxb;            // row stride of xb (elements)
   int32_t ldt;             // row stride of xt (elements)
   int32_t f32_ops;         // 1: xt holds fp32 (NS in fp32), 0: bf16
   int32_t vec;             // 1: caller buffers allow 16-byte (4-element) access
-  int32_t pad_;
   const void* src;         // grad (step) or G (NS only)
   float* buf;              // momentum buffer (step) or null
-  void* dst;               // param (update) or output (NS only)
   float* xm;               // fp32 master X, P x Q
   uint16_t* xb;            // bf16 X, P x Q (null when f32_ops)
   void* xt;                // X^T, Q x P (bf16 or fp32)
@@ -73,6 +70,30 @@ struct GemmTask {
   void* out2;              // UPDX: X^T (odd iter)
   int32_t ld0, ld1;
   const float* scale;      // per-matrix scalars (see EwTask::scale)
+  // UPDX, last iteration: the caller's param (step) or output (NS only).
+  // Oriented element (r, c), r < pv, c < qv, sits at dst[r*qv + c], or at
+  // dst[c*pv + r] when dst_trans (caller's matrix is the transpose).
+  void* dst;
+  int32_t pv, qv;          // valid oriented extents p x q
+  int32_t dst_trans;
+  int32_t dst_dtype;
+  int32_t dst_vec;         // dst_trans only: 4 consecutive r are one aligned access
+  int32_t pad_;
+};
+
+// What the UPDX epilogue does with the new X.
+enum Fin : int32_t {
+  FIN_NONE = 0,    // keep iterating: write X (fp32, bf16) and X^T
+  FIN_UPDATE = 1,  // p <- p * decay - lr * O
+  FIN_OUTPUT = 2,  // out <- O
+};
+
+// Per-launch scalars of one NS iteration.
+struct IterArgs {
+  int32_t iter;
+  int32_t fin;             // Fin; only read by UPDX
+  float a, b, c;           // this iteration's coefficients
+  float lr, decay;         // FIN_UPDATE only
 };
 
 struct NormTask {
@@ -87,11 +108,10 @@ hipError_t launch_momentum(const EwTask* tasks, int ntasks, int total_tiles,
                            hipStream_t s);
 hipError_t launch_norm(const NormTask* tasks, int ntasks, float eps,
                        hipStream_t s);
-// kind in {KIND_SYRK, KIND_POLY, KIND_UPDX}; tile in {64, 128}
+// kind in {KIND_SYRK, KIND_POLY, KIND_UPDX}; tile in {64, 128, 256}
+// (bf16 operands) or {64, 128} (fp32 operands)
 hipError_t launch_gemm(int kind, int tile, int f32_ops,
                        const GemmTask* tasks, int ntasks, int total_tiles,
-                       int iter, float a, float b, float c, hipStream_t s);
-hipError_t launch_update(const EwTask* tasks, int ntasks, int total_tiles,
-                         float lr, float decay, int ns_only, hipStream_t s);
+                       const IterArgs& args, hipStream_t s);
 
 }  // namespace dmuon

@@ -315,12 +315,45 @@ __device__ __forceinline__ void full_decode(int t, int tiles_m, int tiles_n, int
 // Kind-specific epilogue of one T x T output tile.  32x32 MFMA output
 // layout: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4 and column
 // l%32 of its block.
+// Last NS iteration: four oriented rows r..r+3 of column c of the new X go
+// to the caller, as the update p <- p*decay - lr*O or as the output O.
+__device__ __forceinline__ void final_write(const GemmTask& G, const IterArgs& A, int r, int c,
+                                            f32x4 v) {
+  if (c >= G.qv || r >= G.pv) return;
+  void* dst = G.dst;
+  const int dt = G.dst_dtype;
+  const bool upd = A.fin == FIN_UPDATE;
+  if (G.dst_trans && G.dst_vec) {  // caller row c holds r..r+3 contiguously
+    const size_t idx = (size_t)c * G.pv + r;
+    f32x4 o = v;
+    if (upd) {
+      const f32x4 p = load4(dst, dt, idx);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = fmaf(-A.lr, v[e], p[e] * A.decay);
+    }
+    store4(dst, dt, idx, o);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (r + e >= G.pv) break;
+    const size_t idx = G.dst_trans ? (size_t)c * G.pv + r + e : (size_t)(r + e) * G.qv + c;
+    float o = v[e];
+    if (upd) o = fmaf(-A.lr, v[e], load1(dst, dt, idx) * A.decay);
+    store1(dst, dt, idx, o);
+  }
+}
+
 template <int KIND, int T, bool F32, int NT>
 __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm, int tn,
-                                         int wr, int wc, int lane, int iter, float ca, float cb,
-                                         float cc, uint16_t* stage) {
-  constexpr bool kStageXT = (KIND == KIND_UPDX) && !F32;
-  if constexpr (kStageXT) __syncthreads();  // main-loop LDS reads are done
+                                         int wr, int wc, int lane, const IterArgs& A,
+                                         uint16_t* stage) {
+  const int iter = A.iter;
+  const float ca = A.a, cb = A.b, cc = A.c;
+  const bool fin = (KIND == KIND_UPDX) && A.fin != FIN_NONE;
+  // Non-final UPDX of bf16 operands stages X^T through LDS.
+  const bool stage_xt = (KIND == KIND_UPDX) && !F32 && !fin;
+  if (stage_xt) __syncthreads();  // main-loop LDS reads are done
   const int row_base = tm * T + wr + 4 * (lane >> 5);
   const int col_base = tn * T + wc + (lane & 31);
   const bool mirror = G.tri && (tm != tn);
@@ -435,11 +468,14 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
           float* X = G.fbuf;
           const int ldf = G.ld_f;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const size_t o = (size_t)(gi + rr) * ldf + gj;
-            v[rr] = s * fmaf(ca, ld_f32(X + o), v[rr]);
-            st_f32(X + o, v[rr]);
+          for (int rr = 0; rr < 4; ++rr)
+            v[rr] = s * fmaf(ca, ld_f32(X + (size_t)(gi + rr) * ldf + gj), v[rr]);
+          if (fin) {
+            final_write(G, A, gi, gj, v);
+            continue;
           }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) st_f32(X + (size_t)(gi + rr) * ldf + gj, v[rr]);
           void* xt_next = (iter & 1) ? G.out1 : G.out2;
           const int ld1 = G.ld1;
           if constexpr (F32) {
@@ -459,7 +495,7 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
           }
         }
       }
-  if constexpr (kStageXT) {
+  if (stage_xt) {
     __syncthreads();
     uint16_t* xt = static_cast<uint16_t*>((iter & 1) ? G.out1 : G.out2);
     const int ld1 = G.ld1;
@@ -480,8 +516,7 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
 
 template <int KIND, int T, bool F32>
 __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restrict__ tasks,
-                                                   int ntasks, int total_tiles, int iter,
-                                                   float ca, float cb, float cc) {
+                                                   int ntasks, int total_tiles, IterArgs A) {
   using E = typename std::conditional<F32, float, uint16_t>::type;
   constexpr int ESZ = sizeof(E);
   constexpr int BK = 128 / ESZ;           // K elements per stage
@@ -510,7 +545,7 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
 
   const E* __restrict__ Lp = static_cast<const E*>(G.L) + (size_t)tm * T * G.ldl;
   const E* __restrict__ Rp =
-      static_cast<const E*>((iter & 1) ? G.R1 : G.R0) + (size_t)tn * T * G.ldr;
+      static_cast<const E*>((A.iter & 1) ? G.R1 : G.R0) + (size_t)tn * T * G.ldr;
   const int ldl = G.ldl, ldr = G.ldr, kper = G.kper;
   const int nk = G.K / BK;
 
@@ -603,7 +638,7 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
     __syncthreads();
   }
 
-  epilogue<KIND, T, F32, NT>(G, acc, tm, tn, wr, wc, lane, iter, ca, cb, cc, nullptr);
+  epilogue<KIND, T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A, nullptr);
 }
 
 // bf16 main loop fed by direct global->LDS loads (global_load_lds_dwordx4):
@@ -631,8 +666,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int KIND, int T>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restrict__ tasks,
-                                                        int ntasks, int total_tiles, int iter,
-                                                        float ca, float cb, float cc) {
+                                                        int ntasks, int total_tiles, IterArgs A) {
   constexpr int STAGES = 4;
   constexpr int BK = 32;                  // bf16 per row per stage (64 bytes)
   constexpr int WT = T / 2;               // wave tile (2 x 2 waves)
@@ -666,7 +700,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
   {
     const uint16_t* Lp = static_cast<const uint16_t*>(G.L) + (size_t)tm * T * G.ldl;
     const uint16_t* Rp =
-        static_cast<const uint16_t*>((iter & 1) ? G.R1 : G.R0) + (size_t)tn * T * G.ldr;
+        static_cast<const uint16_t*>((A.iter & 1) ? G.R1 : G.R0) + (size_t)tn * T * G.ldr;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = (wave * LPW + i) * 64 + lane;
@@ -738,102 +772,38 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
     }
   }
 
-  epilogue<KIND, T, false, NT>(G, acc, tm, tn, wr, wc, lane, iter, ca, cb, cc, &lds[0][0][0]);
-}
-
-// --------------------------------------------------------------------------
-// Update / output pass over 64 x 64 tiles of the caller's layout.
-//   O[r][c] = X[r][c] (wide) or X[c][r] (tall, staged through LDS)
-//   update:  p <- p * decay - lr * O      output: out <- O
-__global__ __launch_bounds__(EW_THREADS) void update_kernel(
-    const EwTask* __restrict__ tasks, int ntasks, int total_tiles, float lr,
-    float decay, int ns_only) {
-  __shared__ float tile[EW_TILE][EW_TILE + 1];
-  const int gt = blockIdx.x;
-  if (gt >= total_tiles) return;
-  const EwTask& T = tasks[find_task(tasks, ntasks, gt)];
-  const int lt = gt - T.tile_begin;
-  const int r0 = (lt / T.tiles_c) * EW_TILE;
-  const int c0 = (lt % T.tiles_c) * EW_TILE;
-  const int tid = threadIdx.x;
-  const int cx = (tid & 15) * 4;
-  const int ry = tid >> 4;
-
-  if (T.transposed) {
-    // X rows c0.., columns r0..: always inside the padded P x Q buffer.
-    for (int k = 0; k < EW_TILE / 16; ++k) {
-      const int xr = ry + 16 * k;
-      const f32x4 v = ld_f32x4(T.xm + (size_t)(c0 + xr) * T.ldx + r0 + cx);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) tile[xr][cx + e] = v[e];
-    }
-    __syncthreads();
-  }
-  for (int k = 0; k < EW_TILE / 16; ++k) {
-    const int r = ry + 16 * k;
-    const int gr = r0 + r;
-    const int gc = c0 + cx;
-    if (gr >= T.m || gc >= T.n) continue;
-    f32x4 o;
-    if (T.transposed) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = tile[cx + e][r];
-    } else {
-      o = ld_f32x4(T.xm + (size_t)gr * T.ldx + gc);
-    }
-    const size_t idx = (size_t)gr * T.n + gc;
-    if (T.vec && gc + 3 < T.n) {
-      f32x4 outv;
-      if (ns_only) {
-        outv = o;
-      } else {
-        const f32x4 p = load4(T.dst, T.out_dtype, idx);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) outv[e] = fmaf(-lr, o[e], p[e] * decay);
-      }
-      store4(T.dst, T.out_dtype, idx, outv);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (gc + e < T.n) {
-          float val = o[e];
-          if (!ns_only) val = fmaf(-lr, o[e], load1(T.dst, T.out_dtype, idx + e) * decay);
-          store1(T.dst, T.out_dtype, idx + e, val);
-        }
-      }
-    }
-  }
+  epilogue<KIND, T, false, NT>(G, acc, tm, tn, wr, wc, lane, A, &lds[0][0][0]);
 }
 
 template <int KIND, int T>
-hipError_t launch_gemm_f32(const GemmTask* tasks, int ntasks, int total_tiles, int iter, float a,
-                           float b, float c, hipStream_t s) {
+hipError_t launch_gemm_f32(const GemmTask* tasks, int ntasks, int total_tiles, const IterArgs& A,
+                           hipStream_t s) {
   const int grid = (total_tiles + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_reg_kernel<KIND, T, true>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
-                     total_tiles, iter, a, b, c);
+                     total_tiles, A);
   return hipGetLastError();
 }
 
 template <int KIND, int T>
-hipError_t launch_gemm_bf16(const GemmTask* tasks, int ntasks, int total_tiles, int iter, float a,
-                            float b, float c, hipStream_t s) {
+hipError_t launch_gemm_bf16(const GemmTask* tasks, int ntasks, int total_tiles, const IterArgs& A,
+                            hipStream_t s) {
   const int grid = (total_tiles + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_bf16_kernel<KIND, T>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
-                     total_tiles, iter, a, b, c);
+                     total_tiles, A);
   return hipGetLastError();
 }
 
 template <int KIND>
 hipError_t launch_gemm_k(int tile, int f32_ops, const GemmTask* tasks, int ntasks,
-                         int total_tiles, int iter, float a, float b, float c, hipStream_t s) {
+                         int total_tiles, const IterArgs& A, hipStream_t s) {
   if (f32_ops) {
-    if (tile == 64) return launch_gemm_f32<KIND, 64>(tasks, ntasks, total_tiles, iter, a, b, c, s);
-    if (tile == 128) return launch_gemm_f32<KIND, 128>(tasks, ntasks, total_tiles, iter, a, b, c, s);
+    if (tile == 64) return launch_gemm_f32<KIND, 64>(tasks, ntasks, total_tiles, A, s);
+    if (tile == 128) return launch_gemm_f32<KIND, 128>(tasks, ntasks, total_tiles, A, s);
     return hipErrorInvalidValue;
   }
-  if (tile == 64) return launch_gemm_bf16<KIND, 64>(tasks, ntasks, total_tiles, iter, a, b, c, s);
-  if (tile == 128) return launch_gemm_bf16<KIND, 128>(tasks, ntasks, total_tiles, iter, a, b, c, s);
-  if (tile == 256) return launch_gemm_bf16<KIND, 256>(tasks, ntasks, total_tiles, iter, a, b, c, s);
+  if (tile == 64) return launch_gemm_bf16<KIND, 64>(tasks, ntasks, total_tiles, A, s);
+  if (tile == 128) return launch_gemm_bf16<KIND, 128>(tasks, ntasks, total_tiles, A, s);
+  if (tile == 256) return launch_gemm_bf16<KIND, 256>(tasks, ntasks, total_tiles, A, s);
   return hipErrorInvalidValue;
 }
 
@@ -852,24 +822,17 @@ hipError_t launch_norm(const NormTask* tasks, int ntasks, float eps, hipStream_t
 }
 
 hipError_t launch_gemm(int kind, int tile, int f32_ops, const GemmTask* tasks, int ntasks,
-                       int total_tiles, int iter, float a, float b, float c, hipStream_t s) {
+                       int total_tiles, const IterArgs& A, hipStream_t s) {
   switch (kind) {
     case KIND_SYRK:
-      return launch_gemm_k<KIND_SYRK>(tile, f32_ops, tasks, ntasks, total_tiles, iter, a, b, c, s);
+      return launch_gemm_k<KIND_SYRK>(tile, f32_ops, tasks, ntasks, total_tiles, A, s);
     case KIND_POLY:
-      return launch_gemm_k<KIND_POLY>(tile, f32_ops, tasks, ntasks, total_tiles, iter, a, b, c, s);
+      return launch_gemm_k<KIND_POLY>(tile, f32_ops, tasks, ntasks, total_tiles, A, s);
     case KIND_UPDX:
-      return launch_gemm_k<KIND_UPDX>(tile, f32_ops, tasks, ntasks, total_tiles, iter, a, b, c, s);
+      return launch_gemm_k<KIND_UPDX>(tile, f32_ops, tasks, ntasks, total_tiles, A, s);
     default:
       return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_update(const EwTask* tasks, int ntasks, int total_tiles, float lr, float decay,
-                         int ns_only, hipStream_t s) {
-  hipLaunchKernelGGL(update_kernel, dim3(total_tiles), dim3(EW_THREADS), 0, s, tasks, ntasks,
-                     total_tiles, lr, decay, ns_only);
-  return hipGetLastError();
 }
 
 }  // namespace dmuon
