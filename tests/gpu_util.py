@@ -37,3 +37,17 @@ def bf16_ulp(x):
     """Spacing of bfloat16 values at |x| (normal range)."""
     ax = np.maximum(np.abs(x), 2.0 ** -126)
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def bf16_param_excess(p_before, p_after, O, lr):
+    """Error of a bf16 param update p_after ~ RNE(p_before - lr*O) measured
+    beyond the final rounding: the part of |p_after - (p_before - lr*O)|
+    above half an ulp of the stored value, relative to ||lr*O||_F.  Returns
+    (relative excess, share of elements that differ from RNE of the exact
+    value)."""
+    import oracle
+    exact = p_before - lr * O
+    excess = np.maximum(np.abs(p_after - exact) - 0.5 * bf16_ulp(p_after) * 1.0001, 0)
+    e = float(np.linalg.norm(excess) / (lr * np.linalg.norm(O)))
+    frac = float(np.mean(p_after != oracle.round_to_bf16(exact)))
+    return e, frac

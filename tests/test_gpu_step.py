@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import bf16_ulp, exact64, rel_frobenius, sigma_dev, to_dev
+from tests.gpu_util import bf16_param_excess, exact64, rel_frobenius, sigma_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -78,15 +78,12 @@ def _run(cfg, steps, check_ns_steps, shapes=None, cfg_id=None, nesterov=None):
                 # value) may separate p_after from p_before - lr*O_oracle;
                 # whatever exceeds it is NS error and must stay within the
                 # NS tolerance, relative to lr*O.
-                exact = p_before[i] - cfg.lr * O
-                excess = np.maximum(np.abs(p_after - exact) - 0.5 * bf16_ulp(p_after) * 1.0001, 0)
-                e = float(np.linalg.norm(excess) / (cfg.lr * np.linalg.norm(O)))
+                e, frac = bf16_param_excess(p_before[i], p_after, O, cfg.lr)
                 assert e <= ns_tol, ("param excess", step, i, shapes[i], e)
                 # Sanity bound on rounding: the share of elements whose bf16
                 # value differs from RNE(oracle) follows the NS error (a few
                 # percent here); truncating instead of rounding would move
                 # about half of them.
-                frac = float(np.mean(p_after != oracle.round_to_bf16(exact)))
                 assert frac <= 0.25, ("param frac", step, i, frac)
                 report.append(frac)
     return report
