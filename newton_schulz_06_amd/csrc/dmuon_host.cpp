@@ -391,7 +391,6 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.qv = (int32_t)G.q;
           t.dst_trans = G.transposed;
           t.dst_dtype = dst->dtype;
-          t.dst_vec = G.transposed && vec_ok(t.dst, dst->dtype, G.p);
           flops += 2.0 * p * p * q;
         }
         t.tile_begin = acc;

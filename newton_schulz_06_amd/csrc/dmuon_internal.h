@@ -77,8 +77,6 @@ struct GemmTask {
   int32_t pv, qv;          // valid oriented extents p x q
   int32_t dst_trans;
   int32_t dst_dtype;
-  int32_t dst_vec;         // dst_trans only: 4 consecutive r are one aligned access
-  int32_t pad_;
 };
 
 // What the UPDX epilogue does with the new X.

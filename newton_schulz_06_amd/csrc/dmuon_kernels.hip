@@ -21,12 +21,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even, NaN stays NaN: gfx950 converts in
+// hardware (v_cvt_pk_bf16_f32), without a branch.
 __device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t to_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ float from_bf16(uint16_t h) {
@@ -60,13 +66,6 @@ __device__ __forceinline__ float load1(const void* base, int dtype, size_t i) {
                     : from_bf16(ld_u16(static_cast<const uint16_t*>(base) + i));
 }
 
-__device__ __forceinline__ void store1(void* base, int dtype, size_t i, float v) {
-  if (dtype == 0)
-    st_f32(static_cast<float*>(base) + i, v);
-  else
-    st_u16(static_cast<uint16_t*>(base) + i, to_bf16(v));
-}
-
 __device__ __forceinline__ f32x4 load4(const void* base, int dtype, size_t i) {
   f32x4 r;
   if (dtype == 0) {
@@ -83,16 +82,9 @@ __device__ __forceinline__ f32x4 load4(const void* base, int dtype, size_t i) {
 
 __device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d) {
   u32x2 w;
-  w.x = (uint32_t)to_bf16(a) | ((uint32_t)to_bf16(b) << 16);
-  w.y = (uint32_t)to_bf16(c) | ((uint32_t)to_bf16(d) << 16);
+  w.x = to_bf16x2(a, b);
+  w.y = to_bf16x2(c, d);
   return w;
-}
-
-__device__ __forceinline__ void store4(void* base, int dtype, size_t i, f32x4 v) {
-  if (dtype == 0)
-    st_f32x4(static_cast<float*>(base) + i, v);
-  else
-    st_u32x2(static_cast<uint16_t*>(base) + i, pack_bf16x4(v[0], v[1], v[2], v[3]));
 }
 
 // Last task whose tile_begin <= tile (tasks are sorted by tile_begin).
@@ -137,7 +129,9 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
   __shared__ float wsum[EW_THREADS / 64];
   const int gt = blockIdx.x;
   if (gt >= total_tiles) return;
-  const EwTask& T = tasks[find_task(tasks, ntasks, gt)];
+  // A copy, not a reference: stores through the task's pointers could
+  // otherwise alias it and force a reload of every field after each store.
+  const EwTask T = tasks[find_task(tasks, ntasks, gt)];
   const int lt = gt - T.tile_begin;
   const int r0 = (lt / T.tiles_c) * EW_TILE;
   const int c0 = (lt % T.tiles_c) * EW_TILE;
@@ -241,7 +235,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
 __global__ __launch_bounds__(256) void norm_kernel(const NormTask* __restrict__ tasks,
                                                    float eps) {
   __shared__ double wpart[4];
-  const NormTask& T = tasks[blockIdx.x];
+  const NormTask T = tasks[blockIdx.x];
   double acc = 0.0;
   for (int i = threadIdx.x; i < T.tile_count; i += 256)
     acc += (double)ld_f32(T.partial + T.tile_begin + i);
@@ -312,58 +306,43 @@ __device__ __forceinline__ void full_decode(int t, int tiles_m, int tiles_n, int
   tn = w / gsz;
 }
 
-// Kind-specific epilogue of one T x T output tile.  32x32 MFMA output
-// layout: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4 and column
-// l%32 of its block.
-// Last NS iteration: four oriented rows r..r+3 of column c of the new X go
-// to the caller, as the update p <- p*decay - lr*O or as the output O.
-__device__ __forceinline__ void final_write(const GemmTask& G, const IterArgs& A, int r, int c,
-                                            f32x4 v) {
-  if (c >= G.qv || r >= G.pv) return;
-  void* dst = G.dst;
-  const int dt = G.dst_dtype;
-  const bool upd = A.fin == FIN_UPDATE;
-  if (G.dst_trans && G.dst_vec) {  // caller row c holds r..r+3 contiguously
-    const size_t idx = (size_t)c * G.pv + r;
-    f32x4 o = v;
-    if (upd) {
-      const f32x4 p = load4(dst, dt, idx);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = fmaf(-A.lr, v[e], p[e] * A.decay);
-    }
-    store4(dst, dt, idx, o);
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (r + e >= G.pv) break;
-    const size_t idx = G.dst_trans ? (size_t)c * G.pv + r + e : (size_t)(r + e) * G.qv + c;
-    float o = v[e];
-    if (upd) o = fmaf(-A.lr, v[e], load1(dst, dt, idx) * A.decay);
-    store1(dst, dt, idx, o);
-  }
-}
+// Epilogues of one T x T output tile.  32x32 MFMA output layout: lane l,
+// register r holds row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its
+// block; a wave's row of NT blocks is handled at a time, with every global
+// load of that row issued before the first use (no branch in between), so
+// the loads overlap instead of costing one round trip each.
 
+// SYRK (A = s X X^T) and POLY (B = b A + c A A^T) tiles of the upper
+// triangle; off-diagonal tiles are also written mirrored.
 template <int KIND, int T, bool F32, int NT>
-__device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm, int tn,
-                                         int wr, int wc, int lane, const IterArgs& A,
-                                         uint16_t* stage) {
-  const int iter = A.iter;
-  const float ca = A.a, cb = A.b, cc = A.c;
-  const bool fin = (KIND == KIND_UPDX) && A.fin != FIN_NONE;
-  // Non-final UPDX of bf16 operands stages X^T through LDS.
-  const bool stage_xt = (KIND == KIND_UPDX) && !F32 && !fin;
-  if (stage_xt) __syncthreads();  // main-loop LDS reads are done
+__device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
+                                             int tn, int wr, int wc, int lane,
+                                             const IterArgs& A) {
   const int row_base = tm * T + wr + 4 * (lane >> 5);
   const int col_base = tn * T + wc + (lane & 31);
   const bool mirror = G.tri && (tm != tn);
-  float s = 1.f;
-  if (KIND == KIND_SYRK && iter == 0) s = G.scale[1];
-  if (KIND == KIND_UPDX && iter == 0) s = G.scale[0];
+  const float s = (KIND == KIND_SYRK && A.iter == 0) ? G.scale[1] : 1.f;
+  const float cb = A.b, cc = A.c;
   const int P = G.P;
+  float* F = G.fbuf;
+  const int ldf = G.ld_f;
 
 #pragma unroll
-  for (int i = 0; i < NT; ++i)
+  for (int i = 0; i < NT; ++i) {
+    f32x4 av[NT][4];  // POLY: the fp32 A values of this block row
+    if constexpr (KIND == KIND_POLY) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            av[j][g][rr] =
+                ld_f32(F + (size_t)(row_base + i * 32 + 8 * g + rr) * ldf + col_base + j * 32);
+      // keep the loads together: the scheduler would otherwise sink each
+      // one to its use to save registers, serializing the round trips
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -377,11 +356,9 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
         if constexpr (KIND == KIND_SYRK) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) v[rr] *= s;
-          float* A = G.fbuf;
-          const int ldf = G.ld_f;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) st_f32(A + (size_t)(gi + rr) * ldf + gj, v[rr]);
-          if (mirror) st_f32x4(A + (size_t)gj * ldf + gi, v);
+          for (int rr = 0; rr < 4; ++rr) st_f32(F + (size_t)(gi + rr) * ldf + gj, v[rr]);
+          if (mirror) st_f32x4(F + (size_t)gj * ldf + gi, v);
           if constexpr (!F32) {
             uint16_t* o0 = static_cast<uint16_t*>(G.out0);
             const int ld0 = G.ld0;
@@ -423,11 +400,9 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
               }
             }
           }
-        } else if constexpr (KIND == KIND_POLY) {
-          const float* A = G.fbuf;
-          const int ldf = G.ld_f;
+        } else {  // KIND_POLY
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(cb, ld_f32(A + (size_t)(gi + rr) * ldf + gj), cc * v[rr]);
+          for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(cb, av[j][g][rr], cc * v[rr]);
           if constexpr (F32) {
             float* o0 = static_cast<float*>(G.out0);
             const int ld0 = G.ld0;
@@ -464,41 +439,68 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
               }
             }
           }
-        } else {  // KIND_UPDX: X <- s * (a X + B X_raw), s = 1/(||u||+eps) on iter 0
-          float* X = G.fbuf;
-          const int ldf = G.ld_f;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            v[rr] = s * fmaf(ca, ld_f32(X + (size_t)(gi + rr) * ldf + gj), v[rr]);
-          if (fin) {
-            final_write(G, A, gi, gj, v);
-            continue;
-          }
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) st_f32(X + (size_t)(gi + rr) * ldf + gj, v[rr]);
-          void* xt_next = (iter & 1) ? G.out1 : G.out2;
-          const int ld1 = G.ld1;
-          if constexpr (F32) {
-            st_f32x4(static_cast<float*>(xt_next) + (size_t)gj * ld1 + gi, v);
-          } else {
-            uint16_t* xb = static_cast<uint16_t*>(G.out0);
-            const int ld0 = G.ld0;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) st_u16(xb + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
-            // X^T goes through LDS (transposed, 8-byte groups XOR-swizzled)
-            // so that it leaves the tile as full rows.
-            const int il = gi - tm * T, jl = gj - tn * T;
-            const int x = 4 * (jl & (T / 4 - 1));
-            *reinterpret_cast<u32x2*>(stage + jl * T + (il ^ x)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
-            (void)xt_next;
-            (void)ld1;
-          }
         }
       }
-  if (stage_xt) {
+  }
+}
+
+// UPDX, not the last iteration: X <- s (a X + B X_raw) with s = 1/(||u||+eps)
+// on iteration 0.  Writes the fp32 master X, and either X^T in fp32 (fp32
+// operands) or the bf16 X plus X^T in bf16, the latter transposed through
+// LDS (8-byte groups XOR-swizzled) so that it leaves the tile as full rows.
+template <int T, bool F32, int NT>
+__device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
+                                              int tn, int wr, int wc, int lane,
+                                              const IterArgs& A, uint16_t* stage) {
+  if constexpr (!F32) __syncthreads();  // main-loop LDS reads are done
+  const int row_base = tm * T + wr + 4 * (lane >> 5);
+  const int col_base = tn * T + wc + (lane & 31);
+  const float s = A.iter == 0 ? G.scale[0] : 1.f;
+  const float ca = A.a;
+  float* X = G.fbuf;
+  const int ldf = G.ld_f;
+  void* xt_next = (A.iter & 1) ? G.out1 : G.out2;
+  const int ld1 = G.ld1;
+
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    f32x4 xv[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          xv[j][g][rr] =
+              ld_f32(X + (size_t)(row_base + i * 32 + 8 * g + rr) * ldf + col_base + j * 32);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads together (see sym_epilogue)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int gi = row_base + i * 32 + 8 * g;  // rows gi .. gi+3
+        const int gj = col_base + j * 32;
+        f32x4 v;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) v[rr] = s * fmaf(ca, xv[j][g][rr], acc[i][j][4 * g + rr]);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) st_f32(X + (size_t)(gi + rr) * ldf + gj, v[rr]);
+        if constexpr (F32) {
+          st_f32x4(static_cast<float*>(xt_next) + (size_t)gj * ld1 + gi, v);
+        } else {
+          uint16_t* xb = static_cast<uint16_t*>(G.out0);
+          const int ld0 = G.ld0;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) st_u16(xb + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
+          const int il = gi - tm * T, jl = gj - tn * T;
+          const int x = 4 * (jl & (T / 4 - 1));
+          *reinterpret_cast<u32x2*>(stage + jl * T + (il ^ x)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+        }
+      }
+  }
+  if constexpr (!F32) {
     __syncthreads();
-    uint16_t* xt = static_cast<uint16_t*>((iter & 1) ? G.out1 : G.out2);
-    const int ld1 = G.ld1;
+    uint16_t* xt = static_cast<uint16_t*>(xt_next);
     constexpr int CPR = T / 8;            // 16-byte chunks per row
     constexpr int RPP = 256 / CPR;        // rows per pass of the block
     const int tid = threadIdx.x;
@@ -511,6 +513,102 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
       if (pos & 4) { const uint32_t a = w.x, b = w.y; w.x = w.z; w.y = w.w; w.z = a; w.w = b; }
       st_u32x4(xt + (size_t)(tn * T + jl) * ld1 + tm * T + 8 * c, w);
     }
+  }
+}
+
+// UPDX, last iteration: the new X goes straight to the caller's buffer
+// (dtype DT: 0 fp32, 1 bf16), as p <- p*decay - lr*O (FIN_UPDATE) or as
+// O (FIN_OUTPUT).  Oriented element (r, c) lives at dst[r*qv + c], or at
+// dst[c*pv + r] for a transposed caller matrix.  Lanes on padding (outside
+// pv x qv) load dst element 0 and store into their own slot of the padded
+// X buffer, which this iteration no longer needs (the next call's input
+// pass rewrites it): every access is unconditional, so no branch separates
+// the loads from their uses.
+template <int DT>
+__device__ __forceinline__ float dst_load(const void* dst, size_t i) {
+  if constexpr (DT == 0) return ld_f32(static_cast<const float*>(dst) + i);
+  else return from_bf16(ld_u16(static_cast<const uint16_t*>(dst) + i));
+}
+
+template <int DT>
+__device__ __forceinline__ void dst_store(void* p, float v) {
+  if constexpr (DT == 0) st_f32(static_cast<float*>(p), v);
+  else st_u16(static_cast<uint16_t*>(p), to_bf16(v));
+}
+
+template <int T, int NT, int DT>
+__device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
+                                           int tn, int wr, int wc, int lane,
+                                           const IterArgs& A) {
+  const int row_base = tm * T + wr + 4 * (lane >> 5);
+  const int col_base = tn * T + wc + (lane & 31);
+  const float s = A.iter == 0 ? G.scale[0] : 1.f;
+  const float ca = A.a;
+  float* X = G.fbuf;
+  const int ldf = G.ld_f;
+  void* dst = G.dst;
+  constexpr int ESZ = DT == 0 ? 4 : 2;
+  const int pv = G.pv, qv = G.qv;
+  // strides of the oriented row and column index in the caller's buffer
+  const size_t rs = G.dst_trans ? 1 : (size_t)qv;
+  const size_t cs = G.dst_trans ? (size_t)pv : 1;
+  const bool upd = A.fin == FIN_UPDATE;
+
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    f32x4 xv[NT][4], pv4[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          xv[j][g][rr] =
+              ld_f32(X + (size_t)(row_base + i * 32 + 8 * g + rr) * ldf + col_base + j * 32);
+    if (upd) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int r = row_base + i * 32 + 8 * g + rr, c = col_base + j * 32;
+            const size_t idx = (r < pv && c < qv) ? r * rs + c * cs : 0;
+            pv4[j][g][rr] = dst_load<DT>(dst, idx);
+          }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads together (see sym_epilogue)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = row_base + i * 32 + 8 * g + rr, c = col_base + j * 32;
+          float o = s * fmaf(ca, xv[j][g][rr], acc[i][j][4 * g + rr]);
+          if (upd) o = fmaf(-A.lr, o, pv4[j][g][rr] * A.decay);
+          char* to = (r < pv && c < qv)
+                         ? static_cast<char*>(dst) + (r * rs + c * cs) * ESZ
+                         : reinterpret_cast<char*>(X + (size_t)r * ldf + c);
+          dst_store<DT>(to, o);
+        }
+  }
+}
+
+// Dispatch of a finished tile to its epilogue.
+template <int KIND, int T, bool F32, int NT>
+__device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm, int tn,
+                                         int wr, int wc, int lane, const IterArgs& A,
+                                         uint16_t* stage) {
+  if constexpr (KIND == KIND_UPDX) {
+    if (A.fin == FIN_NONE)
+      updx_epilogue<T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A, stage);
+    else if (G.dst_dtype == 0)
+      updx_final<T, NT, 0>(G, acc, tm, tn, wr, wc, lane, A);
+    else
+      updx_final<T, NT, 1>(G, acc, tm, tn, wr, wc, lane, A);
+  } else {
+    sym_epilogue<KIND, T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A);
   }
 }
 
@@ -529,7 +627,9 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
 
   const int vb = xcd_remap(blockIdx.x, gridDim.x);
   if (vb >= total_tiles) return;
-  const GemmTask& G = tasks[find_task(tasks, ntasks, vb)];
+  // By value (see momentum_kernel): the epilogue's stores must not force
+  // reloads of the descriptor.
+  const GemmTask G = tasks[find_task(tasks, ntasks, vb)];
   const int lt = vb - G.tile_begin;
   int tm, tn;
   if (G.tri)
@@ -677,7 +777,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
 
   const int vb = xcd_remap(blockIdx.x, gridDim.x);
   if (vb >= total_tiles) return;
-  const GemmTask& G = tasks[find_task(tasks, ntasks, vb)];
+  // By value (see momentum_kernel): the epilogue's stores must not force
+  // reloads of the descriptor.
+  const GemmTask G = tasks[find_task(tasks, ntasks, vb)];
   const int lt = vb - G.tile_begin;
   int tm, tn;
   if (G.tri)

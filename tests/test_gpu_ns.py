@@ -173,3 +173,21 @@ def test_ns_tiny_shapes():
         gin, outs = _run_ns([g], "f32", "f32")
         want = oracle.direct_newton_schulz(gin[0])
         assert rel_frobenius(outs[0], want) <= 1e-5, shape
+
+
+@pytest.mark.parametrize("prec", ["bf16", "bf16_split"])
+def test_bf16_output_is_rne_of_fp32_output(prec):
+    """The same values (exactly representable in bf16) given once as fp32
+    and once as bf16 go through identical arithmetic; only the final
+    rounding differs, so the bf16 output must equal round-to-nearest-even
+    of the fp32 output bit for bit (pins the kernels' conversion)."""
+    shapes = [(96, 200), (200, 96), (64, 64), (130, 70)]
+    g16 = [to_dev(_gen(s, 60 + i), "bf16") for i, s in enumerate(shapes)]
+    g32 = [g.float() for g in g16]
+    o16 = dm.ns_orthogonalize(g16, prec=prec)
+    o32 = dm.ns_orthogonalize(g32, prec=prec)
+    torch.cuda.synchronize()
+    for s, a, b in zip(shapes, o16, o32):
+        want = oracle.round_to_bf16(exact64(b))
+        got = exact64(a)
+        assert np.array_equal(got, want), (s, int(np.sum(got != want)))
