@@ -29,7 +29,6 @@ METRIC = "Muon step ms & NS TFLOP/s (MFMA util %) per owned matrix batch, 1 GPU"
 # MI355X published dense MFMA peaks (TFLOP/s) and HBM3E bandwidth (GB/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-GEMM_KINDS = ("syrk", "poly", "update_x")
 
 
 def log(msg):
@@ -44,6 +43,25 @@ def ns_flops(shapes, ns_steps):
         p, q = float(min(m, n)), float(max(m, n))
         tot += ns_steps * (p * (p + 1) * q + p * p * (p + 1) + 2 * p * p * q)
     return tot
+
+
+def roofline(row, arith):
+    """Roofline position of a kernel from its algorithmic flops and bytes
+    (summed over its launches) and its measured time: the bound is whichever
+    of the MFMA peak and the HBM peak allows less time for that work."""
+    t_mfma = row["flops"] / (PEAK_TFLOPS[arith] * 1e12) if row["flops"] else 0.0
+    t_hbm = row["bytes"] / (PEAK_HBM_GBS * 1e9)
+    secs = row["ms"] * 1e-3
+    out = {"intensity_flop_per_byte": round(row["flops"] / row["bytes"], 2) if row["bytes"] else None,
+           "mfma_frac": round(t_mfma / secs, 4), "hbm_frac": round(t_hbm / secs, 4)}
+    if t_mfma >= t_hbm:
+        achieved, peak = row["flops"] / secs / 1e12, PEAK_TFLOPS[arith]
+        out.update({"bound": "mfma", "unit": "TFLOP/s"})
+    else:
+        achieved, peak = row["bytes"] / secs / 1e9, PEAK_HBM_GBS
+        out.update({"bound": "hbm", "unit": "GB/s"})
+    out.update({"achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4)})
+    return out
 
 
 def parse():
@@ -220,16 +238,10 @@ def main():
         f"NS {ns_tflops:.1f} TFLOP/s")
 
     row = prof.rows[dominant]
-    if dominant in GEMM_KINDS:
-        achieved = row["flops"] / row["ms"] / 1e9
-        peak = PEAK_TFLOPS[arith]
-        roof = {"bound": "mfma", "unit": "TFLOP/s"}
-    else:
-        achieved = row["bytes"] / row["ms"] / 1e6
-        peak = PEAK_HBM_GBS
-        roof = {"bound": "hbm", "unit": "GB/s"}
-    roof.update({"kernel": dominant, "achieved": round(achieved, 2), "peak": peak,
-                 "frac": round(achieved / peak, 4),
+    roof = roofline(row, arith)
+    roof.update({"kernel": dominant,
+                 "flops_per_launch": row["flops"] / row["launches"],
+                 "bytes_per_launch": row["bytes"] / row["launches"],
                  "avg_launch_ms": round(row["ms"] / row["launches"], 5),
                  "launches": row["launches"],
                  "traffic": traffic_for(dominant, cfg.name)})

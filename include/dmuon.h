@@ -171,8 +171,10 @@ const char* dmuon_backend_info(void);
  * fills up to `max` rows of `out` (one per kind that ran), returning the
  * number of rows, or -1 on error.  `flops` and `bytes` are the algorithmic
  * work of those launches: symmetric-aware flops of the NS products
- * (p(p+1)q for A = X X^T, p^2(p+1) for A A, 2p^2q for B X); for the
- * element-wise kernels, the bytes the step must move at minimum.
+ * (p(p+1)q for A = X X^T, p^2(p+1) for A A, 2p^2q for B X), and the HBM
+ * bytes of each launch with every operand read once and every output
+ * written once in the library's workspace layout (for the element-wise
+ * kernels, the bytes the step must move at minimum).
  * Kinds: 0 momentum, 1 input, 2 norm, 3 syrk, 4 poly, 5 update_x.  The
  * last update_x launch of a call also applies the parameter update (or
  * writes the NS output), so there is no separate update kind.

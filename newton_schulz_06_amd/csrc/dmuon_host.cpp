@@ -235,6 +235,10 @@ struct GemmLaunch {
   size_t off;  // byte offset of the task array in the device table
   int ntasks, total;
   double flops;
+  // Algorithmic HBM bytes of one launch: every operand read once, every
+  // output written once, in the designed layout; UPDX differs on the last
+  // iteration (caller's param or output instead of the next X copies).
+  double bytes, bytes_fin;
 };
 
 struct Plan {
@@ -328,7 +332,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
     for (int tile : kTiles) {
       const size_t begin = gtasks.size();
       int acc = 0;
-      double flops = 0;
+      double flops = 0, bytes = 0, bytes_fin = 0;
       for (int i = 0; i < n; ++i) {
         const Geom& G = L.g[i];
         if (G.tile != tile) continue;
@@ -353,6 +357,8 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.out1 = t.split ? ws + G.r3 : nullptr;
           t.ld0 = t.ld1 = (int32_t)G.ld_aop;
           flops += p * (p + 1) * q;
+          // X operand in; fp32 A and its operand form (bf16, or L3 + R3) out
+          bytes += (L.f32_ops ? 4.0 : 2.0) * p * q + p * p * (4.0 + (L.f32_ops ? 0.0 : G.split_a ? 12.0 : 2.0));
         } else if (kind == KIND_POLY) {
           t.split = G.split_b;  // writes B as [hi|lo]
           t.L = ws + G.aop;
@@ -367,6 +373,9 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.out0 = ws + G.bop;
           t.ld0 = (int32_t)G.ld_bop;
           flops += p * p * (p + 1);
+          // A operand (bf16, L3 + R3, or fp32) and fp32 A in; B operand out
+          bytes += p * p * ((L.f32_ops ? 4.0 : G.split_a ? 12.0 : 2.0) + 4.0 +
+                            (L.f32_ops ? 4.0 : G.split_b ? 4.0 : 2.0));
         } else {
           t.L = ws + G.bop;
           t.R0 = ws + G.xt0;
@@ -392,13 +401,24 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.dst_trans = G.transposed;
           t.dst_dtype = dst->dtype;
           flops += 2.0 * p * p * q;
+          // B operand, X^T and the fp32 X in; then either fp32 X, bf16 X and
+          // X^T out, or (last iteration) the caller's matrix read (update
+          // only) and written
+          {
+            const double bop = L.f32_ops ? 4.0 : G.split_b ? 4.0 : 2.0;
+            const double xt = L.f32_ops ? 4.0 : 2.0;
+            const double in = p * p * bop + p * q * (xt + 4.0);
+            bytes += in + p * q * (4.0 + xt + (L.f32_ops ? 0.0 : 2.0));
+            bytes_fin += in + p * q * esize(dst->dtype) * (ns_only ? 1.0 : 2.0);
+          }
         }
         t.tile_begin = acc;
         acc += t.tile_count;
         gtasks.push_back(t);
       }
       if (gtasks.size() > begin) {
-        GemmLaunch gl{kind, tile, 0, (int)(gtasks.size() - begin), acc, flops};
+        GemmLaunch gl{kind, tile, 0, (int)(gtasks.size() - begin), acc, flops, bytes,
+                      kind == KIND_UPDX ? bytes_fin : bytes};
         plan->gemms.push_back(gl);
         ranges.push_back({begin, gtasks.size()});
       }
@@ -548,7 +568,8 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
     }
     for (const GemmLaunch& gl : plan.gemms) {
       const GemmTask* tasks = reinterpret_cast<const GemmTask*>(tab + gl.off);
-      st = check(timed(gl.kind, gl.flops, 0, s,
+      const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
+      st = check(timed(gl.kind, gl.flops, bytes, s,
                        [&] {
                          return launch_gemm(gl.kind, gl.tile, plan.f32_ops, tasks, gl.ntasks,
                                             gl.total, args, s);

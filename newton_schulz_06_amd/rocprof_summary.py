@@ -6,9 +6,9 @@
 `trace` prints per-kernel dispatch counts and average durations from the
 kernel trace; `counter` prints per-kernel averages of every collected
 counter.  With `copy_mib`, the plain copy of that many MiB that
-``bench.py --calib-copy`` runs is located by its size and the ratio
-known / measured is printed as the scale factor for FETCH_SIZE and
-WRITE_SIZE (KiB per dispatch).
+``bench.py --calib-copy`` runs (the largest dispatch of the runtime's copy
+kernel) gives the ratio known / measured, printed as the scale factor for
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch).
 """
 import collections
 import csv
@@ -56,28 +56,25 @@ def trace(dirname):
 def counter(dirname, copy_mib=None):
     path = _csv(dirname, "counter_collection.csv")
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
-    sizes = {}
+    raw = collections.defaultdict(dict)  # counter -> {(dispatch, kernel name): value}
     for r in csv.DictReader(open(path)):
         k = short_name(r["Kernel_Name"])
         vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
-        sizes[(k, r["Dispatch_Id"])] = int(r["Grid_Size"])
+        raw[r["Counter_Name"]][(r["Dispatch_Id"], r["Kernel_Name"])] = float(r["Counter_Value"])
     for k, cs in vals.items():
         parts = [f"{c}={sum(v) / len(v):.1f}" for c, v in sorted(cs.items())]
         print(f"{k:42s} n={len(next(iter(cs.values())))}  " + "  ".join(parts))
     if copy_mib:
+        # The plain device copy of ``bench.py --calib-copy`` is the largest
+        # dispatch of the runtime's copy kernel in the run.
         known_kib = float(copy_mib) * 1024.0
-        best = None
-        for k, cs in vals.items():
-            for c in ("FETCH_SIZE", "WRITE_SIZE"):
-                for v in cs.get(c, []):
-                    if v > 0 and abs(v - known_kib) / known_kib < 0.25:
-                        best = (k, c, v) if best is None else best
-        if best:
-            k, c, v = best
-            print(f"calibration: {k} {c}={v:.1f} KiB for a {copy_mib} MiB copy -> "
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            vs = [v for (k, name), v in raw.get(c, {}).items() if "copyBuffer" in name]
+            if not vs:
+                continue
+            v = max(vs)
+            print(f"calibration: {c}={v:.1f} KiB for a {copy_mib} MiB copy -> "
                   f"scale {known_kib / v:.4f}")
-        else:
-            print("calibration: no dispatch near the copy size found")
 
 
 if __name__ == "__main__":

@@ -1,0 +1,33 @@
+"""Host-side logic of bench.py: the algorithmic flop count, the roofline
+bound choice, and the single-GPU guard (no GPU needed)."""
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+
+def test_ns_flops_formula():
+    # p=2, q=3, one step: p(p+1)q + p^2(p+1) + 2p^2q = 18 + 12 + 24
+    assert bench.ns_flops([(3, 2)], 1) == 54.0
+    assert bench.ns_flops([(2, 3), (3, 2)], 5) == 2 * 5 * 54.0
+
+
+def test_roofline_picks_the_binding_peak():
+    # 2.5e12 flops take 1 ms at the bf16 peak; 8e9 bytes take 1 ms at 8 TB/s
+    row = {"flops": 2.5e12, "bytes": 1e9, "ms": 2.0, "launches": 1}
+    r = bench.roofline(row, "bf16")
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["frac"] == pytest.approx(0.5) and r["achieved"] == pytest.approx(1250.0)
+    row = {"flops": 2.5e11, "bytes": 8e9, "ms": 4.0, "launches": 2}
+    r = bench.roofline(row, "bf16")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["frac"] == pytest.approx(0.25) and r["mfma_frac"] == pytest.approx(0.025)
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
