@@ -742,12 +742,18 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
 }
 
 // bf16 main loop fed by direct global->LDS loads (global_load_lds_dwordx4):
-// STAGES buffers of K = 32 per stage (64-byte rows) are kept in flight, so
-// each K-step's loads were issued STAGES-1 steps before they are consumed.
-// Rows are stored without padding; the 16-byte chunk of k-slot `kc` of row
-// r lives at slot kc ^ swz(r), which makes the 16-byte operand reads of 16
-// consecutive rows hit distinct bank groups (and 8 rows for 32 banks).
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// STAGES buffers of BK k-values per row are kept in flight, so each K-step's
+// loads were issued STAGES-1 steps before they are consumed.  Rows are
+// stored without padding as CPR = BK/8 chunks of 16 bytes; k-chunk `kc` of
+// row r lives at slot kc ^ swz(r), which makes the 16-byte operand reads of
+// 8 consecutive rows (one LDS access phase) hit distinct banks: with 64-byte
+// rows two rows share a 128-byte bank line, with 128-byte rows each row
+// spans all banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 4) return ((r >> 1) ^ (r >> 2)) & 3;
+  else return r & (CPR - 1);
+}
 
 // 16 bytes per lane from global memory straight into LDS at the wave-uniform
 // base `lds` (lane l lands at lds + 16*l).  Kept out of the kernel templates:
@@ -764,14 +770,38 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Waits until at most `younger` stages of LOADS loads each are outstanding
+// (younger <= MAXY; a wave-uniform value, so the branches are scalar).
+template <int LOADS, int MAXY>
+__device__ __forceinline__ void wait_stages(int younger) {
+  if constexpr (MAXY == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (younger >= MAXY) wait_vmcnt<MAXY * LOADS>();
+    else wait_stages<LOADS, MAXY - 1>(younger);
+  }
+}
+
+// K depth of a stage (bf16 per row) and stages in flight, per tile size.
+// LDS holds STAGES x 2 operands x T rows x 2*BK bytes: 48 KB (T = 64),
+// 64 KB (128), 128 KB (256).  128-byte rows halve the number of L2
+// requests against 64-byte rows; measured on the NS shapes, that beats
+// keeping more (shallower) stages in flight.
+template <int T>
+constexpr int kBK = 64;
+template <int T>
+constexpr int kStages = T == 64 ? 3 : 2;
+
 template <int KIND, int T>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restrict__ tasks,
                                                         int ntasks, int total_tiles, IterArgs A) {
-  constexpr int STAGES = 4;
-  constexpr int BK = 32;                  // bf16 per row per stage (64 bytes)
+  constexpr int STAGES = kStages<T>;
+  constexpr int BK = kBK<T>;              // bf16 per row per stage
+  constexpr int CPR = BK / 8;             // 16-byte chunks per row
   constexpr int WT = T / 2;               // wave tile (2 x 2 waves)
   constexpr int NT = WT / 32;             // 32x32 MFMA blocks per wave side
-  constexpr int LPW = T / 64;             // 1 KB load instructions per wave per operand
+  constexpr int LPW = T * CPR / 256;      // 1 KB load instructions per wave per operand
+  static_assert(LPW >= 1 && (STAGES - 2) * 2 * LPW < 64, "stage shape");
   constexpr int LOADS = 2 * LPW;          // loads per thread per stage
   __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES][2][T * BK];
 
@@ -796,7 +826,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
   const int kper = G.kper;
 
   // Per-lane global source of each load instruction: chunk c of the stage
-  // (row c/4, slot c%4) holds global k-chunk slot ^ swz(row).
+  // (row c/CPR, slot c%CPR) holds global k-chunk slot ^ swz(row).
   const uint16_t* srcL[LPW];
   const uint16_t* srcR[LPW];
   {
@@ -806,8 +836,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = (wave * LPW + i) * 64 + lane;
-      const int row = c >> 2;
-      const int kc = (c & 3) ^ swz(row);
+      const int row = c / CPR;
+      const int kc = (c % CPR) ^ swz<CPR>(row);
       srcL[i] = Lp + (size_t)row * G.ldl + kc * 8;
       srcR[i] = Rp + (size_t)row * G.ldr + kc * 8;
     }
@@ -832,16 +862,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // Operand read offsets (elements) inside a stage buffer, per k-substep.
-  int offA[2][NT], offB[2][NT];
+  constexpr int KS = BK / 16;  // MFMA k-substeps per stage
+  int offA[KS][NT], offB[KS][NT];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int kc = ks * 2 + (lane >> 5);
       const int ra = wr + t * 32 + (lane & 31);
       const int rb = wc + t * 32 + (lane & 31);
-      offA[ks][t] = ra * BK + 8 * (kc ^ swz(ra));
-      offB[ks][t] = rb * BK + 8 * (kc ^ swz(rb));
+      offA[ks][t] = ra * BK + 8 * (kc ^ swz<CPR>(ra));
+      offB[ks][t] = rb * BK + 8 * (kc ^ swz<CPR>(rb));
     }
 
 #pragma unroll
@@ -850,16 +881,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
 
   for (int kt = 0; kt < nk; ++kt) {
     // Stage kt must have landed: allow the younger stages to stay in flight.
-    const int younger = min(nk - 1 - kt, STAGES - 2);
-    if (younger >= 2) wait_vmcnt<2 * LOADS>();
-    else if (younger == 1) wait_vmcnt<LOADS>();
-    else wait_vmcnt<0>();
+    wait_stages<LOADS, STAGES - 2>(min(nk - 1 - kt, STAGES - 2));
     __builtin_amdgcn_s_barrier();
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     const uint16_t* sa = lds[kt % STAGES][0];
     const uint16_t* sb = lds[kt % STAGES][1];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       bf16x8 a[NT], b[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
