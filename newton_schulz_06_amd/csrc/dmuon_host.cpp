@@ -69,13 +69,14 @@ int64_t ld_for(int64_t n, int64_t esz) {
 struct Geom {
   int64_t m, n, p, q, P, Q;
   int tile, transposed, split_a, split_b;
+  int hilo;  // master X as bf16 X + bf16 remainder (else fp32, next to bf16 X)
   int64_t ld_xm, ld_xb, ld_xt, ld_a32, ld_aop, ld_bop;  // row strides (elements)
-  size_t xm, xb, xt0, xt1, a32, aop, r3, bop;          // byte offsets in ws
+  size_t xm, xb, xlo, xt0, xt1, a32, aop, bop;         // byte offsets in ws
 };
 
 struct Layout {
   std::vector<Geom> g;
-  size_t partial_off = 0, scale_off = 0, total = 0;
+  size_t partial_off = 0, scale_off = 0, sink_off = 0, total = 0;
   int64_t in_tiles = 0;
   int f32_ops = 0;
 };
@@ -114,6 +115,8 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
   off = align_up(off + sizeof(float) * (size_t)tiles, kWsAlign);
   L.scale_off = off;
   off = align_up(off + sizeof(float) * 4 * (size_t)n, kWsAlign);
+  L.sink_off = off;  // writable bytes nothing reads (padding lanes' stores)
+  off = align_up(off + 16, kWsAlign);
   const int64_t e = L.f32_ops ? 4 : 2;
   for (int i = 0; i < n; ++i) {
     Geom& G = L.g[i];
@@ -127,21 +130,23 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
     G.ld_xb = ld_for(G.Q, 2);
     G.ld_xt = ld_for(G.P, e);
     G.ld_a32 = ld_for(G.P, 4);
-    G.xm = take(4 * P * G.ld_xm);
-    G.xb = L.f32_ops ? 0 : take(2 * P * G.ld_xb);
+    G.xm = G.xb = G.xlo = G.a32 = 0;
+    // Same rule as the kernels' kHiLoMaster: tiles below 256.
+    G.hilo = !L.f32_ops && G.tile < 256;
+    if (!G.hilo) G.xm = take(4 * P * G.ld_xm);       // fp32 X
+    if (!L.f32_ops) G.xb = take(2 * P * G.ld_xb);    // bf16 X
+    if (G.hilo) G.xlo = take(2 * P * G.ld_xb);       // bf16 (X - bf16 X)
     G.xt0 = take(e * Q * G.ld_xt);
     G.xt1 = take(e * Q * G.ld_xt);
-    G.a32 = take(4 * P * G.ld_a32);
+    if (L.f32_ops || !G.split_a) G.a32 = take(4 * P * G.ld_a32);
     if (L.f32_ops) {
       G.aop = G.a32;
       G.ld_aop = G.ld_a32;
-      G.r3 = 0;
       G.ld_bop = ld_for(G.P, 4);
       G.bop = take(4 * P * G.ld_bop);
     } else {
-      G.ld_aop = ld_for(G.split_a ? 3 * G.P : G.P, 2);
+      G.ld_aop = ld_for(G.split_a ? 4 * G.P : G.P, 2);  // [hi|lo|hi|hi] rows when split
       G.aop = take(2 * P * G.ld_aop);
-      G.r3 = G.split_a ? take(2 * P * G.ld_aop) : 0;
       G.ld_bop = ld_for(G.split_b ? 2 * G.P : G.P, 2);
       G.bop = take(2 * P * G.ld_bop);
     }
@@ -302,8 +307,9 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
     t.f32_ops = L.f32_ops;
     t.src = src->mats[i].ptr;
     t.buf = bufs ? static_cast<float*>(bufs->mats[i].ptr) : nullptr;
-    t.xm = reinterpret_cast<float*>(ws + G.xm);
+    t.xm = G.hilo ? nullptr : reinterpret_cast<float*>(ws + G.xm);
     t.xb = L.f32_ops ? nullptr : reinterpret_cast<uint16_t*>(ws + G.xb);
+    t.xlo = G.hilo ? reinterpret_cast<uint16_t*>(ws + G.xlo) : nullptr;
     t.xt = ws + G.xt0;
     t.partial = partial;
     t.scale = scale + 4 * i;
@@ -350,31 +356,35 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.tiles_m = t.tiles_n = nt;
           t.tri = 1;
           t.tile_count = nt * (nt + 1) / 2;
-          t.fbuf = reinterpret_cast<float*>(ws + G.a32);
+          t.split = G.split_a;  // writes A as [hi|lo|hi|hi] rows, no fp32 A
+          t.fbuf = t.split ? nullptr : reinterpret_cast<float*>(ws + G.a32);
           t.ld_f = (int32_t)G.ld_a32;
-          t.split = G.split_a;  // writes A as [hi|hi|lo] / [hi|lo|hi]
           t.out0 = L.f32_ops ? nullptr : ws + G.aop;
-          t.out1 = t.split ? ws + G.r3 : nullptr;
-          t.ld0 = t.ld1 = (int32_t)G.ld_aop;
+          t.ld0 = (int32_t)G.ld_aop;
           flops += p * (p + 1) * q;
-          // X operand in; fp32 A and its operand form (bf16, or L3 + R3) out
-          bytes += (L.f32_ops ? 4.0 : 2.0) * p * q + p * p * (4.0 + (L.f32_ops ? 0.0 : G.split_a ? 12.0 : 2.0));
+          // X operand in; fp32 A and/or its operand form out
+          bytes += (L.f32_ops ? 4.0 : 2.0) * p * q +
+                   p * p * (L.f32_ops ? 4.0 : G.split_a ? 8.0 : 6.0);
         } else if (kind == KIND_POLY) {
           t.split = G.split_b;  // writes B as [hi|lo]
+          // Split A: L = columns 0..3P of the [hi|lo|hi|hi] rows, R =
+          // columns P..4P, so L R^T = hi lo^T + lo hi^T + hi hi^T.
           t.L = ws + G.aop;
-          t.R0 = t.R1 = G.split_a ? ws + G.r3 : ws + G.aop;
+          t.R0 = t.R1 = ws + G.aop + (G.split_a ? 2 * (size_t)P : 0);
           t.ldl = t.ldr = (int32_t)G.ld_aop;
           t.K = t.kper = G.split_a ? 3 * P : P;
           t.tiles_m = t.tiles_n = nt;
           t.tri = 1;
           t.tile_count = nt * (nt + 1) / 2;
-          t.fbuf = reinterpret_cast<float*>(ws + G.a32);
+          t.fbuf = G.split_a ? nullptr : reinterpret_cast<float*>(ws + G.a32);
           t.ld_f = (int32_t)G.ld_a32;
+          t.ahl = G.split_a ? reinterpret_cast<const uint16_t*>(ws + G.aop) : nullptr;
+          t.ld_ahl = (int32_t)G.ld_aop;
           t.out0 = ws + G.bop;
           t.ld0 = (int32_t)G.ld_bop;
           flops += p * p * (p + 1);
-          // A operand (bf16, L3 + R3, or fp32) and fp32 A in; B operand out
-          bytes += p * p * ((L.f32_ops ? 4.0 : G.split_a ? 12.0 : 2.0) + 4.0 +
+          // A in (fp32; bf16 + fp32; or the split rows); B operand out
+          bytes += p * p * ((L.f32_ops ? 4.0 : G.split_a ? 8.0 : 6.0) +
                             (L.f32_ops ? 4.0 : G.split_b ? 4.0 : 2.0));
         } else {
           t.L = ws + G.bop;
@@ -388,10 +398,12 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.tiles_n = Q / tile;
           t.tri = 0;
           t.tile_count = t.tiles_m * t.tiles_n;
-          t.fbuf = reinterpret_cast<float*>(ws + G.xm);
+          t.fbuf = G.hilo ? nullptr : reinterpret_cast<float*>(ws + G.xm);
           t.ld_f = (int32_t)G.ld_xm;
           t.out0 = L.f32_ops ? nullptr : ws + G.xb;
+          t.xlo = G.hilo ? reinterpret_cast<uint16_t*>(ws + G.xlo) : nullptr;
           t.ld0 = (int32_t)G.ld_xb;
+          t.sink = ws + L.sink_off;
           t.out1 = ws + G.xt0;
           t.out2 = ws + G.xt1;
           t.ld1 = (int32_t)G.ld_xt;
@@ -401,14 +413,15 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.dst_trans = G.transposed;
           t.dst_dtype = dst->dtype;
           flops += 2.0 * p * p * q;
-          // B operand, X^T and the fp32 X in; then either fp32 X, bf16 X and
-          // X^T out, or (last iteration) the caller's matrix read (update
-          // only) and written
+          // B operand, X^T and the master X (fp32, or bf16 X + remainder)
+          // in; then the master X and X^T out, or (last iteration) the
+          // caller's matrix read (update only) and written
           {
             const double bop = L.f32_ops ? 4.0 : G.split_b ? 4.0 : 2.0;
             const double xt = L.f32_ops ? 4.0 : 2.0;
             const double in = p * p * bop + p * q * (xt + 4.0);
-            bytes += in + p * q * (4.0 + xt + (L.f32_ops ? 0.0 : 2.0));
+            // master out: fp32 (+ bf16 copy), or bf16 X + remainder
+            bytes += in + p * q * (xt + (L.f32_ops ? 4.0 : G.hilo ? 4.0 : 6.0));
             bytes_fin += in + p * q * esize(dst->dtype) * (ns_only ? 1.0 : 2.0);
           }
         }

@@ -43,8 +43,9 @@ struct EwTask {
   int32_t vec;             // 1: caller buffers allow 16-byte (4-element) access
   const void* src;         // grad (step) or G (NS only)
   float* buf;              // momentum buffer (step) or null
-  float* xm;               // fp32 master X, P x Q
-  uint16_t* xb;            // bf16 X, P x Q (null when f32_ops)
+  float* xm;               // fp32 X, P x Q (f32_ops only)
+  uint16_t* xb;            // bf16 X = high part of X, P x Q (bf16 modes)
+  uint16_t* xlo;           // bf16 X - xb, P x Q, stride ldxb (bf16 modes)
   void* xt;                // X^T, Q x P (bf16 or fp32)
   float* partial;          // per-tile sums of squares (indexed by global tile)
   float* scale;            // per-matrix scalars: [0]=1/(s+eps) [1]=its square
@@ -61,15 +62,21 @@ struct GemmTask {
   int32_t ldl, ldr, K, kper;
   int32_t tiles_m, tiles_n, tile_begin, tile_count;
   int32_t tri;             // 1: upper-triangle tiles only (+ mirrored write)
-  int32_t split;           // 1: bf16 hi/lo operand layout in the epilogue
+  int32_t split;           // SYRK: write A as [hi|lo|hi|hi]; POLY: write B as [hi|lo]
   int32_t P;               // padded p (segment offset of split layouts)
   int32_t ld_f;            // stride of fbuf
-  float* fbuf;             // SYRK: A (out)  POLY: A (in)  UPDX: X master
-  void* out0;              // SYRK: A operand / L3  POLY: B operand  UPDX: Xb
-  void* out1;              // SYRK: R3            UPDX: X^T (even iter)
+  float* fbuf;             // fp32 A (SYRK out, POLY in; null when A is split)
+                           // or fp32 X (UPDX, fp32 operands)
+  void* out0;              // SYRK: A operand  POLY: B operand  UPDX: bf16 X
+  void* out1;              // UPDX: X^T (even iter)
   void* out2;              // UPDX: X^T (odd iter)
   int32_t ld0, ld1;
   const float* scale;      // per-matrix scalars (see EwTask::scale)
+  uint16_t* xlo;           // UPDX, bf16 operands: X - bf16 X (stride ld0)
+  const uint16_t* ahl;     // POLY with split A: A as [hi | lo | ...] rows
+  int32_t ld_ahl;          // its row stride
+  int32_t pad0_;
+  void* sink;              // 16 writable, never-read bytes (see updx_final)
   // UPDX, last iteration: the caller's param (step) or output (NS only).
   // Oriented element (r, c), r < pv, c < qv, sits at dst[r*qv + c], or at
   // dst[c*pv + r] when dst_trans (caller's matrix is the transpose).

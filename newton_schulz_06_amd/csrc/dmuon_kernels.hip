@@ -2,12 +2,13 @@
 //
 // Data layout in the workspace, per matrix (p = min(m, n), q = max(m, n),
 // P and Q padded up to the GEMM tile; every pad element is kept at zero):
-//   xm    fp32 master copy of the oriented X, P x Q row-major
-//   xb    bf16 copy of X (the SYRK operand), P x Q           [bf16 modes]
+//   xm    fp32 X (the oriented G), P x Q row-major         [fp32 mode]
+//   xb    bf16 X (the SYRK operand), P x Q                  [bf16 modes]
+//   xlo   bf16 (X - xb): xb + xlo is the master X          [bf16 modes]
 //   xt    X^T, Q x P, two buffers used in turn (the B X operand)
-//   a32   fp32 A = X X^T, P x P
-//   aop   A as MFMA operand: bf16 P x P, or hi/lo layouts   [bf16 modes]
-//   bop   B = bA + cA^2 as MFMA operand (fp32 / bf16 / hi-lo)
+//   a32   fp32 A = X X^T, P x P                     [unless A is split]
+//   aop   A as MFMA operand: bf16 P x P, or [hi|lo|hi|hi] rows (4P)
+//   bop   B = bA + cA^2 as MFMA operand (fp32 / bf16 / [hi|lo] rows)
 // With every operand stored K-contiguous, all three products of one NS
 // iteration are "NT" products C = L R^T and share one MFMA main loop.
 #include <type_traits>
@@ -85,6 +86,36 @@ __device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d)
   w.x = to_bf16x2(a, b);
   w.y = to_bf16x2(c, d);
   return w;
+}
+
+__device__ __forceinline__ f32x4 unpack_bf16x4(u32x2 w) {
+  f32x4 r;
+  r[0] = __uint_as_float(w.x << 16);
+  r[1] = __uint_as_float(w.x & 0xffff0000u);
+  r[2] = __uint_as_float(w.y << 16);
+  r[3] = __uint_as_float(w.y & 0xffff0000u);
+  return r;
+}
+
+// The master copy of X, four consecutive elements at offset o (of the
+// fp32 row stride ldx or the bf16 row stride ldxb): fp32 only (fp32
+// operands); fp32 plus its bf16 rounding (bf16 operands, no xlo); or the
+// bf16 rounding `hi` plus the bf16 rounding of the remainder (xlo given),
+// which keeps about 16 significant bits.  The bf16 X is the SYRK operand.
+__device__ __forceinline__ void store_master4(const EwTask& T, size_t row, int col, f32x4 u) {
+  if (T.f32_ops) {
+    st_f32x4(T.xm + row * T.ldx + col, u);
+    return;
+  }
+  const u32x2 hi = pack_bf16x4(u[0], u[1], u[2], u[3]);
+  st_u32x2(T.xb + row * T.ldxb + col, hi);
+  if (T.xlo) {
+    const f32x4 h = unpack_bf16x4(hi);
+    st_u32x2(T.xlo + row * T.ldxb + col,
+             pack_bf16x4(u[0] - h[0], u[1] - h[1], u[2] - h[2], u[3] - h[3]));
+  } else {
+    st_f32x4(T.xm + row * T.ldx + col, u);
+  }
 }
 
 // Last task whose tile_begin <= tile (tasks are sorted by tile_begin).
@@ -185,9 +216,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
     }
     // Same-layout copy: X itself for a wide matrix, X^T for a tall one.
     if (!T.transposed) {
-      st_f32x4(T.xm + (size_t)gr * T.ldx + gc, u);
-      if (!f32ops)
-        st_u32x2(T.xb + (size_t)gr * T.ldxb + gc, pack_bf16x4(u[0], u[1], u[2], u[3]));
+      store_master4(T, (size_t)gr, gc, u);
     } else {
       const size_t o = (size_t)gr * T.ldt + gc;
       if (f32ops)
@@ -212,9 +241,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
       else
         st_u32x2(static_cast<uint16_t*>(T.xt) + o, pack_bf16x4(v[0], v[1], v[2], v[3]));
     } else {
-      st_f32x4(T.xm + (size_t)orow * T.ldx + ocol, v);
-      if (!f32ops)
-        st_u32x2(T.xb + (size_t)orow * T.ldxb + ocol, pack_bf16x4(v[0], v[1], v[2], v[3]));
+      store_master4(T, (size_t)orow, ocol, v);
     }
   }
   // Block sum of squares, fixed order.
@@ -313,8 +340,9 @@ __device__ __forceinline__ void full_decode(int t, int tiles_m, int tiles_n, int
 // the loads overlap instead of costing one round trip each.
 
 // SYRK (A = s X X^T) and POLY (B = b A + c A A^T) tiles of the upper
-// triangle; off-diagonal tiles are also written mirrored.
-template <int KIND, int T, bool F32, int NT>
+// triangle; off-diagonal tiles are also written mirrored.  AHL: POLY reads
+// A as hi + lo from the split operand rows instead of the fp32 A.
+template <int KIND, int T, bool F32, int NT, bool AHL>
 __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
                                              int tn, int wr, int wc, int lane,
                                              const IterArgs& A) {
@@ -329,16 +357,22 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
 
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    f32x4 av[NT][4];  // POLY: the fp32 A values of this block row
+    f32x4 av[NT][4];  // POLY: the A values of this block row
     if constexpr (KIND == KIND_POLY) {
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            av[j][g][rr] =
-                ld_f32(F + (size_t)(row_base + i * 32 + 8 * g + rr) * ldf + col_base + j * 32);
+          for (int rr = 0; rr < 4; ++rr) {
+            const int r = row_base + i * 32 + 8 * g + rr, c = col_base + j * 32;
+            if constexpr (AHL) {
+              const uint16_t* h = G.ahl + (size_t)r * G.ld_ahl + c;
+              av[j][g][rr] = from_bf16(ld_u16(h)) + from_bf16(ld_u16(h + P));
+            } else {
+              av[j][g][rr] = ld_f32(F + (size_t)r * ldf + c);
+            }
+          }
       // keep the loads together: the scheduler would otherwise sink each
       // one to its use to save registers, serializing the round trips
       __builtin_amdgcn_sched_barrier(0);
@@ -356,9 +390,11 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
         if constexpr (KIND == KIND_SYRK) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) v[rr] *= s;
+          if (!G.split) {  // fp32 A, read back by the polynomial epilogue
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) st_f32(F + (size_t)(gi + rr) * ldf + gj, v[rr]);
-          if (mirror) st_f32x4(F + (size_t)gj * ldf + gi, v);
+            for (int rr = 0; rr < 4; ++rr) st_f32(F + (size_t)(gi + rr) * ldf + gj, v[rr]);
+            if (mirror) st_f32x4(F + (size_t)gj * ldf + gi, v);
+          }
           if constexpr (!F32) {
             uint16_t* o0 = static_cast<uint16_t*>(G.out0);
             const int ld0 = G.ld0;
@@ -368,35 +404,27 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
               if (mirror)
                 st_u32x2(o0 + (size_t)gj * ld0 + gi, pack_bf16x4(v[0], v[1], v[2], v[3]));
             } else {
-              // L3 = [hi | hi | lo], R3 = [hi | lo | hi] along K (3P), so
-              // L3 R3^T = hi hi^T + hi lo^T + lo hi^T.
-              uint16_t* o1 = static_cast<uint16_t*>(G.out1);
-              const int ld1 = G.ld1;
-              f32x4 hi, lo;
+              // Rows [hi | lo | hi | hi] along K (4P).  The polynomial
+              // product pairs columns 0..3P (hi, lo, hi) with columns
+              // P..4P (lo, hi, hi): hi lo^T + lo hi^T + hi hi^T.
+              const u32x2 h4 = pack_bf16x4(v[0], v[1], v[2], v[3]);
+              const f32x4 hf = unpack_bf16x4(h4);
+              const u32x2 l4 =
+                  pack_bf16x4(v[0] - hf[0], v[1] - hf[1], v[2] - hf[2], v[3] - hf[3]);
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) {
-                hi[rr] = from_bf16(to_bf16(v[rr]));
-                lo[rr] = v[rr] - hi[rr];
-              }
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const size_t rL = (size_t)(gi + rr) * ld0 + gj;
-                const size_t rR = (size_t)(gi + rr) * ld1 + gj;
-                const uint16_t h = to_bf16(hi[rr]), l = to_bf16(lo[rr]);
-                st_u16(o0 + rL, h); st_u16(o0 + rL + P, h); st_u16(o0 + rL + 2 * P, l);
-                st_u16(o1 + rR, h); st_u16(o1 + rR + P, l); st_u16(o1 + rR + 2 * P, h);
+                const size_t o = (size_t)(gi + rr) * ld0 + gj;
+                const uint16_t h = (uint16_t)((rr & 1 ? h4[rr >> 1] >> 16 : h4[rr >> 1]) & 0xffffu);
+                const uint16_t l = (uint16_t)((rr & 1 ? l4[rr >> 1] >> 16 : l4[rr >> 1]) & 0xffffu);
+                st_u16(o0 + o, h); st_u16(o0 + o + P, l);
+                st_u16(o0 + o + 2 * P, h); st_u16(o0 + o + 3 * P, h);
               }
               if (mirror) {
-                const u32x2 h4 = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
-                const u32x2 l4 = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
-                const size_t mL = (size_t)gj * ld0 + gi;
-                const size_t mR = (size_t)gj * ld1 + gi;
-                st_u32x2(o0 + mL, h4);
-                st_u32x2(o0 + mL + P, h4);
-                st_u32x2(o0 + mL + 2 * P, l4);
-                st_u32x2(o1 + mR, h4);
-                st_u32x2(o1 + mR + P, l4);
-                st_u32x2(o1 + mR + 2 * P, h4);
+                const size_t o = (size_t)gj * ld0 + gi;
+                st_u32x2(o0 + o, h4);
+                st_u32x2(o0 + o + P, l4);
+                st_u32x2(o0 + o + 2 * P, h4);
+                st_u32x2(o0 + o + 3 * P, h4);
               }
             }
           }
@@ -444,14 +472,36 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
   }
 }
 
+// How bf16-operand tiles of size T keep the master X: as bf16 X plus its
+// bf16 remainder (T < 256: fewer bytes, and at several blocks per CU the
+// extra access instructions are hidden), or in fp32 next to the bf16 copy
+// (T = 256: one block per CU, where the epilogue is bound by the number of
+// memory instructions).  The host picks the same layout per tile size.
+template <int T>
+constexpr bool kHiLoMaster = T < 256;
+
+// The master X at (r, c): fp32, or xb + xlo (both bf16).
+template <bool F32, bool HL>
+__device__ __forceinline__ float load_master(const GemmTask& G, int r, int c) {
+  if constexpr (F32 || !HL) {
+    return ld_f32(G.fbuf + (size_t)r * G.ld_f + c);
+  } else {
+    const size_t o = (size_t)r * G.ld0 + c;
+    return from_bf16(ld_u16(static_cast<const uint16_t*>(G.out0) + o)) +
+           from_bf16(ld_u16(G.xlo + o));
+  }
+}
+
 // UPDX, not the last iteration: X <- s (a X + B X_raw) with s = 1/(||u||+eps)
-// on iteration 0.  Writes the fp32 master X, and either X^T in fp32 (fp32
-// operands) or the bf16 X plus X^T in bf16, the latter transposed through
-// LDS (8-byte groups XOR-swizzled) so that it leaves the tile as full rows.
+// on iteration 0.  Writes the master X (fp32, or bf16 X and its bf16
+// remainder), and X^T: in fp32 with fp32 operands, else in bf16 transposed
+// through LDS (8-byte groups XOR-swizzled) so that it leaves the tile as
+// full rows.
 template <int T, bool F32, int NT>
 __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
                                               int tn, int wr, int wc, int lane,
                                               const IterArgs& A, uint16_t* stage) {
+  constexpr bool HL = kHiLoMaster<T>;
   if constexpr (!F32) __syncthreads();  // main-loop LDS reads are done
   const int row_base = tm * T + wr + 4 * (lane >> 5);
   const int col_base = tn * T + wc + (lane & 31);
@@ -471,8 +521,8 @@ __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[N
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          xv[j][g][rr] =
-              ld_f32(X + (size_t)(row_base + i * 32 + 8 * g + rr) * ldf + col_base + j * 32);
+          xv[j][g][rr] = load_master<F32, HL>(G, row_base + i * 32 + 8 * g + rr,
+                                              col_base + j * 32);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads together (see sym_epilogue)
 #pragma unroll
     for (int j = 0; j < NT; ++j)
@@ -483,11 +533,13 @@ __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[N
         f32x4 v;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) v[rr] = s * fmaf(ca, xv[j][g][rr], acc[i][j][4 * g + rr]);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) st_f32(X + (size_t)(gi + rr) * ldf + gj, v[rr]);
         if constexpr (F32) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) st_f32(X + (size_t)(gi + rr) * ldf + gj, v[rr]);
           st_f32x4(static_cast<float*>(xt_next) + (size_t)gj * ld1 + gi, v);
-        } else {
+        } else if constexpr (!HL) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) st_f32(X + (size_t)(gi + rr) * ldf + gj, v[rr]);
           uint16_t* xb = static_cast<uint16_t*>(G.out0);
           const int ld0 = G.ld0;
 #pragma unroll
@@ -495,6 +547,21 @@ __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[N
           const int il = gi - tm * T, jl = gj - tn * T;
           const int x = 4 * (jl & (T / 4 - 1));
           *reinterpret_cast<u32x2*>(stage + jl * T + (il ^ x)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+        } else {
+          uint16_t* xb = static_cast<uint16_t*>(G.out0);
+          const int ld0 = G.ld0;
+          const u32x2 h4 = pack_bf16x4(v[0], v[1], v[2], v[3]);
+          const f32x4 hf = unpack_bf16x4(h4);
+          const u32x2 l4 = pack_bf16x4(v[0] - hf[0], v[1] - hf[1], v[2] - hf[2], v[3] - hf[3]);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const size_t o = (size_t)(gi + rr) * ld0 + gj;
+            st_u16(xb + o, (uint16_t)((rr & 1 ? h4[rr >> 1] >> 16 : h4[rr >> 1]) & 0xffffu));
+            st_u16(G.xlo + o, (uint16_t)((rr & 1 ? l4[rr >> 1] >> 16 : l4[rr >> 1]) & 0xffffu));
+          }
+          const int il = gi - tm * T, jl = gj - tn * T;
+          const int x = 4 * (jl & (T / 4 - 1));
+          *reinterpret_cast<u32x2*>(stage + jl * T + (il ^ x)) = h4;
         }
       }
   }
@@ -520,10 +587,9 @@ __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[N
 // (dtype DT: 0 fp32, 1 bf16), as p <- p*decay - lr*O (FIN_UPDATE) or as
 // O (FIN_OUTPUT).  Oriented element (r, c) lives at dst[r*qv + c], or at
 // dst[c*pv + r] for a transposed caller matrix.  Lanes on padding (outside
-// pv x qv) load dst element 0 and store into their own slot of the padded
-// X buffer, which this iteration no longer needs (the next call's input
-// pass rewrites it): every access is unconditional, so no branch separates
-// the loads from their uses.
+// pv x qv) load dst element 0 and store into the task's sink (workspace
+// bytes nothing reads): every access is unconditional, so no branch
+// separates the loads from their uses.
 template <int DT>
 __device__ __forceinline__ float dst_load(const void* dst, size_t i) {
   if constexpr (DT == 0) return ld_f32(static_cast<const float*>(dst) + i);
@@ -536,7 +602,7 @@ __device__ __forceinline__ void dst_store(void* p, float v) {
   else st_u16(static_cast<uint16_t*>(p), to_bf16(v));
 }
 
-template <int T, int NT, int DT>
+template <int T, bool F32, int NT, int DT>
 __device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
                                            int tn, int wr, int wc, int lane,
                                            const IterArgs& A) {
@@ -544,8 +610,6 @@ __device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][
   const int col_base = tn * T + wc + (lane & 31);
   const float s = A.iter == 0 ? G.scale[0] : 1.f;
   const float ca = A.a;
-  float* X = G.fbuf;
-  const int ldf = G.ld_f;
   void* dst = G.dst;
   constexpr int ESZ = DT == 0 ? 4 : 2;
   const int pv = G.pv, qv = G.qv;
@@ -563,8 +627,8 @@ __device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          xv[j][g][rr] =
-              ld_f32(X + (size_t)(row_base + i * 32 + 8 * g + rr) * ldf + col_base + j * 32);
+          xv[j][g][rr] = load_master<F32, kHiLoMaster<T>>(G, row_base + i * 32 + 8 * g + rr,
+                                                          col_base + j * 32);
     if (upd) {
 #pragma unroll
       for (int j = 0; j < NT; ++j)
@@ -587,9 +651,8 @@ __device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][
           const int r = row_base + i * 32 + 8 * g + rr, c = col_base + j * 32;
           float o = s * fmaf(ca, xv[j][g][rr], acc[i][j][4 * g + rr]);
           if (upd) o = fmaf(-A.lr, o, pv4[j][g][rr] * A.decay);
-          char* to = (r < pv && c < qv)
-                         ? static_cast<char*>(dst) + (r * rs + c * cs) * ESZ
-                         : reinterpret_cast<char*>(X + (size_t)r * ldf + c);
+          char* to = (r < pv && c < qv) ? static_cast<char*>(dst) + (r * rs + c * cs) * ESZ
+                                        : static_cast<char*>(G.sink);
           dst_store<DT>(to, o);
         }
   }
@@ -604,11 +667,16 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
     if (A.fin == FIN_NONE)
       updx_epilogue<T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A, stage);
     else if (G.dst_dtype == 0)
-      updx_final<T, NT, 0>(G, acc, tm, tn, wr, wc, lane, A);
+      updx_final<T, F32, NT, 0>(G, acc, tm, tn, wr, wc, lane, A);
     else
-      updx_final<T, NT, 1>(G, acc, tm, tn, wr, wc, lane, A);
+      updx_final<T, F32, NT, 1>(G, acc, tm, tn, wr, wc, lane, A);
+  } else if constexpr (KIND == KIND_POLY && !F32) {
+    if (G.ahl)
+      sym_epilogue<KIND, T, F32, NT, true>(G, acc, tm, tn, wr, wc, lane, A);
+    else
+      sym_epilogue<KIND, T, F32, NT, false>(G, acc, tm, tn, wr, wc, lane, A);
   } else {
-    sym_epilogue<KIND, T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A);
+    sym_epilogue<KIND, T, F32, NT, false>(G, acc, tm, tn, wr, wc, lane, A);
   }
 }
 

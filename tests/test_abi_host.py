@@ -73,9 +73,12 @@ def _tile(p, prec):
 
 
 def _expected_ws(shapes, prec):
-    """Workspace rule: partials + scales, then per matrix X master, bf16 X,
-    two X^T buffers, fp32 A and the operand copies of A and B, each rounded
-    to 256 bytes, rows padded to odd multiples of 256 bytes."""
+    """Workspace rule: partials, scales and a 16-byte sink, then per matrix
+    the master X (fp32 X, plus bf16 X for bf16 operands; or, below 256-tiles,
+    bf16 X plus its bf16 remainder), two X^T
+    buffers, fp32 A (unless A is split), the operand forms of A ([hi|lo|hi|hi]
+    rows when split) and B ([hi|lo] when split); each region rounded to 256
+    bytes, rows padded to odd multiples of 256 bytes."""
     a = lambda x: _pad(x, 256)  # noqa: E731
     tiles = 0
     per = []
@@ -90,13 +93,15 @@ def _expected_ws(shapes, prec):
             per.append(a(4 * P * _ld(Q, 4)) + 2 * a(4 * Q * _ld(P, 4)) + a(4 * P * _ld(P, 4))
                        + a(4 * P * _ld(P, 4)))
         else:
-            base = a(4 * P * _ld(Q, 4)) + a(2 * P * _ld(Q, 2)) + 2 * a(2 * Q * _ld(P, 2)) \
-                + a(4 * P * _ld(P, 4))
-            aop = a(2 * P * _ld(3 * P if split_a else P, 2))
-            base += aop * (2 if split_a else 1)
+            hilo = t < 256  # master X: bf16 + bf16 remainder below 256-tiles, else fp32
+            base = a(2 * P * _ld(Q, 2)) + 2 * a(2 * Q * _ld(P, 2))
+            base += a(2 * P * _ld(Q, 2)) if hilo else a(4 * P * _ld(Q, 4))
+            if not split_a:
+                base += a(4 * P * _ld(P, 4))
+            base += a(2 * P * _ld(4 * P if split_a else P, 2))
             base += a(2 * P * _ld(2 * P if split_b else P, 2))
             per.append(base)
-    return a(4 * tiles) + a(16 * len(shapes)) + sum(per)
+    return a(4 * tiles) + a(16 * len(shapes)) + a(16) + sum(per)
 
 
 @pytest.mark.parametrize("prec", ["f32", "bf16", "bf16_split", "auto", "bf16_split_a"])
