@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the per-owner Muon step (test infrastructure only).
+"""fp64 CPU oracle for the per-owner Muon step and its element-wise companions
+(gradient clipping, AdamW) -- test infrastructure only.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP product path
@@ -19,4 +20,11 @@ from .muon_ref import (  # noqa: F401
     direct_newton_schulz,
     muon_step,
     round_to_bf16,
+)
+from .optim_ref import (  # noqa: F401
+    CLIP_EPS,
+    ADAMW_DEFAULTS,
+    total_norm,
+    clip_grad_norm,
+    adamw_step,
 )
