@@ -151,6 +151,75 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params,
                                int32_t nesterov,
                                void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Gradient-norm clipping of Muon gradients (DMuon "API Reference",
+ * clip_grad_norm_: only DMuon's Muon gradients, norm_type 2.0 by default,
+ * the stats of MuonGradClipStats; clip_grad_norm_buckets_: every bucket
+ * keeps its own norm and coefficient).  Per bucket b:
+ *   total = (sum over its gradients of |g|^p)^(1/p)   (p = +inf: max |g|;
+ *           a NaN anywhere gives NaN)
+ *   coef  = max_norm / (total + 1e-6)
+ *   g    <- g * min(coef, 1)   (every element; bf16 rounded to nearest even;
+ *           a NaN coef makes the bucket NaN, as multiplying by it does)
+ *   grads       F32 or BF16 tensors (m x n, row-major), updated in place.
+ *   bucket_of   host array, bucket of each gradient, values in
+ *               [0, nbuckets); NULL means every gradient is in bucket 0
+ *               (then nbuckets must be 1).
+ *   max_norm    finite, >= 0; ignored when stats_only != 0, in which case
+ *               nothing is scaled and coef is reported as 1.
+ *   norm_type   p > 0, or +inf.
+ *   stats       device array of nbuckets entries (8-byte aligned), written
+ *               on the stream; read it after the stream has reached this
+ *               point.
+ *   ws          device workspace of dmuon_clip_workspace_size bytes,
+ *               256-byte aligned; contents on entry are ignored.
+ * Distributed reduction of the per-rank norms is outside this one-GPU call.
+ * Errors: as dmuon_muon_step (nothing is enqueued when validation fails).
+ */
+typedef struct {
+  double total_norm;    /* bucket norm before clipping */
+  double clip_coef;     /* max_norm / (total_norm + 1e-6); 1 for stats only */
+  int32_t clipped;      /* clip_coef < 1 */
+  int32_t found_inf;    /* total_norm is not finite */
+  int64_t param_count;  /* elements in the bucket */
+} dmuon_clip_stats_t;
+
+dmuon_status_t dmuon_clip_workspace_size(const dmuon_batch_t* grads,
+                                         int32_t nbuckets, size_t* bytes);
+
+dmuon_status_t dmuon_clip_grad_norm(const dmuon_batch_t* grads,
+                                    const int32_t* bucket_of, int32_t nbuckets,
+                                    double max_norm, int32_t stats_only,
+                                    double norm_type,
+                                    dmuon_clip_stats_t* stats,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * AdamW update of the parameters Muon does not own (DMuon "API Reference",
+ * Muon: step runs AdamW on them; the signature's adamw_lr=1e-3,
+ * adamw_betas=(0.9, 0.999), adamw_weight_decay=0.01, adamw_eps=1e-8 are
+ * the Python binding's defaults).  Decoupled weight decay, t = step:
+ *   p <- p * (1 - lr * weight_decay)
+ *   m <- beta1 * m + (1 - beta1) * g
+ *   v <- beta2 * v + (1 - beta2) * g^2
+ *   p <- p - lr / (1 - beta1^t) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ *   params      F32 or BF16, updated in place (bf16 rounded to nearest even).
+ *   grads       F32 or BF16, read only.
+ *   exp_avg, exp_avg_sq   F32 moments, updated in place.
+ * Same count and per-index shapes in the four batches, no overlaps; step
+ * >= 1 (the count after this update); betas in [0, 1), eps > 0.  The
+ * hyperparameters are doubles: 1 - beta and the bias corrections are formed
+ * in double before the kernels get their fp32 factors (1 - beta from an
+ * fp32 beta2 = 0.999 would be 1.3e-5 off).  No workspace.  Errors: as
+ * dmuon_muon_step.
+ */
+dmuon_status_t dmuon_adamw_step(const dmuon_batch_t* params,
+                                const dmuon_batch_t* grads,
+                                const dmuon_batch_t* exp_avg,
+                                const dmuon_batch_t* exp_avg_sq,
+                                int64_t step, double lr, double beta1, double beta2,
+                                double eps, double weight_decay, void* stream);
+
 /* Static string for a status code. */
 const char* dmuon_status_str(dmuon_status_t status);
 
@@ -175,9 +244,10 @@ const char* dmuon_backend_info(void);
  * bytes of each launch with every operand read once and every output
  * written once in the library's workspace layout (for the element-wise
  * kernels, the bytes the step must move at minimum).
- * Kinds: 0 momentum, 1 input, 2 norm, 3 syrk, 4 poly, 5 update_x.  The
- * last update_x launch of a call also applies the parameter update (or
- * writes the NS output), so there is no separate update kind.
+ * Kinds: 0 momentum, 1 input, 2 norm, 3 syrk, 4 poly, 5 update_x,
+ * 6 clip_norm, 7 clip_scale, 8 adamw.  The last update_x launch of a call
+ * also applies the parameter update (or writes the NS output), so there is
+ * no separate update kind.
  */
 typedef struct {
   char name[24];

@@ -50,7 +50,14 @@ class ProfileRow(ctypes.Structure):
                 ("ms", ctypes.c_double), ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
 
 
+class ClipStats(ctypes.Structure):
+    _fields_ = [("total_norm", ctypes.c_double), ("clip_coef", ctypes.c_double),
+                ("clipped", ctypes.c_int32), ("found_inf", ctypes.c_int32),
+                ("param_count", ctypes.c_int64)]
+
+
 EXPORTS = ("dmuon_ns_workspace_size", "dmuon_ns_orthogonalize", "dmuon_muon_step",
+           "dmuon_clip_workspace_size", "dmuon_clip_grad_norm", "dmuon_adamw_step",
            "dmuon_status_str", "dmuon_last_error", "dmuon_backend_info",
            "dmuon_profile_begin", "dmuon_profile_end")
 
@@ -80,6 +87,18 @@ def lib():
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p]
     L.dmuon_muon_step.restype = st
+    L.dmuon_clip_workspace_size.argtypes = [ctypes.POINTER(Batch), ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_size_t)]
+    L.dmuon_clip_workspace_size.restype = st
+    L.dmuon_clip_grad_norm.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.c_int32, ctypes.c_double, ctypes.c_int32,
+                                       ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p]
+    L.dmuon_clip_grad_norm.restype = st
+    L.dmuon_adamw_step.argtypes = [ctypes.POINTER(Batch)] * 4 + [
+        ctypes.c_int64, ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+        ctypes.c_double, ctypes.c_void_p]
+    L.dmuon_adamw_step.restype = st
     L.dmuon_status_str.argtypes = [ctypes.c_int]
     L.dmuon_status_str.restype = ctypes.c_char_p
     L.dmuon_last_error.argtypes = []
@@ -131,6 +150,28 @@ def make_batch(tensors):
         elif c != code:
             raise DmuonValueError(DMUON_E_INVALID, "a batch holds one dtype")
         arr[i] = Mat(int(t.shape[0]), int(t.shape[1]), int(t.data_ptr()))
+    return Batch(arr, len(tensors), code), arr
+
+
+def make_flat_batch(tensors):
+    """Batch descriptor for the element-wise entry points: any contiguous
+    device tensor, described as (first dim) x (the rest), or 1 x n for a
+    vector.  Returns (Batch, keepalive)."""
+    tensors = list(tensors)
+    arr = (Mat * max(1, len(tensors)))()
+    code = DMUON_F32
+    for i, t in enumerate(tensors):
+        if not t.is_contiguous():
+            raise DmuonValueError(DMUON_E_INVALID, "every tensor must be contiguous")
+        c = _dtype_code(t)
+        if i == 0:
+            code = c
+        elif c != code:
+            raise DmuonValueError(DMUON_E_INVALID, "a batch holds one dtype")
+        if t.dim() == 0 or t.numel() == 0:
+            raise DmuonValueError(DMUON_E_INVALID, "empty tensors are not supported")
+        m = int(t.shape[0]) if t.dim() > 1 else 1
+        arr[i] = Mat(m, int(t.numel()) // m, int(t.data_ptr()))
     return Batch(arr, len(tensors), code), arr
 
 
@@ -227,7 +268,8 @@ def muon_step(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_decay=0.0, 
                                  _stream_handle(stream)))
 
 
-KINDS = ("momentum", "input", "norm", "syrk", "poly", "update_x")
+KINDS = ("momentum", "input", "norm", "syrk", "poly", "update_x", "clip_norm", "clip_scale",
+         "adamw")
 
 
 class profile:
@@ -304,3 +346,103 @@ class PreparedNs:
                      self.wptr, self.wbytes, self.stream)
         if st:
             _check(st)
+
+
+# ------------------------------------------------- element-wise companions --
+
+def clip_workspace_size(shapes, nbuckets=1) -> int:
+    """dmuon_clip_workspace_size for gradients of these (m, n) shapes."""
+    b, keep = shape_batch(shapes)
+    out = ctypes.c_size_t(0)
+    _check(lib().dmuon_clip_workspace_size(ctypes.byref(b), int(nbuckets), ctypes.byref(out)))
+    return int(out.value)
+
+
+class PreparedClip:
+    """dmuon_clip_grad_norm with the descriptors marshalled once.  Calling it
+    enqueues the clipping on the stream; ``stats()`` waits for the stream and
+    returns one dict per bucket (total_norm, clip_coef, clipped, found_inf,
+    param_count)."""
+
+    def __init__(self, grads, max_norm, *, norm_type=2.0, buckets=None, stream=None):
+        import torch
+        grads = list(grads)
+        self.bg, self._kg = make_flat_batch(grads)
+        self.nb = 1 if buckets is None else max(buckets) + 1
+        self._bk = None
+        bptr = None
+        if buckets is not None:
+            if len(buckets) != len(grads):
+                raise DmuonValueError(DMUON_E_INVALID, "one bucket index per gradient")
+            self._bk = (ctypes.c_int32 * len(buckets))(*[int(b) for b in buckets])
+            bptr = ctypes.cast(self._bk, ctypes.POINTER(ctypes.c_int32))
+        self.bptr = bptr
+        self.stats_only = max_norm is None
+        self.max_norm = 0.0 if max_norm is None else float(max_norm)
+        self.norm_type = float(norm_type)
+        device = grads[0].device if grads else "cuda"
+        shapes = [(self.bg.mats[i].m, self.bg.mats[i].n) for i in range(len(grads))]
+        self.ws = torch.empty(max(1, clip_workspace_size(shapes, self.nb)), dtype=torch.uint8,
+                              device=device)
+        self.dev_stats = torch.empty(ctypes.sizeof(ClipStats) * self.nb, dtype=torch.uint8,
+                                     device=device)
+        self.stream = _stream_handle(stream)
+        self.fn = lib().dmuon_clip_grad_norm
+
+    def __call__(self):
+        st = self.fn(ctypes.byref(self.bg), self.bptr, self.nb, self.max_norm,
+                     int(self.stats_only), self.norm_type, int(self.dev_stats.data_ptr()),
+                     int(self.ws.data_ptr()), int(self.ws.numel()), self.stream)
+        if st:
+            _check(st)
+
+    def stats(self):
+        raw = bytes(self.dev_stats.cpu().numpy())
+        out = []
+        for b in range(self.nb):
+            r = ClipStats.from_buffer_copy(raw, b * ctypes.sizeof(ClipStats))
+            out.append(dict(total_norm=r.total_norm, clip_coef=r.clip_coef,
+                            clipped=bool(r.clipped), found_inf=bool(r.found_inf),
+                            param_count=int(r.param_count)))
+        return out
+
+
+def clip_grad_norm(grads, max_norm, *, norm_type=2.0, buckets=None, stream=None):
+    """dmuon_clip_grad_norm on `grads` (in place); returns the per-bucket
+    stats (waits for the stream).  ``max_norm=None`` only measures."""
+    c = PreparedClip(grads, max_norm, norm_type=norm_type, buckets=buckets, stream=stream)
+    c()
+    return c.stats()
+
+
+ADAMW_DEFAULTS = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+
+
+class PreparedAdamW:
+    """dmuon_adamw_step with the descriptors marshalled once; ``__call__(step)``
+    enqueues one update with the given 1-based step count."""
+
+    def __init__(self, params, grads, exp_avg, exp_avg_sq, *, lr=1e-3, betas=(0.9, 0.999),
+                 eps=1e-8, weight_decay=0.01, stream=None):
+        self._k = []
+        self.b = []
+        for ts in (params, grads, exp_avg, exp_avg_sq):
+            b, k = make_flat_batch(ts)
+            self.b.append(b)
+            self._k.append(k)
+        self.hp = (float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay))
+        self.stream = _stream_handle(stream)
+        self.fn = lib().dmuon_adamw_step
+
+    def __call__(self, step):
+        st = self.fn(*[ctypes.byref(b) for b in self.b], int(step), *self.hp, self.stream)
+        if st:
+            _check(st)
+
+
+def adamw_step(params, grads, exp_avg, exp_avg_sq, step, *, lr=1e-3, betas=(0.9, 0.999),
+               eps=1e-8, weight_decay=0.01, stream=None):
+    """dmuon_adamw_step: in-place AdamW update of `params`, `exp_avg` and
+    `exp_avg_sq` (defaults as in the adamw_* arguments of DMuon's Muon)."""
+    PreparedAdamW(params, grads, exp_avg, exp_avg_sq, lr=lr, betas=betas, eps=eps,
+                  weight_decay=weight_decay, stream=stream)(step)

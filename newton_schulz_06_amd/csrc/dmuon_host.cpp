@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstdio>
 #include <cstring>
 #include <memory>
@@ -534,7 +535,8 @@ struct Prof {
 };
 thread_local Prof g_prof;
 
-const char* kKindNames[KIND_COUNT] = {"momentum", "input", "norm", "syrk", "poly", "update_x"};
+const char* kKindNames[KIND_COUNT] = {"momentum", "input", "norm", "syrk", "poly",
+                                      "update_x", "clip_norm", "clip_scale", "adamw"};
 
 template <class F>
 hipError_t timed(int kind, double flops, double bytes, hipStream_t s, F&& launch) {
@@ -605,7 +607,105 @@ dmuon_status_t check_ws(const Layout& L, void* ws, size_t ws_bytes) {
   return DMUON_OK;
 }
 
+// ------------------------------------------------------- flat launches --
+// Task tables of the element-wise companions (clipping, AdamW), cached per
+// call signature like the NS plans.
+struct FlatPlan {
+  std::vector<int64_t> key;
+  int device = -1;
+  void* dtab = nullptr;
+  int ntasks = 0, nblocks = 0;
+  ~FlatPlan() {
+    if (dtab) {
+      int cur = -1;
+      (void)hipGetDevice(&cur);
+      (void)hipSetDevice(device);
+      (void)hipDeviceSynchronize();
+      (void)hipFree(dtab);
+      (void)hipSetDevice(cur);
+    }
+  }
+};
+std::vector<std::unique_ptr<FlatPlan>>& g_flat = *new std::vector<std::unique_ptr<FlatPlan>>();
+
+int64_t numel(const dmuon_mat_t& M) { return M.m * M.n; }
+
+// Chunk counts per tensor; fails when the launch would not fit int32.
+dmuon_status_t flat_blocks(const dmuon_batch_t* b, std::vector<FlatTask>* tasks, int* nblocks) {
+  int64_t blk = 0;
+  tasks->assign(b->count, FlatTask{});
+  for (int i = 0; i < b->count; ++i) {
+    FlatTask& t = (*tasks)[i];
+    t.n = numel(b->mats[i]);
+    const int64_t nb = (t.n + FLAT_CHUNK - 1) / FLAT_CHUNK;
+    t.blk_begin = (int32_t)blk;
+    t.nblk = (int32_t)nb;
+    blk += nb;
+    if (blk > INT32_MAX) return fail(DMUON_E_UNSUPPORTED, "batch too large (block count)");
+  }
+  *nblocks = (int)blk;
+  return DMUON_OK;
+}
+
+// Looks up (or uploads) the task table for `tasks`; caller holds g_plan_mu.
+dmuon_status_t get_flat_plan(const std::vector<FlatTask>& tasks, int nblocks, int64_t op,
+                             FlatPlan** out) {
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::vector<int64_t> key;
+  key.reserve(2 + 8 * tasks.size());
+  key.push_back(op);
+  key.push_back(device);
+  for (const FlatTask& t : tasks) {
+    key.push_back(t.n);
+    key.push_back(t.bucket);
+    key.push_back(t.dtype + 4 * t.gdtype + 16 * t.vec);
+    key.push_back((int64_t)reinterpret_cast<uintptr_t>(t.p));
+    key.push_back((int64_t)reinterpret_cast<uintptr_t>(t.g));
+    key.push_back((int64_t)reinterpret_cast<uintptr_t>(t.m));
+    key.push_back((int64_t)reinterpret_cast<uintptr_t>(t.v));
+  }
+  for (size_t k = 0; k < g_flat.size(); ++k) {
+    if (g_flat[k]->key == key) {
+      std::unique_ptr<FlatPlan> hit = std::move(g_flat[k]);
+      g_flat.erase(g_flat.begin() + (long)k);
+      g_flat.push_back(std::move(hit));
+      *out = g_flat.back().get();
+      return DMUON_OK;
+    }
+  }
+  auto plan = std::make_unique<FlatPlan>();
+  plan->key = std::move(key);
+  plan->device = device;
+  plan->ntasks = (int)tasks.size();
+  plan->nblocks = nblocks;
+  const size_t bytes = sizeof(FlatTask) * tasks.size();
+  e = hipMalloc(&plan->dtab, bytes);
+  if (e != hipSuccess) {
+    plan->dtab = nullptr;
+    return fail(DMUON_E_HIP, std::string("hipMalloc(task table): ") + hipGetErrorString(e));
+  }
+  e = hipMemcpy(plan->dtab, tasks.data(), bytes, hipMemcpyHostToDevice);
+  if (e != hipSuccess)
+    return fail(DMUON_E_HIP, std::string("hipMemcpy(task table): ") + hipGetErrorString(e));
+  if (g_flat.size() >= kMaxPlans) g_flat.erase(g_flat.begin());
+  g_flat.push_back(std::move(plan));
+  *out = g_flat.back().get();
+  return DMUON_OK;
+}
+
+// Clipping workspace: per-block partials, then one factor per bucket.
+size_t clip_ws_bytes(int nblocks, int nbuckets) {
+  return align_up(sizeof(float) * (size_t)nblocks, kWsAlign) +
+         align_up(sizeof(float) * (size_t)nbuckets, kWsAlign);
+}
+
 }  // namespace
+
+static_assert(sizeof(dmuon_clip_stats_t) == sizeof(dmuon::ClipStats), "clip stats layout");
+static_assert(offsetof(dmuon_clip_stats_t, param_count) == offsetof(dmuon::ClipStats, param_count),
+              "clip stats layout");
 
 // ================================================================== C ABI ==
 
@@ -696,6 +796,174 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t*
   if ((st = get_plan(L, grads, params, bufs, false, static_cast<char*>(ws), &plan))) return st;
   return run(*plan, cfg, false, momentum, nesterov ? 1 : 0, lr, decay,
              static_cast<hipStream_t>(stream));
+}
+
+dmuon_status_t dmuon_clip_workspace_size(const dmuon_batch_t* grads, int32_t nbuckets,
+                                         size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DMUON_E_INVALID, "bytes: null");
+  dmuon_status_t st = check_batch(grads, "grads", false);
+  if (st) return st;
+  if (nbuckets < 1) return fail(DMUON_E_INVALID, "nbuckets must be >= 1");
+  std::vector<FlatTask> tasks;
+  int nblocks = 0;
+  if ((st = flat_blocks(grads, &tasks, &nblocks))) return st;
+  *bytes = grads->count ? clip_ws_bytes(nblocks, nbuckets) : 0;
+  return DMUON_OK;
+}
+
+dmuon_status_t dmuon_clip_grad_norm(const dmuon_batch_t* grads, const int32_t* bucket_of,
+                                    int32_t nbuckets, double max_norm, int32_t stats_only,
+                                    double norm_type, dmuon_clip_stats_t* stats, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  dmuon_status_t st = check_batch(grads, "grads", true);
+  if (st) return st;
+  if (nbuckets < 1) return fail(DMUON_E_INVALID, "nbuckets must be >= 1");
+  if (!bucket_of && nbuckets != 1)
+    return fail(DMUON_E_INVALID, "bucket_of may be null only with one bucket");
+  if (!(norm_type > 0.0)) return fail(DMUON_E_INVALID, "norm_type must be > 0 (or +inf)");
+  if (!stats_only && !(std::isfinite(max_norm) && max_norm >= 0.0))
+    return fail(DMUON_E_INVALID, "max_norm must be finite and >= 0");
+  if (!stats) return fail(DMUON_E_INVALID, "stats: null");
+  if (reinterpret_cast<uintptr_t>(stats) % 8) return fail(DMUON_E_INVALID, "stats: not 8-byte aligned");
+  std::vector<int> used(nbuckets, 0);
+  for (int i = 0; i < grads->count; ++i) {
+    const int b = bucket_of ? bucket_of[i] : 0;
+    if (b < 0 || b >= nbuckets)
+      return fail(DMUON_E_INVALID, "bucket_of[" + std::to_string(i) + "] out of range");
+    used[b] = 1;
+  }
+  std::vector<FlatTask> tasks;
+  int nblocks = 0;
+  if ((st = flat_blocks(grads, &tasks, &nblocks))) return st;
+  const size_t need = grads->count ? clip_ws_bytes(nblocks, nbuckets) : 0;
+  if (need) {
+    if (!ws) return fail(DMUON_E_WORKSPACE, "workspace: null pointer");
+    if (reinterpret_cast<uintptr_t>(ws) % kWsAlign)
+      return fail(DMUON_E_WORKSPACE, "workspace: pointer not 256-byte aligned");
+    if (ws_bytes < need)
+      return fail(DMUON_E_WORKSPACE, "workspace: " + std::to_string(ws_bytes) + " bytes given, " +
+                                         std::to_string(need) + " needed");
+  }
+  std::vector<Span> spans;
+  add_spans(spans, grads, 0);
+  if (need) {
+    const uintptr_t wlo = reinterpret_cast<uintptr_t>(ws);
+    spans.push_back({wlo, wlo + need, 1, 0});
+  }
+  const uintptr_t slo = reinterpret_cast<uintptr_t>(stats);
+  spans.push_back({slo, slo + sizeof(dmuon_clip_stats_t) * (size_t)nbuckets, 2, 0});
+  static const char* const names[] = {"grads", "ws", "stats"};
+  if ((st = check_disjoint(spans, names))) return st;
+
+  for (int i = 0; i < grads->count; ++i) {
+    FlatTask& t = tasks[i];
+    t.bucket = bucket_of ? bucket_of[i] : 0;
+    t.dtype = grads->dtype;
+    t.p = grads->mats[i].ptr;
+    t.vec = vec_ok(t.p, grads->dtype, 4);
+  }
+  const int mode = std::isinf(norm_type) ? NORM_INF
+                   : norm_type == 2.0    ? NORM_L2
+                   : norm_type == 1.0    ? NORM_L1
+                                         : NORM_P;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  FlatPlan* plan = nullptr;
+  if (grads->count && (st = get_flat_plan(tasks, nblocks, 1, &plan))) return st;
+  const FlatTask* dt = plan ? static_cast<const FlatTask*>(plan->dtab) : nullptr;
+  float* partial = static_cast<float*>(ws);
+  float* scale = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                          align_up(sizeof(float) * (size_t)nblocks, kWsAlign));
+  double bytes = 0;
+  for (int i = 0; i < grads->count; ++i) bytes += (double)tasks[i].n * esize(grads->dtype);
+  auto check = [](hipError_t e, const char* what) -> dmuon_status_t {
+    if (e == hipSuccess) return DMUON_OK;
+    return fail(DMUON_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  };
+  st = check(timed(KIND_CLIP_NORM, 0, bytes, s,
+                   [&] {
+                     hipError_t e = hipSuccess;
+                     if (nblocks)
+                       e = launch_clip_norm(dt, plan->ntasks, nblocks, mode, (float)norm_type,
+                                            partial, s);
+                     if (e != hipSuccess) return e;
+                     return launch_clip_finalize(dt, grads->count, nbuckets, mode, norm_type,
+                                                 max_norm, stats_only ? 1 : 0, partial,
+                                                 reinterpret_cast<ClipStats*>(stats), scale, s);
+                   }),
+             "clip norm launch");
+  if (st || stats_only || nblocks == 0) return st;
+  return check(timed(KIND_CLIP_SCALE, 0, 2.0 * bytes, s,
+                     [&] { return launch_clip_scale(dt, plan->ntasks, nblocks, scale, s); }),
+               "clip scale launch");
+}
+
+dmuon_status_t dmuon_adamw_step(const dmuon_batch_t* params, const dmuon_batch_t* grads,
+                                const dmuon_batch_t* exp_avg, const dmuon_batch_t* exp_avg_sq,
+                                int64_t step, double lr, double beta1, double beta2,
+                                double eps, double weight_decay, void* stream) {
+  g_last_error.clear();
+  dmuon_status_t st = check_batch(params, "params", true);
+  if (st) return st;
+  if ((st = check_batch(grads, "grads", true))) return st;
+  if ((st = check_batch(exp_avg, "exp_avg", true))) return st;
+  if ((st = check_batch(exp_avg_sq, "exp_avg_sq", true))) return st;
+  if ((st = same_shapes(params, grads, "params", "grads"))) return st;
+  if ((st = same_shapes(params, exp_avg, "params", "exp_avg"))) return st;
+  if ((st = same_shapes(params, exp_avg_sq, "params", "exp_avg_sq"))) return st;
+  if (exp_avg->dtype != DMUON_F32 || exp_avg_sq->dtype != DMUON_F32)
+    return fail(DMUON_E_INVALID, "exp_avg and exp_avg_sq must be F32");
+  if (step < 1) return fail(DMUON_E_INVALID, "step counts from 1");
+  if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(weight_decay) ||
+      !(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps > 0.0))
+    return fail(DMUON_E_INVALID, "need finite lr and weight_decay, betas in [0, 1), eps > 0");
+  if (params->count == 0) return DMUON_OK;
+  std::vector<Span> spans;
+  add_spans(spans, params, 0);
+  add_spans(spans, grads, 1);
+  add_spans(spans, exp_avg, 2);
+  add_spans(spans, exp_avg_sq, 3);
+  static const char* const names[] = {"params", "grads", "exp_avg", "exp_avg_sq"};
+  if ((st = check_disjoint(spans, names))) return st;
+  std::vector<FlatTask> tasks;
+  int nblocks = 0;
+  if ((st = flat_blocks(params, &tasks, &nblocks))) return st;
+  double bytes = 0;
+  for (int i = 0; i < params->count; ++i) {
+    FlatTask& t = tasks[i];
+    t.dtype = params->dtype;
+    t.gdtype = grads->dtype;
+    t.p = params->mats[i].ptr;
+    t.g = grads->mats[i].ptr;
+    t.m = static_cast<float*>(exp_avg->mats[i].ptr);
+    t.v = static_cast<float*>(exp_avg_sq->mats[i].ptr);
+    t.vec = vec_ok(t.p, params->dtype, 4) && vec_ok(t.g, grads->dtype, 4) &&
+            vec_ok(t.m, DMUON_F32, 4) && vec_ok(t.v, DMUON_F32, 4);
+    bytes += (double)t.n * (2.0 * esize(params->dtype) + esize(grads->dtype) + 16.0);
+  }
+  // Bias corrections in double, handed to the kernel as fp32 factors.
+  AdamArgs a;
+  a.decay = (float)(1.0 - lr * weight_decay);
+  a.beta1 = (float)beta1;
+  a.one_minus_beta1 = (float)(1.0 - beta1);
+  a.beta2 = (float)beta2;
+  a.one_minus_beta2 = (float)(1.0 - beta2);
+  const double bc1 = 1.0 - std::pow(beta1, (double)step);
+  const double bc2 = 1.0 - std::pow(beta2, (double)step);
+  a.step_size = (float)(lr / bc1);
+  a.inv_bc2_sqrt = (float)(1.0 / std::sqrt(bc2));
+  a.eps = (float)eps;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  FlatPlan* plan = nullptr;
+  if ((st = get_flat_plan(tasks, nblocks, 2, &plan))) return st;
+  const hipError_t e = timed(KIND_ADAMW, 0, bytes, s, [&] {
+    return launch_adamw(static_cast<const FlatTask*>(plan->dtab), plan->ntasks, nblocks, a, s);
+  });
+  if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("adamw launch: ") + hipGetErrorString(e));
+  return DMUON_OK;
 }
 
 const char* dmuon_status_str(dmuon_status_t s) {

@@ -18,6 +18,9 @@ enum Kind : int {
   KIND_UPDX,          // X <- a X + B X; on the last iteration the result
                       // goes straight to the caller: p <- p (1 - lr wd) - lr O
                       // (step) or out <- O (NS only)
+  KIND_CLIP_NORM,     // gradient clipping: norm partials + per-bucket finalize
+  KIND_CLIP_SCALE,    // gradient clipping: g <- g * factor
+  KIND_ADAMW,         // AdamW update of non-Muon parameters
   KIND_COUNT
 };
 
@@ -106,6 +109,63 @@ struct NormTask {
   const float* partial;
   float* scale;
 };
+
+// ---------------------------------------------------------------------------
+// Flat element-wise launches (gradient clipping, AdamW): every tensor is
+// cut into chunks of FLAT_CHUNK elements, one block per chunk.
+constexpr int FLAT_THREADS = 256;
+constexpr int FLAT_CHUNK = FLAT_THREADS * 16;
+
+struct FlatTask {
+  int64_t n;               // elements of the tensor
+  int32_t blk_begin;       // first block (chunk) of this tensor
+  int32_t nblk;            // blocks of this tensor
+  int32_t bucket;          // clipping: bucket index
+  int32_t dtype;           // dtype of `p` (0 fp32, 1 bf16)
+  int32_t gdtype;          // AdamW: dtype of `g`
+  int32_t vec;             // every pointer allows 4-element vector access
+  void* p;                 // clipping: the gradient; AdamW: the parameter
+  const void* g;           // AdamW: the gradient
+  float* m;                // AdamW: first moment
+  float* v;                // AdamW: second moment
+};
+
+// How the clipping norm is formed: sum of squares, sum of magnitudes, max
+// magnitude, or sum of |g|^p.
+enum NormMode : int32_t { NORM_L2 = 0, NORM_L1 = 1, NORM_INF = 2, NORM_P = 3 };
+
+// Per-bucket result of the clipping finalize, in the caller's layout (the
+// public dmuon_clip_stats_t).
+struct ClipStats {
+  double total_norm;
+  double clip_coef;
+  int32_t clipped;
+  int32_t found_inf;
+  int64_t param_count;
+};
+
+// Scalars of one AdamW launch, derived on the host from (lr, betas, eps,
+// weight decay, step).
+struct AdamArgs {
+  float decay;             // 1 - lr * weight_decay
+  float beta1, one_minus_beta1;
+  float beta2, one_minus_beta2;
+  float step_size;         // lr / (1 - beta1^t)
+  float inv_bc2_sqrt;      // 1 / sqrt(1 - beta2^t)
+  float eps;
+};
+
+// Launch helpers implemented in dmuon_optim.hip.
+hipError_t launch_clip_norm(const FlatTask* tasks, int ntasks, int total_blocks, int mode,
+                            float p, float* partial, hipStream_t s);
+hipError_t launch_clip_finalize(const FlatTask* tasks, int ntasks, int nbuckets, int mode,
+                                double p, double max_norm, int stats_only,
+                                const float* partial, ClipStats* stats, float* scale,
+                                hipStream_t s);
+hipError_t launch_clip_scale(const FlatTask* tasks, int ntasks, int total_blocks,
+                             const float* scale, hipStream_t s);
+hipError_t launch_adamw(const FlatTask* tasks, int ntasks, int total_blocks,
+                        const AdamArgs& args, hipStream_t s);
 
 // Launch helpers implemented in dmuon_kernels.hip.
 hipError_t launch_momentum(const EwTask* tasks, int ntasks, int total_tiles,

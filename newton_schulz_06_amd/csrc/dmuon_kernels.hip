@@ -13,89 +13,11 @@
 // iteration are "NT" products C = L R^T and share one MFMA main loop.
 #include <type_traits>
 
+#include "dmuon_device.h"
 #include "dmuon_internal.h"
 
 namespace dmuon {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// fp32 -> bf16, round to nearest even, NaN stays NaN: gfx950 converts in
-// hardware (v_cvt_pk_bf16_f32), without a branch.
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  return __builtin_bit_cast(uint16_t, (__bf16)f);
-}
-
-__device__ __forceinline__ uint32_t to_bf16x2(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-__device__ __forceinline__ float from_bf16(uint16_t h) {
-  return __uint_as_float((uint32_t)h << 16);
-}
-
-// Global-memory accessors.  Device pointers reach the kernels through task
-// tables, where the compiler cannot prove their address space; without an
-// explicit global (address space 1) access it emits flat instructions,
-// which also wait on the LDS counter.
-#define GMEM __attribute__((address_space(1)))
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float ld_f32(const float* p) { return *(const GMEM float*)p; }
-__device__ __forceinline__ void st_f32(float* p, float v) { *(GMEM float*)p = v; }
-__device__ __forceinline__ f32x4 ld_f32x4(const float* p) { return *(const GMEM f32x4*)p; }
-__device__ __forceinline__ void st_f32x4(float* p, f32x4 v) { *(GMEM f32x4*)p = v; }
-__device__ __forceinline__ uint16_t ld_u16(const uint16_t* p) { return *(const GMEM uint16_t*)p; }
-__device__ __forceinline__ void st_u16(uint16_t* p, uint16_t v) { *(GMEM uint16_t*)p = v; }
-__device__ __forceinline__ u32x2 ld_u32x2(const uint16_t* p) { return *(const GMEM u32x2*)p; }
-__device__ __forceinline__ void st_u32x2(uint16_t* p, u32x2 v) { *(GMEM u32x2*)p = v; }
-__device__ __forceinline__ void st_u32x4(uint16_t* p, u32x4 v) { *(GMEM u32x4*)p = v; }
-__device__ __forceinline__ uint4 ld_u128(const void* p) {
-  const u32x4 w = *(const GMEM u32x4*)p;
-  return make_uint4(w.x, w.y, w.z, w.w);
-}
-
-__device__ __forceinline__ float load1(const void* base, int dtype, size_t i) {
-  return dtype == 0 ? ld_f32(static_cast<const float*>(base) + i)
-                    : from_bf16(ld_u16(static_cast<const uint16_t*>(base) + i));
-}
-
-__device__ __forceinline__ f32x4 load4(const void* base, int dtype, size_t i) {
-  f32x4 r;
-  if (dtype == 0) {
-    r = ld_f32x4(static_cast<const float*>(base) + i);
-  } else {
-    const u32x2 w = ld_u32x2(static_cast<const uint16_t*>(base) + i);
-    r[0] = __uint_as_float(w.x << 16);
-    r[1] = __uint_as_float(w.x & 0xffff0000u);
-    r[2] = __uint_as_float(w.y << 16);
-    r[3] = __uint_as_float(w.y & 0xffff0000u);
-  }
-  return r;
-}
-
-__device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d) {
-  u32x2 w;
-  w.x = to_bf16x2(a, b);
-  w.y = to_bf16x2(c, d);
-  return w;
-}
-
-__device__ __forceinline__ f32x4 unpack_bf16x4(u32x2 w) {
-  f32x4 r;
-  r[0] = __uint_as_float(w.x << 16);
-  r[1] = __uint_as_float(w.x & 0xffff0000u);
-  r[2] = __uint_as_float(w.y << 16);
-  r[3] = __uint_as_float(w.y & 0xffff0000u);
-  return r;
-}
 
 // The master copy of X, four consecutive elements at offset o (of the
 // fp32 row stride ldx or the bf16 row stride ldxb): fp32 only (fp32
@@ -116,35 +38,6 @@ __device__ __forceinline__ void store_master4(const EwTask& T, size_t row, int c
   } else {
     st_f32x4(T.xm + row * T.ldx + col, u);
   }
-}
-
-// Last task whose tile_begin <= tile (tasks are sorted by tile_begin).
-template <class Task>
-__device__ __forceinline__ int find_task(const Task* tasks, int ntasks, int tile) {
-  int lo = 0, hi = ntasks - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tasks[mid].tile_begin <= tile) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// --------------------------------------------------------------------------
-// Wavefront sum: DPP within each row of 16 lanes, then cross-row shuffles.
-// Every lane ends with the same value, summed in a fixed order.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
 }
 
 // --------------------------------------------------------------------------

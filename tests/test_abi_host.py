@@ -270,3 +270,95 @@ def test_python_binding_maps_errors():
         dm.workspace_size([(0, 3)])
     with pytest.raises(dm.DmuonError):
         dm.workspace_size([(1 << 21, 3)])
+
+
+# ------------------------------------------- clipping and AdamW validation --
+
+FAKE_P, FAKE_M, FAKE_V, FAKE_ST = 0x50000000, 0x60000000, 0x70000000, 0x80000000
+
+
+def _call_clip(g, buckets=None, nb=1, max_norm=1.0, stats_only=0, p=2.0, stats=FAKE_ST,
+               ws=FAKE_WS, ws_bytes=1 << 40):
+    bk = None
+    if buckets is not None:
+        arr = (ctypes.c_int32 * len(buckets))(*buckets)
+        bk = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return dm.lib().dmuon_clip_grad_norm(ctypes.byref(g), bk, nb, max_norm, stats_only, p,
+                                         stats, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_clip_workspace_size():
+    # per-block fp32 partials (blocks of 4096 elements), then one fp32 factor
+    # per bucket, each rounded up to 256 bytes
+    shapes = [(100, 300), (4096, 14336), (7, 1)]
+    blocks = sum(-(-m * n // 4096) for m, n in shapes)
+    assert dm.clip_workspace_size(shapes, 3) == _pad(4 * blocks, 256) + _pad(12, 256)
+    assert dm.clip_workspace_size([], 1) == 0
+
+
+CLIP_BAD = {
+    "no buckets": dict(nb=0),
+    "bucket map missing": dict(nb=2),
+    "bucket out of range": dict(buckets=[0, 2], nb=2),
+    "negative bucket": dict(buckets=[-1, 0], nb=2),
+    "zero norm type": dict(p=0.0),
+    "nan norm type": dict(p=float("nan")),
+    "negative max_norm": dict(max_norm=-1.0),
+    "nan max_norm": dict(max_norm=float("nan")),
+    "null stats": dict(stats=0),
+    "misaligned stats": dict(stats=FAKE_ST + 4),
+    "workspace too small": dict(ws_bytes=16),
+    "null workspace": dict(ws=0),
+    "stats overlap grads": dict(stats=FAKE_G + 64),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CLIP_BAD))
+def test_clip_rejects(name):
+    g, k = _mats([(64, 96, FAKE_G), (32, 8, FAKE_G + 64 * 96 * 4)])
+    want = dm.DMUON_E_WORKSPACE if "workspace" in name else dm.DMUON_E_INVALID
+    assert _call_clip(g, **CLIP_BAD[name]) == want, _err()
+
+
+def test_clip_stats_only_ignores_max_norm():
+    # max_norm is not checked when only measuring: validation passes and the
+    # call reaches the device
+    g, k = _mats([(64, 96, FAKE_G)])
+    st = _call_clip(g, max_norm=float("nan"), stats_only=1)
+    assert st in (dm.DMUON_OK, dm.DMUON_E_HIP), _err()
+    assert st != dm.DMUON_E_INVALID
+
+
+def _call_adamw(p, g, m, v, step=1, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.01):
+    return dm.lib().dmuon_adamw_step(ctypes.byref(p), ctypes.byref(g), ctypes.byref(m),
+                                     ctypes.byref(v), step, lr, b1, b2, eps, wd, None)
+
+
+def _adam_mats(shape=(16, 8), pd=dm.DMUON_F32, gd=dm.DMUON_F32, md=dm.DMUON_F32,
+               gptr=FAKE_G):
+    return (_mats([(*shape, FAKE_P)], pd)[0], _mats([(*shape, gptr)], gd)[0],
+            _mats([(*shape, FAKE_M)], md)[0], _mats([(*shape, FAKE_V)], dm.DMUON_F32)[0])
+
+
+ADAMW_BAD = {
+    "step 0": (dict(), dict(step=0)),
+    "beta1 1": (dict(), dict(b1=1.0)),
+    "beta2 negative": (dict(), dict(b2=-0.1)),
+    "eps 0": (dict(), dict(eps=0.0)),
+    "lr inf": (dict(), dict(lr=float("inf"))),
+    "bf16 moments": (dict(md=dm.DMUON_BF16), dict()),
+    "grads overlap params": (dict(gptr=FAKE_P + 8), dict()),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ADAMW_BAD))
+def test_adamw_rejects(name):
+    mk, kw = ADAMW_BAD[name]
+    p, g, m, v = _adam_mats(**mk)
+    assert _call_adamw(p, g, m, v, **kw) == dm.DMUON_E_INVALID, _err()
+
+
+def test_adamw_shape_mismatch_rejected():
+    p, g, m, v = _adam_mats()
+    g2 = _mats([(16, 9, FAKE_G)])[0]
+    assert _call_adamw(p, g2, m, v) == dm.DMUON_E_INVALID, _err()
