@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--op", default="muon", choices=["muon", "clip", "adamw"],
+                    help="muon: the Muon step (default); clip / adamw: the element-wise "
+                         "companions (gradient clipping, AdamW) on their own workloads")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's host timing (0 disables it)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -105,7 +108,8 @@ def make_inputs(cfg, n_sets, device):
 
 def kernel_sha():
     h = hashlib.sha256()
-    for f in ("dmuon_kernels.hip", "dmuon_internal.h", "dmuon_host.cpp"):
+    for f in ("dmuon_kernels.hip", "dmuon_optim.hip", "dmuon_device.h", "dmuon_internal.h",
+              "dmuon_host.cpp"):
         with open(os.path.join(ROOT, "newton_schulz_06_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -168,12 +172,144 @@ def cpu_baseline(cfg, budget_s):
     }
 
 
+OP_METRIC = {
+    "clip": "Muon gradient clipping (norm + scale) ms & HBM GB/s, 1 GPU",
+    "adamw": "AdamW update of non-Muon params ms & HBM GB/s, 1 GPU",
+}
+
+
+def run_op(args):
+    """Gradient clipping or AdamW on its workload: K timed calls, HBM-bound,
+    value = algorithmic bytes moved per second."""
+    import numpy as np
+    import torch
+    import workloads
+    import newton_schulz_06_amd as dm
+
+    oc = workloads.OP_CONFIGS[args.op]
+    steps = args.steps if args.steps is not None else 20
+    warmup = args.warmup if args.warmup is not None else 3
+    device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
+    gen = torch.Generator(device=device).manual_seed(17)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[oc.dtype]
+    esz = 4 if oc.dtype == "f32" else 2
+    numel = sum(m * n for m, n in oc.shapes)
+    log(f"{args.op} on {oc.name}: {len(oc.shapes)} tensors, {numel / 1e6:.1f}M elements")
+    if args.op == "clip":
+        gs = [torch.randn(s, device=device, generator=gen).to(dt) for s in oc.shapes]
+        call = dm.PreparedClip(gs, oc.max_norm, buckets=list(oc.buckets))
+        # Every call must really clip: measure the largest bucket norm once,
+        # then halve max_norm from call to call (each call scales by ~1/2).
+        probe = dm.PreparedClip(gs, None, buckets=list(oc.buckets))
+        probe()
+        m0 = 0.5 * min(s["total_norm"] for s in probe.stats())
+        run = lambda t: call(m0 * 0.5 ** t)  # noqa: E731
+        bytes_call = 3.0 * numel * esz  # read (norm), read + write (scale)
+    else:
+        ps = [(0.02 * torch.randn(s, device=device, generator=gen)).to(dt) for s in oc.shapes]
+        gs = [(0.1 * torch.randn(s, device=device, generator=gen)).to(dt) for s in oc.shapes]
+        ms = [torch.zeros(s, device=device) for s in oc.shapes]
+        vs = [torch.zeros(s, device=device) for s in oc.shapes]
+        call = dm.PreparedAdamW(ps, gs, ms, vs)
+        run = call
+        bytes_call = numel * (2.0 * esz + esz + 16.0)  # p r/w, g, m and v r/w
+    torch.cuda.synchronize()
+    for w in range(max(warmup - 1, 0)):
+        run(w + 1)
+    with dm.profile() as prof_all:
+        run(warmup)
+    torch.cuda.synchronize()
+    dominant = max(prof_all.rows, key=lambda k: prof_all.rows[k]["ms"])
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with dm.profile(kinds=[dominant]) as prof:
+        e0.record(stream)
+        for s in range(steps):
+            run(warmup + 1 + s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    gbs = bytes_call / (ms_step * 1e-3) / 1e9
+    log(f"timed {steps} calls: {ms_step:.4f} ms/call, {gbs:.1f} GB/s")
+    row = prof.rows[dominant]
+    roof = roofline(row, "f32")
+    roof.update({"kernel": dominant,
+                 "flops_per_launch": 0.0,
+                 "bytes_per_launch": row["bytes"] / row["launches"],
+                 "avg_launch_ms": round(row["ms"] / row["launches"], 5),
+                 "launches": row["launches"],
+                 "traffic": traffic_for(dominant, oc.name)})
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = op_cpu_baseline(args.op, oc, min(args.cpu_seconds, 10.0))
+    out = {
+        "metric": OP_METRIC[args.op],
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": oc.dtype,
+        "data": "synthetic",
+        "config": {"workload": oc.name, "tensors": len(oc.shapes), "elements": numel,
+                   "shapes": sorted({f"{m}x{n}" for m, n in oc.shapes}),
+                   "buckets": len(set(oc.buckets)) if oc.buckets else None,
+                   "parallelism": "1 GPU"},
+        "bytes_per_step": bytes_call,
+        "kernel_ms_one_step": {k: round(v["ms"], 4) for k, v in prof_all.rows.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def op_cpu_baseline(op, oc, budget_s):
+    """The fp64 oracle on the host over whole row blocks of the workload's
+    tensors until the budget is used; reported as algorithmic GB/s."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+    done, t_total, nbytes = 0, 0.0, 0.0
+    esz = 4 if oc.dtype == "f32" else 2
+    rows = 256
+    for m, n in oc.shapes:
+        r = min(rows, m)
+        if op == "clip":
+            g = rng.standard_normal((r, n))
+            t0 = time.perf_counter()
+            oracle.clip_grad_norm([g], oc.max_norm)
+            t_total += time.perf_counter() - t0
+            nbytes += 3.0 * g.size * esz
+        else:
+            p, g = 0.02 * rng.standard_normal((r, n)), 0.1 * rng.standard_normal((r, n))
+            t0 = time.perf_counter()
+            oracle.adamw_step(p, g, np.zeros_like(p), np.zeros_like(p), 1)
+            t_total += time.perf_counter() - t0
+            nbytes += g.size * (3.0 * esz + 16.0)
+        done += r * n
+        if t_total >= budget_s:
+            break
+    return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{done / 1e6:.2f}M elements ({rows}-row blocks), {t_total:.2f} s; numpy fp64"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.op != "muon":
+        run_op(args)
+        return
     import torch
     import workloads
     import newton_schulz_06_amd as dm

@@ -389,8 +389,10 @@ class PreparedClip:
         self.stream = _stream_handle(stream)
         self.fn = lib().dmuon_clip_grad_norm
 
-    def __call__(self):
-        st = self.fn(ctypes.byref(self.bg), self.bptr, self.nb, self.max_norm,
+    def __call__(self, max_norm=None):
+        """Enqueues the clipping; ``max_norm`` overrides the prepared value."""
+        mx = self.max_norm if max_norm is None else float(max_norm)
+        st = self.fn(ctypes.byref(self.bg), self.bptr, self.nb, mx,
                      int(self.stats_only), self.norm_type, int(self.dev_stats.data_ptr()),
                      int(self.ws.data_ptr()), int(self.ws.numel()), self.stream)
         if st:

@@ -630,14 +630,16 @@ std::vector<std::unique_ptr<FlatPlan>>& g_flat = *new std::vector<std::unique_pt
 
 int64_t numel(const dmuon_mat_t& M) { return M.m * M.n; }
 
-// Chunk counts per tensor; fails when the launch would not fit int32.
-dmuon_status_t flat_blocks(const dmuon_batch_t* b, std::vector<FlatTask>* tasks, int* nblocks) {
+// Chunk counts per tensor (chunks of `chunk` elements); fails when the
+// launch would not fit int32.
+dmuon_status_t flat_blocks(const dmuon_batch_t* b, int64_t chunk, std::vector<FlatTask>* tasks,
+                           int* nblocks) {
   int64_t blk = 0;
   tasks->assign(b->count, FlatTask{});
   for (int i = 0; i < b->count; ++i) {
     FlatTask& t = (*tasks)[i];
     t.n = numel(b->mats[i]);
-    const int64_t nb = (t.n + FLAT_CHUNK - 1) / FLAT_CHUNK;
+    const int64_t nb = (t.n + chunk - 1) / chunk;
     t.blk_begin = (int32_t)blk;
     t.nblk = (int32_t)nb;
     blk += nb;
@@ -807,7 +809,7 @@ dmuon_status_t dmuon_clip_workspace_size(const dmuon_batch_t* grads, int32_t nbu
   if (nbuckets < 1) return fail(DMUON_E_INVALID, "nbuckets must be >= 1");
   std::vector<FlatTask> tasks;
   int nblocks = 0;
-  if ((st = flat_blocks(grads, &tasks, &nblocks))) return st;
+  if ((st = flat_blocks(grads, (int64_t)FLAT_STEP * FLAT_ITERS_CLIP, &tasks, &nblocks))) return st;
   *bytes = grads->count ? clip_ws_bytes(nblocks, nbuckets) : 0;
   return DMUON_OK;
 }
@@ -836,7 +838,7 @@ dmuon_status_t dmuon_clip_grad_norm(const dmuon_batch_t* grads, const int32_t* b
   }
   std::vector<FlatTask> tasks;
   int nblocks = 0;
-  if ((st = flat_blocks(grads, &tasks, &nblocks))) return st;
+  if ((st = flat_blocks(grads, (int64_t)FLAT_STEP * FLAT_ITERS_CLIP, &tasks, &nblocks))) return st;
   const size_t need = grads->count ? clip_ws_bytes(nblocks, nbuckets) : 0;
   if (need) {
     if (!ws) return fail(DMUON_E_WORKSPACE, "workspace: null pointer");
@@ -929,7 +931,7 @@ dmuon_status_t dmuon_adamw_step(const dmuon_batch_t* params, const dmuon_batch_t
   if ((st = check_disjoint(spans, names))) return st;
   std::vector<FlatTask> tasks;
   int nblocks = 0;
-  if ((st = flat_blocks(params, &tasks, &nblocks))) return st;
+  if ((st = flat_blocks(params, (int64_t)FLAT_STEP * FLAT_ITERS_ADAMW, &tasks, &nblocks))) return st;
   double bytes = 0;
   for (int i = 0; i < params->count; ++i) {
     FlatTask& t = tasks[i];

@@ -112,9 +112,13 @@ struct NormTask {
 
 // ---------------------------------------------------------------------------
 // Flat element-wise launches (gradient clipping, AdamW): every tensor is
-// cut into chunks of FLAT_CHUNK elements, one block per chunk.
+// cut into chunks, one block per chunk.  A block handles 16 elements per
+// thread at a time (FLAT_STEP), FLAT_ITERS_* times: AdamW keeps four arrays
+// per element live, clipping only one and needs bigger blocks to stream.
 constexpr int FLAT_THREADS = 256;
-constexpr int FLAT_CHUNK = FLAT_THREADS * 16;
+constexpr int FLAT_STEP = FLAT_THREADS * 16;
+constexpr int FLAT_ITERS_ADAMW = 1;
+constexpr int FLAT_ITERS_CLIP = 4;
 
 struct FlatTask {
   int64_t n;               // elements of the tensor

@@ -73,10 +73,49 @@ __device__ __forceinline__ void store4_tail(void* base, int dtype, int64_t i, in
     if (i + e < n) store1_dt(base, dtype, (size_t)(i + e), x[e]);
 }
 
+// The ITERS x 16 elements of this thread in a chunk starting at `chunk`:
+// element chunk + it*FLAT_STEP + (k*FLAT_THREADS + tid)*4 + e.  A chunk that
+// lies wholly inside an aligned tensor (every chunk but a tensor's last)
+// loads without per-lane conditions, so nothing separates the loads from
+// each other; the tail chunk checks each element.
+template <int ITERS>
+__device__ __forceinline__ void load_chunk(const void* base, int dtype, int64_t chunk, int64_t n,
+                                           bool vec, int tid, f32x4 (&x)[ITERS][4]) {
+  if (vec && chunk + (int64_t)ITERS * FLAT_STEP <= n) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        x[it][k] = load4(base, dtype,
+                         (size_t)(chunk + (int64_t)it * FLAT_STEP + (k * FLAT_THREADS + tid) * 4));
+  } else {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        x[it][k] = load4_tail(base, dtype,
+                              chunk + (int64_t)it * FLAT_STEP + (k * FLAT_THREADS + tid) * 4, n,
+                              vec);
+  }
+}
+
+template <int ITERS>
+__device__ __forceinline__ void store_chunk(void* base, int dtype, int64_t chunk, int64_t n,
+                                            bool vec, int tid, const f32x4 (&x)[ITERS][4]) {
+  const bool full = vec && chunk + (int64_t)ITERS * FLAT_STEP <= n;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      store4_tail(base, dtype, chunk + (int64_t)it * FLAT_STEP + (k * FLAT_THREADS + tid) * 4,
+                  full ? INT64_MAX : n, vec, x[it][k]);
+}
+
 // ---------------------------------------------------------------------------
-// Clipping, pass 1: every block reduces its chunk to one partial (sum of
-// squares, sum of magnitudes, sum of |g|^p, or NaN-keeping max of |g|), in a
-// fixed order: 16 elements per thread, then the wave, then the 4 waves.
+// Clipping, pass 1: every block reduces its chunk (FLAT_ITERS_CLIP steps of
+// 16 elements per thread) to one partial (sum of squares, sum of
+// magnitudes, sum of |g|^p, or NaN-keeping max of |g|), in a fixed order:
+// per thread, then the wave, then the 4 waves.
 __global__ __launch_bounds__(FLAT_THREADS) void clip_norm_kernel(
     const FlatTask* __restrict__ tasks, int ntasks, int total_blocks, int mode, float p,
     float* __restrict__ partial) {
@@ -84,23 +123,27 @@ __global__ __launch_bounds__(FLAT_THREADS) void clip_norm_kernel(
   const int b = blockIdx.x;
   if (b >= total_blocks) return;
   const FlatTask T = tasks[find_flat(tasks, ntasks, b)];
-  const int64_t base = (int64_t)(b - T.blk_begin) * FLAT_CHUNK;
+  const int64_t chunk = (int64_t)(b - T.blk_begin) * FLAT_STEP * FLAT_ITERS_CLIP;
   const int tid = threadIdx.x;
-  f32x4 x[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    x[k] = load4_tail(T.p, T.dtype, base + ((int64_t)k * FLAT_THREADS + tid) * 4, T.n, T.vec);
+  // One step of 16 elements per thread at a time (past the end they read
+  // as zeros, which no norm changes), accumulated in a fixed order.
   float acc = 0.f;
+  for (int it = 0; it < FLAT_ITERS_CLIP; ++it) {
+    const int64_t base = chunk + (int64_t)it * FLAT_STEP;
+    if (base >= T.n) break;
+    f32x4 x[1][4];
+    load_chunk<1>(T.p, T.dtype, base, T.n, T.vec, tid, x);
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = fabsf(x[k][e]);
-      if (mode == NORM_L2) acc = fmaf(a, a, acc);
-      else if (mode == NORM_L1) acc += a;
-      else if (mode == NORM_INF) acc = nanmax(acc, a);
-      else acc += powf(a, p);
-    }
+      for (int e = 0; e < 4; ++e) {
+        const float a = fabsf(x[0][k][e]);
+        if (mode == NORM_L2) acc = fmaf(a, a, acc);
+        else if (mode == NORM_L1) acc += a;
+        else if (mode == NORM_INF) acc = nanmax(acc, a);
+        else acc += powf(a, p);
+      }
+  }
   acc = mode == NORM_INF ? wave_nanmax(acc) : wave_sum(acc);
   if ((tid & 63) == 0) wpart[tid >> 6] = acc;
   __syncthreads();
@@ -172,17 +215,18 @@ __global__ __launch_bounds__(FLAT_THREADS) void clip_scale_kernel(
   const FlatTask T = tasks[find_flat(tasks, ntasks, b)];
   const float f = ld_f32(scale + T.bucket);
   if (f == 1.f) return;
-  const int64_t base = (int64_t)(b - T.blk_begin) * FLAT_CHUNK;
+  const int64_t chunk = (int64_t)(b - T.blk_begin) * FLAT_STEP * FLAT_ITERS_CLIP;
   const int tid = threadIdx.x;
-  f32x4 x[4];
+  for (int it = 0; it < FLAT_ITERS_CLIP; ++it) {
+    const int64_t base = chunk + (int64_t)it * FLAT_STEP;
+    if (base >= T.n) break;
+    f32x4 x[1][4];
+    load_chunk<1>(T.p, T.dtype, base, T.n, T.vec, tid, x);
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    x[k] = load4_tail(T.p, T.dtype, base + ((int64_t)k * FLAT_THREADS + tid) * 4, T.n, T.vec);
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[k][e] *= f;
-    store4_tail(T.p, T.dtype, base + ((int64_t)k * FLAT_THREADS + tid) * 4, T.n, T.vec, x[k]);
+      for (int e = 0; e < 4; ++e) x[0][k][e] *= f;
+    store_chunk<1>(T.p, T.dtype, base, T.n, T.vec, tid, x);
   }
 }
 
@@ -195,34 +239,29 @@ __global__ __launch_bounds__(FLAT_THREADS) void adamw_kernel(
   const int b = blockIdx.x;
   if (b >= total_blocks) return;
   const FlatTask T = tasks[find_flat(tasks, ntasks, b)];
-  const int64_t base = (int64_t)(b - T.blk_begin) * FLAT_CHUNK;
+  static_assert(FLAT_ITERS_ADAMW == 1, "one step of 16 elements per thread");
+  const int64_t base = (int64_t)(b - T.blk_begin) * FLAT_STEP;
   const int tid = threadIdx.x;
-  f32x4 p[4], g[4], m[4], v[4];
+  f32x4 p[1][4], g[1][4], m[1][4], v[1][4];
+  load_chunk<1>(T.p, T.dtype, base, T.n, T.vec, tid, p);
+  load_chunk<1>(T.g, T.gdtype, base, T.n, T.vec, tid, g);
+  load_chunk<1>(T.m, 0, base, T.n, T.vec, tid, m);
+  load_chunk<1>(T.v, 0, base, T.n, T.vec, tid, v);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t i = base + ((int64_t)k * FLAT_THREADS + tid) * 4;
-    p[k] = load4_tail(T.p, T.dtype, i, T.n, T.vec);
-    g[k] = load4_tail(T.g, T.gdtype, i, T.n, T.vec);
-    m[k] = load4_tail(T.m, 0, i, T.n, T.vec);
-    v[k] = load4_tail(T.v, 0, i, T.n, T.vec);
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 4; ++k)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float gg = g[k][e];
-      const float mm = fmaf(A.beta1, m[k][e], A.one_minus_beta1 * gg);
-      const float vv = fmaf(A.beta2, v[k][e], A.one_minus_beta2 * gg * gg);
+      const float gg = g[0][k][e];
+      const float mm = fmaf(A.beta1, m[0][k][e], A.one_minus_beta1 * gg);
+      const float vv = fmaf(A.beta2, v[0][k][e], A.one_minus_beta2 * gg * gg);
       const float den = fmaf(sqrtf(vv), A.inv_bc2_sqrt, A.eps);
-      p[k][e] = fmaf(-A.step_size, mm / den, p[k][e] * A.decay);
-      m[k][e] = mm;
-      v[k][e] = vv;
+      p[0][k][e] = fmaf(-A.step_size, mm / den, p[0][k][e] * A.decay);
+      m[0][k][e] = mm;
+      v[0][k][e] = vv;
     }
-    const int64_t i = base + ((int64_t)k * FLAT_THREADS + tid) * 4;
-    store4_tail(T.p, T.dtype, i, T.n, T.vec, p[k]);
-    store4_tail(T.m, 0, i, T.n, T.vec, m[k]);
-    store4_tail(T.v, 0, i, T.n, T.vec, v[k]);
-  }
+  store_chunk<1>(T.p, T.dtype, base, T.n, T.vec, tid, p);
+  store_chunk<1>(T.m, 0, base, T.n, T.vec, tid, m);
+  store_chunk<1>(T.v, 0, base, T.n, T.vec, tid, v);
 }
 
 }  // namespace

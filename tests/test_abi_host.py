@@ -288,10 +288,10 @@ def _call_clip(g, buckets=None, nb=1, max_norm=1.0, stats_only=0, p=2.0, stats=F
 
 
 def test_clip_workspace_size():
-    # per-block fp32 partials (blocks of 4096 elements), then one fp32 factor
-    # per bucket, each rounded up to 256 bytes
+    # per-block fp32 partials (blocks of 16384 elements), then one fp32
+    # factor per bucket, each rounded up to 256 bytes
     shapes = [(100, 300), (4096, 14336), (7, 1)]
-    blocks = sum(-(-m * n // 4096) for m, n in shapes)
+    blocks = sum(-(-m * n // 16384) for m, n in shapes)
     assert dm.clip_workspace_size(shapes, 3) == _pad(4 * blocks, 256) + _pad(12, 256)
     assert dm.clip_workspace_size([], 1) == 0
 

@@ -7,6 +7,7 @@ oracle and the HIP path read their inputs from it.
 """
 from .synth import (  # noqa: F401
     CONFIGS,
+    OP_CONFIGS,
     Config,
     c4_shapes,
     grad_np,

@@ -225,3 +225,26 @@ def param_torch(m, n, cfg_id, idx, device, dtype):
     gen = _torch_gen(device, seed_words(cfg_id, 0, idx, STREAM_PARAM))
     return (0.02 * torch.randn(m, n, generator=gen, device=device,
                                dtype=torch.float32)).to(dtype)
+
+
+# ------------------------------------------------ element-wise companions --
+
+@dataclass(frozen=True)
+class OpConfig:
+    """Workload of an element-wise companion of the Muon step."""
+    name: str
+    shapes: tuple            # tensor shapes
+    dtype: str               # param / gradient dtype
+    buckets: tuple = ()      # clipping: bucket of each tensor
+    max_norm: float = 0.0    # clipping: chosen below the gradients' norm
+    notes: str = field(default="", compare=False)
+
+
+OP_CONFIGS = {
+    # the 28 projection gradients of the Llama-8B batch, one bucket per layer
+    # (bench.py lowers max_norm from call to call so that every call clips)
+    "clip": OpConfig("llama8b_proj_grads_4_buckets", _llama8b(4), "bf16",
+                     buckets=tuple(i // 7 for i in range(28)), max_norm=100.0),
+    # AdamW's share of a Llama-8B: token embedding and LM head (vocab 128256)
+    "adamw": OpConfig("llama8b_embed_lmhead", ((128256, 4096),) * 2, "bf16"),
+}
