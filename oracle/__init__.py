@@ -18,6 +18,9 @@ from .muon_ref import (  # noqa: F401
     ns_iterate_left,
     ns_iterate_right,
     direct_newton_schulz,
+    gram_windows,
+    gram_newton_schulz_factors,
+    gram_newton_schulz,
     muon_step,
     round_to_bf16,
 )

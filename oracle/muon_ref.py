@@ -24,7 +24,19 @@ documentation pages; readings of unstated points are marked READING):
    coefficients; the standard quintic (3.4445, -4.7750, 2.0315) is used at
    every step.  YOU_COEFFICIENTS are printed on the same page and are the
    second table used here.
-5. update (DMuon "HSDP Training (Multi-Node)", "What Happens Under the Hood":
+5. Gram-space NS (DMuon "API Reference", ``gram_newton_schulz`` and
+   ``gram_newton_schulz_factors``: iterate on the Gram matrix instead of the
+   full matrix, with per-step coefficients and restarts (default ``[2]``);
+   the result is the normalized, oriented G left-multiplied by one Gram
+   factor per restart window).
+   READING: the pages give no formulas.  The iteration of step 4,
+   X_{k+1} = P_k X_k with P_k = a I + b A_k + c A_k^2 and A_k = X_k X_k^T, is
+   carried in Gram space: within a window starting at X_s, A_s = X_s X_s^T,
+   Q accumulates P_k Q and A_{k+1} = P_k A_k P_k (P_k is symmetric); at the
+   window's end X <- Q X_s.  A restart at step r starts a new window there
+   (restart indices outside 1..steps-1 have no effect).  Exactly equal to
+   step 4 in exact arithmetic.
+6. update (DMuon "HSDP Training (Multi-Node)", "What Happens Under the Hood":
    the owner runs NS + momentum + weight decay + update; "API Reference",
    ``Muon`` signature: lr=0.02, momentum=0.95, weight_decay=0.0).
    READING: decoupled weight decay ``p <- p - lr*wd*p - lr*O`` on the
@@ -150,6 +162,56 @@ def direct_newton_schulz(G, steps: int = 5, eps: float = DEFAULT_EPS,
     X, transposed = orient(G)
     X = frobenius_normalize(X, eps)
     X = ns_iterate_left(X, table)
+    return X.T if transposed else X
+
+
+def gram_windows(n_steps: int, restart_iterations=None):
+    """[start, end) step ranges between restarts (default restart at 2)."""
+    restarts = [2] if restart_iterations is None else [int(r) for r in restart_iterations]
+    if any(r < 0 for r in restarts):
+        raise ValueError("restart indices are >= 0")
+    cuts = sorted({0, n_steps} | {r for r in restarts if 0 < r < n_steps})
+    return list(zip(cuts[:-1], cuts[1:]))
+
+
+def gram_newton_schulz_factors(G, steps: int = 5, eps: float = DEFAULT_EPS, coefficients=None,
+                               restart_iterations=None):
+    """Gram-space NS factors of G: ``(segments, transposed, normalizer)``.
+
+    DMuon "API Reference", ``gram_newton_schulz_factors``: one Gram factor
+    per restart window, applied in order from the left to the normalized,
+    oriented G; the normalizer is ||G||_F + eps (READING in the header).
+    """
+    table = coefficient_table(coefficients, steps)
+    X, transposed = orient(G)
+    normalizer = float(np.linalg.norm(X)) + eps
+    X = X / normalizer
+    p = X.shape[0]
+    segments = []
+    for s, e in gram_windows(len(table), restart_iterations):
+        A = X @ X.T
+        Q = np.eye(p)
+        for k in range(s, e):
+            a, b, c = table[k]
+            P = a * np.eye(p) + b * A + c * (A @ A)
+            Q = P @ Q
+            A = P @ A @ P
+        segments.append(Q)
+        X = Q @ X
+    return tuple(segments), transposed, normalizer
+
+
+def gram_newton_schulz(G, steps: int = 5, eps: float = DEFAULT_EPS, coefficients=None,
+                       restart_iterations=None):
+    """Gram-space NS of G (DMuon "API Reference", ``gram_newton_schulz``):
+    the factors of :func:`gram_newton_schulz_factors` applied to the
+    normalized, oriented G; same shape as G, float64."""
+    segments, transposed, normalizer = gram_newton_schulz_factors(
+        G, steps, eps, coefficients, restart_iterations)
+    X, _ = orient(G)
+    X = X / normalizer
+    for Q in segments:
+        X = Q @ X
     return X.T if transposed else X
 
 
