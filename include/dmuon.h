@@ -89,26 +89,49 @@ typedef struct {
 } dmuon_batch_t;
 
 /*
+ * How the NS polynomial is evaluated (DMuon "API Reference", NewtonSchulz
+ * backend "direct" or "gram").
+ *   DMUON_NS_DIRECT  X <- a X + (b A + c A^2) X with A = X X^T, per step.
+ *   DMUON_NS_GRAM    Gram space (gram_newton_schulz): per restart window,
+ *                    A = X X^T, then per step P = a I + b A + c A^2,
+ *                    Q <- P Q, A <- P A P, and X <- Q X at the window's
+ *                    end.  Equal to DIRECT in exact arithmetic.  Runs with
+ *                    fp32 operands only (prec F32, or AUTO which resolves
+ *                    to F32): with bf16 operands the Q factor amplifies the
+ *                    rounding of X in the small singular directions.
+ */
+typedef enum { DMUON_NS_DIRECT = 0, DMUON_NS_GRAM = 1 } dmuon_ns_backend_t;
+
+/*
  * Newton-Schulz configuration (DMuon "API Reference", direct_newton_schulz:
  * per-step (a, b, c) coefficients whose list length is the number of
- * iterations; eps is added to the Frobenius norm used to normalize).
- *   coeffs    host array of 3 * ns_steps floats (a0, b0, c0, a1, ...), or
- *             NULL for (3.4445, -4.7750, 2.0315) at every step.
- *   ns_steps  1..16.
- *   eps       >= 0 and finite (1e-7 in DMuon's signature).
- *   prec      dmuon_prec_t.
+ * iterations; eps is added to the Frobenius norm used to normalize;
+ * gram_newton_schulz: restart_iterations, default [2]).
+ *   coeffs     host array of 3 * ns_steps floats (a0, b0, c0, a1, ...), or
+ *              NULL for (3.4445, -4.7750, 2.0315) at every step.
+ *   ns_steps   1..16.
+ *   eps        >= 0 and finite (1e-7 in DMuon's signature).
+ *   prec       dmuon_prec_t.
+ *   backend    dmuon_ns_backend_t.
+ *   restarts   GRAM only: host array of nrestarts step indices where a new
+ *              window starts (indices outside 1..ns_steps-1 have no
+ *              effect; negative ones are rejected), or NULL for [2].
  */
 typedef struct {
   const float* coeffs;
   int32_t ns_steps;
   float eps;
   int32_t prec;
+  int32_t backend;
+  int32_t nrestarts;
+  const int32_t* restarts;
 } dmuon_ns_cfg_t;
 
 /*
  * Workspace bytes needed by dmuon_ns_orthogonalize / dmuon_muon_step for a
- * batch of these shapes.  Only the shapes, count and cfg->prec matter (the
- * pointers of `g` are not read; they may be NULL).  Pure host computation.
+ * batch of these shapes.  Only the shapes, count, cfg->prec and
+ * cfg->backend matter (the pointers of `g` are not read; they may be NULL).
+ * Pure host computation.
  */
 dmuon_status_t dmuon_ns_workspace_size(const dmuon_batch_t* g,
                                        const dmuon_ns_cfg_t* cfg,

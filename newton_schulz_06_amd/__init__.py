@@ -41,7 +41,11 @@ class Batch(ctypes.Structure):
 
 class NsCfg(ctypes.Structure):
     _fields_ = [("coeffs", ctypes.POINTER(ctypes.c_float)), ("ns_steps", ctypes.c_int32),
-                ("eps", ctypes.c_float), ("prec", ctypes.c_int32)]
+                ("eps", ctypes.c_float), ("prec", ctypes.c_int32), ("backend", ctypes.c_int32),
+                ("nrestarts", ctypes.c_int32), ("restarts", ctypes.POINTER(ctypes.c_int32))]
+
+
+BACKEND = {"direct": 0, "gram": 1}
 
 
 class ProfileRow(ctypes.Structure):
@@ -182,19 +186,31 @@ def shape_batch(shapes, dtype=DMUON_BF16):
     return Batch(arr, len(shapes), dtype), arr
 
 
-def make_cfg(coefficients=None, ns_steps=5, eps=1e-7, prec="bf16"):
+def make_cfg(coefficients=None, ns_steps=5, eps=1e-7, prec="bf16", backend="direct",
+             restart_iterations=None):
+    """NS configuration.  ``backend``: "direct" or "gram"; for "gram",
+    ``restart_iterations`` None means DMuon's default [2]."""
     if isinstance(prec, str):
         prec = PREC[prec]
-    keep = None
+    if isinstance(backend, str):
+        backend = BACKEND[backend]
+    keep = []
     ptr = None
     if coefficients is not None:
         flat = [float(v) for row in coefficients for v in row]
         if len(flat) != 3 * len(coefficients):
             raise DmuonValueError(DMUON_E_INVALID, "coefficient rows must be (a, b, c)")
         ns_steps = len(coefficients)
-        keep = (ctypes.c_float * len(flat))(*flat)
-        ptr = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
-    return NsCfg(ptr, int(ns_steps), float(eps), int(prec)), keep
+        arr = (ctypes.c_float * len(flat))(*flat)
+        keep.append(arr)
+        ptr = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    rptr, nr = None, 0
+    if restart_iterations is not None:
+        r = [int(v) for v in restart_iterations]
+        arr = (ctypes.c_int32 * max(1, len(r)))(*r)
+        keep.append(arr)
+        rptr, nr = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), len(r)
+    return NsCfg(ptr, int(ns_steps), float(eps), int(prec), int(backend), nr, rptr), keep
 
 
 def _stream_handle(stream):
@@ -210,29 +226,30 @@ def backend_info() -> str:
     return lib().dmuon_backend_info().decode()
 
 
-def workspace_size(shapes, prec="bf16") -> int:
+def workspace_size(shapes, prec="bf16", backend="direct") -> int:
     """dmuon_ns_workspace_size for a list of (m, n) shapes."""
     b, keep = shape_batch(shapes)
-    cfg, ck = make_cfg(prec=prec)
+    cfg, ck = make_cfg(prec=prec, backend=backend)
     out = ctypes.c_size_t(0)
     _check(lib().dmuon_ns_workspace_size(ctypes.byref(b), ctypes.byref(cfg), ctypes.byref(out)))
     return int(out.value)
 
 
-def alloc_workspace(shapes, prec="bf16", device="cuda"):
+def alloc_workspace(shapes, prec="bf16", device="cuda", backend="direct"):
     """Device workspace (a torch uint8 tensor) big enough for these shapes."""
     import torch
-    return torch.empty(max(1, workspace_size(shapes, prec)), dtype=torch.uint8, device=device)
+    return torch.empty(max(1, workspace_size(shapes, prec, backend)), dtype=torch.uint8,
+                       device=device)
 
 
-def _ws(workspace, shapes, prec, device):
+def _ws(workspace, shapes, prec, device, backend="direct"):
     if workspace is None:
-        workspace = alloc_workspace(shapes, prec, device)
+        workspace = alloc_workspace(shapes, prec, device, backend)
     return workspace, ctypes.c_void_p(int(workspace.data_ptr())), int(workspace.numel())
 
 
 def ns_orthogonalize(gs, outs=None, *, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
-                     workspace=None, stream=None):
+                     backend="direct", restart_iterations=None, workspace=None, stream=None):
     """dmuon_ns_orthogonalize: outs[i] = NS(gs[i]) in gs[i]'s dtype.
     `outs` defaults to new tensors; passing `outs=gs` works in place."""
     import torch
@@ -242,26 +259,26 @@ def ns_orthogonalize(gs, outs=None, *, coefficients=None, ns_steps=5, eps=1e-7, 
     outs = list(outs)
     bg, kg = make_batch(gs)
     bo, ko = make_batch(outs)
-    cfg, kc = make_cfg(coefficients, ns_steps, eps, prec)
+    cfg, kc = make_cfg(coefficients, ns_steps, eps, prec, backend, restart_iterations)
     device = gs[0].device if gs else "cuda"
-    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in gs], prec, device)
+    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in gs], prec, device, backend)
     _check(lib().dmuon_ns_orthogonalize(ctypes.byref(bg), ctypes.byref(bo), ctypes.byref(cfg),
                                         wptr, wbytes, _stream_handle(stream)))
     return outs
 
 
 def muon_step(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_decay=0.0, nesterov=True,
-              coefficients=None, ns_steps=5, eps=1e-7, prec="bf16", workspace=None,
-              stream=None):
+              coefficients=None, ns_steps=5, eps=1e-7, prec="bf16", backend="direct",
+              restart_iterations=None, workspace=None, stream=None):
     """dmuon_muon_step: in-place update of `params` and `bufs` (defaults as
     in DMuon's Muon signature)."""
     params, grads, bufs = list(params), list(grads), list(bufs)
     bp, kp = make_batch(params)
     bg, kg = make_batch(grads)
     bb, kb = make_batch(bufs)
-    cfg, kc = make_cfg(coefficients, ns_steps, eps, prec)
+    cfg, kc = make_cfg(coefficients, ns_steps, eps, prec, backend, restart_iterations)
     device = grads[0].device if grads else "cuda"
-    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in grads], prec, device)
+    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in grads], prec, device, backend)
     _check(lib().dmuon_muon_step(ctypes.byref(bp), ctypes.byref(bg), ctypes.byref(bb),
                                  ctypes.byref(cfg), float(momentum), float(lr),
                                  float(weight_decay), int(bool(nesterov)), wptr, wbytes,
@@ -269,7 +286,7 @@ def muon_step(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_decay=0.0, 
 
 
 KINDS = ("momentum", "input", "norm", "syrk", "poly", "update_x", "clip_norm", "clip_scale",
-         "adamw")
+         "adamw", "gram_mul")
 
 
 class profile:
@@ -304,7 +321,7 @@ class PreparedMuonStep:
 
     def __init__(self, params, bufs, grad_sets, *, lr=0.02, momentum=0.95, weight_decay=0.0,
                  nesterov=True, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
-                 workspace=None, stream=None):
+                 backend="direct", restart_iterations=None, workspace=None, stream=None):
         self._keep = []
         self.bp, k = make_batch(params); self._keep.append(k)
         self.bb, k = make_batch(bufs); self._keep.append(k)
@@ -313,9 +330,10 @@ class PreparedMuonStep:
             b, k = make_batch(gs)
             self.bgs.append(b)
             self._keep.append(k)
-        self.cfg, k = make_cfg(coefficients, ns_steps, eps, prec); self._keep.append(k)
+        self.cfg, k = make_cfg(coefficients, ns_steps, eps, prec, backend, restart_iterations)
+        self._keep.append(k)
         shapes = [tuple(p.shape) for p in params]
-        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, params[0].device)
+        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, params[0].device, backend)
         self.stream = _stream_handle(stream)
         self.scalars = (ctypes.c_float(momentum), ctypes.c_float(lr),
                         ctypes.c_float(weight_decay), ctypes.c_int32(int(bool(nesterov))))
@@ -332,12 +350,13 @@ class PreparedNs:
     """dmuon_ns_orthogonalize with the descriptors marshalled once."""
 
     def __init__(self, gs, outs, *, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
-                 workspace=None, stream=None):
+                 backend="direct", restart_iterations=None, workspace=None, stream=None):
         self.bg, self._kg = make_batch(gs)
         self.bo, self._ko = make_batch(outs)
-        self.cfg, self._kc = make_cfg(coefficients, ns_steps, eps, prec)
+        self.cfg, self._kc = make_cfg(coefficients, ns_steps, eps, prec, backend,
+                                      restart_iterations)
         shapes = [tuple(g.shape) for g in gs]
-        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, gs[0].device)
+        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, gs[0].device, backend)
         self.stream = _stream_handle(stream)
         self.fn = lib().dmuon_ns_orthogonalize
 

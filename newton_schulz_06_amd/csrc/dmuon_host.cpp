@@ -73,6 +73,7 @@ struct Geom {
   int hilo;  // master X as bf16 X + bf16 remainder (else fp32, next to bf16 X)
   int64_t ld_xm, ld_xb, ld_xt, ld_a32, ld_aop, ld_bop;  // row strides (elements)
   size_t xm, xb, xlo, xt0, xt1, a32, aop, bop;         // byte offsets in ws
+  size_t pm, pa, qa, qb;  // Gram-space NS: P, P A, and the Q pair (fp32 P x P)
 };
 
 struct Layout {
@@ -80,11 +81,13 @@ struct Layout {
   size_t partial_off = 0, scale_off = 0, sink_off = 0, total = 0;
   int64_t in_tiles = 0;
   int f32_ops = 0;
+  int gram = 0;  // Gram-space NS layout (fp32 operands)
 };
 
-dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
+dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout* out) {
   Layout L;
-  L.f32_ops = (prec == DMUON_NS_F32);
+  L.gram = backend == DMUON_NS_GRAM;
+  L.f32_ops = (prec == DMUON_NS_F32) || L.gram;
   const int n = b->count;
   L.g.resize(n);
   int64_t tiles = 0;
@@ -140,7 +143,17 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, Layout* out) {
     G.xt0 = take(e * Q * G.ld_xt);
     G.xt1 = take(e * Q * G.ld_xt);
     if (L.f32_ops || !G.split_a) G.a32 = take(4 * P * G.ld_a32);
-    if (L.f32_ops) {
+    G.pm = G.pa = G.qa = G.qb = 0;
+    if (L.gram) {
+      G.aop = G.a32;
+      G.ld_aop = G.ld_a32;
+      G.ld_bop = G.ld_a32;
+      G.bop = 0;
+      G.pm = take(4 * P * G.ld_a32);
+      G.pa = take(4 * P * G.ld_a32);
+      G.qa = take(4 * P * G.ld_a32);
+      G.qb = take(4 * P * G.ld_a32);
+    } else if (L.f32_ops) {
       G.aop = G.a32;
       G.ld_aop = G.ld_a32;
       G.ld_bop = ld_for(G.P, 4);
@@ -180,6 +193,20 @@ dmuon_status_t check_batch(const dmuon_batch_t* b, const char* name, bool need_p
   return DMUON_OK;
 }
 
+// Backend and restart list (also needed by the workspace-size query).
+dmuon_status_t check_backend(const dmuon_ns_cfg_t* cfg) {
+  if (cfg->backend != DMUON_NS_DIRECT && cfg->backend != DMUON_NS_GRAM)
+    return fail(DMUON_E_INVALID, "cfg: unknown backend");
+  if (cfg->nrestarts < 0 || (!cfg->restarts && cfg->nrestarts != 0))
+    return fail(DMUON_E_INVALID, "cfg: restarts must hold nrestarts entries");
+  for (int i = 0; i < cfg->nrestarts; ++i)
+    if (cfg->restarts[i] < 0) return fail(DMUON_E_INVALID, "cfg: negative restart index");
+  if (cfg->backend == DMUON_NS_GRAM && cfg->prec != DMUON_NS_F32 && cfg->prec != DMUON_NS_AUTO)
+    return fail(DMUON_E_UNSUPPORTED,
+                "cfg: Gram-space NS runs with fp32 operands only (prec F32 or AUTO)");
+  return DMUON_OK;
+}
+
 dmuon_status_t check_cfg(const dmuon_ns_cfg_t* cfg) {
   if (!cfg) return fail(DMUON_E_INVALID, "cfg: null");
   if (cfg->ns_steps < 1 || cfg->ns_steps > kMaxSteps)
@@ -192,7 +219,7 @@ dmuon_status_t check_cfg(const dmuon_ns_cfg_t* cfg) {
     for (int i = 0; i < 3 * cfg->ns_steps; ++i)
       if (!std::isfinite(cfg->coeffs[i]))
         return fail(DMUON_E_INVALID, "cfg: non-finite coefficient");
-  return DMUON_OK;
+  return check_backend(cfg);
 }
 
 dmuon_status_t same_shapes(const dmuon_batch_t* a, const dmuon_batch_t* b, const char* an,
@@ -245,6 +272,24 @@ struct GemmLaunch {
   // output written once, in the designed layout; UPDX differs on the last
   // iteration (caller's param or output instead of the next X copies).
   double bytes, bytes_fin;
+  int group;  // direct NS: the kind; Gram-space NS: a GramGroup
+};
+
+// Launch groups of Gram-space NS: one product with its buffers.  P of a
+// window's first step lands in Q_a (Q starts as that P); later steps write
+// P to pm and multiply into the other Q buffer.
+enum GramGroup : int {
+  GG_SYRK = 100,   // A = X X^T
+  GG_P_QA,         // P = a I + b A + c A^2 -> Q_a
+  GG_P_PM,         //                        -> pm
+  GG_PA_QA,        // pa = P A, P in Q_a
+  GG_PA_PM,        //           P in pm
+  GG_A_QA,         // A = P pa, P in Q_a
+  GG_A_PM,         //           P in pm
+  GG_Q_AB,         // Q_b = pm Q_a
+  GG_Q_BA,         // Q_a = pm Q_b
+  GG_QX_QA,        // X = Q X, Q in Q_a
+  GG_QX_QB,        //          Q in Q_b
 };
 
 struct Plan {
@@ -252,6 +297,7 @@ struct Plan {
   int device = -1;
   void* dtab = nullptr;
   int f32_ops = 0;
+  int gram = 0;
   size_t in_off = 0, norm_off = 0;
   int nmat = 0, in_tiles = 0;
   double in_bytes = 0, norm_bytes = 0;
@@ -279,6 +325,117 @@ bool vec_ok(const void* p, int dtype, int64_t n) {
   return p && reinterpret_cast<uintptr_t>(p) % need == 0 && n % 4 == 0;
 }
 
+// Gram-space NS launch groups (fp32 operands), appended to `gtasks`: one
+// group per (product, buffers), split by tile class like the direct kinds.
+void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, char* ws,
+                       float* scale, Plan* plan, std::vector<GemmTask>& gtasks,
+                       std::vector<std::pair<size_t, size_t>>& ranges) {
+  const int n = (int)L.g.size();
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  // `fill` sets the product-specific fields of one matrix's task and adds
+  // its algorithmic flops and bytes.
+  auto add_group = [&](int group, int kind, auto&& fill) {
+    for (int tile : kTiles) {
+      const size_t begin = gtasks.size();
+      int acc = 0;
+      double flops = 0, bytes = 0, bytes_fin = 0;
+      for (int i = 0; i < n; ++i) {
+        const Geom& G = L.g[i];
+        if (G.tile != tile) continue;
+        GemmTask t{};
+        t.P = (int)G.P;
+        t.scale = scale + 4 * i;
+        const int nt = (int)G.P / tile;
+        t.tiles_m = t.tiles_n = nt;
+        t.tri = 1;
+        t.tile_count = nt * (nt + 1) / 2;
+        t.K = t.kper = (int)G.P;
+        t.ldl = t.ldr = t.ld0 = t.ld_f = (int32_t)G.ld_a32;
+        fill(t, G, i, tile, flops, bytes, bytes_fin);
+        t.tile_begin = acc;
+        acc += t.tile_count;
+        gtasks.push_back(t);
+      }
+      if (gtasks.size() > begin) {
+        plan->gemms.push_back(GemmLaunch{kind, tile, 0, (int)(gtasks.size() - begin), acc, flops,
+                                         bytes, kind == KIND_UPDX ? bytes_fin : bytes, group});
+        ranges.push_back({begin, gtasks.size()});
+      }
+    }
+  };
+  using D = double;
+  // A = X X^T (scaled by 1/(||u||+eps)^2 on the first window)
+  add_group(GG_SYRK, KIND_SYRK, [&](GemmTask& t, const Geom& G, int, int, D& f, D& b, D&) {
+    t.L = t.R0 = t.R1 = ws + G.xm;
+    t.ldl = t.ldr = (int32_t)G.ld_xm;
+    t.K = t.kper = (int)G.Q;
+    t.fbuf = f32(G.a32);
+    const D p = (D)G.p, q = (D)G.q;
+    f += p * (p + 1) * q;
+    b += 4 * p * q + 4 * p * p;
+  });
+  // P = a I + b A + c A^2 (reads A as both operands and for the b A term)
+  for (int g : {GG_P_QA, GG_P_PM})
+    add_group(g, KIND_POLY, [&](GemmTask& t, const Geom& G, int, int, D& f, D& b, D&) {
+      t.L = t.R0 = t.R1 = ws + G.a32;
+      t.fbuf = f32(G.a32);
+      t.out0 = ws + (g == GG_P_QA ? G.qa : G.pm);
+      t.add_diag = 1;
+      const D p = (D)G.p;
+      f += p * p * (p + 1);
+      b += 8 * p * p;
+    });
+  // symmetric products C = L R (all operands commuting polynomials in A)
+  struct Mul { int group; size_t Geom::*l; size_t Geom::*r; size_t Geom::*out; };
+  const Mul muls[] = {{GG_PA_QA, &Geom::qa, &Geom::a32, &Geom::pa},
+                      {GG_PA_PM, &Geom::pm, &Geom::a32, &Geom::pa},
+                      {GG_A_QA, &Geom::qa, &Geom::pa, &Geom::a32},
+                      {GG_A_PM, &Geom::pm, &Geom::pa, &Geom::a32},
+                      {GG_Q_AB, &Geom::pm, &Geom::qa, &Geom::qb},
+                      {GG_Q_BA, &Geom::pm, &Geom::qb, &Geom::qa}};
+  for (const Mul& mu : muls)
+    add_group(mu.group, KIND_GRAMMUL, [&](GemmTask& t, const Geom& G, int, int, D& f, D& b, D&) {
+      t.L = ws + G.*mu.l;
+      t.R0 = t.R1 = ws + G.*mu.r;
+      t.out0 = ws + G.*mu.out;
+      const D p = (D)G.p;
+      f += p * p * (p + 1);
+      b += 12 * p * p;
+    });
+  // X = Q X at a window's end (the X update with a = 0); the last window
+  // writes the caller's matrix
+  for (int g : {GG_QX_QA, GG_QX_QB})
+    add_group(g, KIND_UPDX, [&](GemmTask& t, const Geom& G, int i, int tile, D& f, D& b,
+                                D& bfin) {
+      t.L = ws + (g == GG_QX_QA ? G.qa : G.qb);
+      t.R0 = ws + G.xt0;
+      t.R1 = ws + G.xt1;
+      t.ldl = (int32_t)G.ld_a32;
+      t.ldr = (int32_t)G.ld_xt;
+      t.K = t.kper = (int)G.P;
+      t.tiles_m = (int)G.P / tile;
+      t.tiles_n = (int)G.Q / tile;
+      t.tri = 0;
+      t.tile_count = t.tiles_m * t.tiles_n;
+      t.fbuf = f32(G.xm);
+      t.ld_f = (int32_t)G.ld_xm;
+      t.out1 = ws + G.xt0;
+      t.out2 = ws + G.xt1;
+      t.ld1 = (int32_t)G.ld_xt;
+      t.dst = dst->mats[i].ptr;
+      t.pv = (int32_t)G.p;
+      t.qv = (int32_t)G.q;
+      t.dst_trans = G.transposed;
+      t.dst_dtype = dst->dtype;
+      t.sink = ws + L.sink_off;
+      const D p = (D)G.p, q = (D)G.q;
+      f += 2 * p * p * q;
+      const D in = 4 * p * p + 8 * p * q;  // Q, X^T, and X (read for the a X term)
+      b += in + 8 * p * q;
+      bfin += in + p * q * esize(dst->dtype) * (ns_only ? 1.0 : 2.0);
+    });
+}
+
 // Builds the launch tables for one call shape and uploads them.
 dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_batch_t* dst,
                           const dmuon_batch_t* bufs, bool ns_only, char* ws, int device,
@@ -287,6 +444,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   plan->key = std::move(key);
   plan->device = device;
   plan->f32_ops = L.f32_ops;
+  plan->gram = L.gram;
   const int n = src->count;
   plan->nmat = n;
   float* partial = reinterpret_cast<float*>(ws + L.partial_off);
@@ -333,9 +491,10 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
 
   // GEMM tasks, grouped by (kind, tile class).
   std::vector<GemmTask> gtasks;
-  const int kinds[3] = {KIND_SYRK, KIND_POLY, KIND_UPDX};
+  const int kinds_direct[3] = {KIND_SYRK, KIND_POLY, KIND_UPDX};
   std::vector<std::pair<size_t, size_t>> ranges;  // [begin, end) in gtasks per launch
-  for (int kind : kinds) {
+  if (L.gram) build_gram_groups(L, dst, ns_only, ws, scale, plan.get(), gtasks, ranges);
+  for (int kind : (L.gram ? std::vector<int>() : std::vector<int>(kinds_direct, kinds_direct + 3))) {
     for (int tile : kTiles) {
       const size_t begin = gtasks.size();
       int acc = 0;
@@ -432,7 +591,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
       }
       if (gtasks.size() > begin) {
         GemmLaunch gl{kind, tile, 0, (int)(gtasks.size() - begin), acc, flops, bytes,
-                      kind == KIND_UPDX ? bytes_fin : bytes};
+                      kind == KIND_UPDX ? bytes_fin : bytes, kind};
         plan->gemms.push_back(gl);
         ranges.push_back({begin, gtasks.size()});
       }
@@ -479,6 +638,7 @@ dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_b
   key.push_back(device);
   key.push_back(ns_only);
   key.push_back(L.f32_ops);
+  key.push_back(L.gram);
   key.push_back(src->dtype);
   key.push_back(dst->dtype);
   key.push_back((int64_t)reinterpret_cast<uintptr_t>(ws));
@@ -536,7 +696,8 @@ struct Prof {
 thread_local Prof g_prof;
 
 const char* kKindNames[KIND_COUNT] = {"momentum", "input", "norm", "syrk", "poly",
-                                      "update_x", "clip_norm", "clip_scale", "adamw"};
+                                      "update_x", "clip_norm", "clip_scale", "adamw",
+                                      "gram_mul"};
 
 template <class F>
 hipError_t timed(int kind, double flops, double bytes, hipStream_t s, F&& launch) {
@@ -547,6 +708,70 @@ hipError_t timed(int kind, double flops, double bytes, hipStream_t s, F&& launch
   if (e1) (void)hipEventRecord(e1, s);
   if (e0 && e1) g_prof.recs.push_back({kind, e0, e1, flops, bytes});
   return err;
+}
+
+// Gram-space NS: per restart window, A = X X^T; per step P, then Q <- P Q
+// and A <- P (P A) (not after the window's last step); X <- Q X at the
+// window's end, the last window into the caller's matrix.
+dmuon_status_t run_gram(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, float lr,
+                        float decay, hipStream_t s) {
+  const char* tab = static_cast<const char*>(plan.dtab);
+  auto group = [&](int gid, const IterArgs& args) -> dmuon_status_t {
+    for (const GemmLaunch& gl : plan.gemms) {
+      if (gl.group != gid) continue;
+      const GemmTask* tasks = reinterpret_cast<const GemmTask*>(tab + gl.off);
+      const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
+      const hipError_t e = timed(gl.kind, gl.flops, bytes, s, [&] {
+        return launch_gemm(gl.kind, gl.tile, 1, tasks, gl.ntasks, gl.total, args, s);
+      });
+      if (e != hipSuccess)
+        return fail(DMUON_E_HIP, std::string("Gram NS product launch: ") + hipGetErrorString(e));
+    }
+    return DMUON_OK;
+  };
+  const int n = cfg->ns_steps;
+  std::vector<int> cuts = {0, n};
+  if (cfg->restarts) {
+    for (int i = 0; i < cfg->nrestarts; ++i)
+      if (cfg->restarts[i] > 0 && cfg->restarts[i] < n) cuts.push_back(cfg->restarts[i]);
+  } else if (2 < n) {
+    cuts.push_back(2);  // default restart
+  }
+  std::sort(cuts.begin(), cuts.end());
+  cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+  const int windows = (int)cuts.size() - 1;
+  dmuon_status_t st;
+  for (int w = 0; w < windows; ++w) {
+    IterArgs base{};
+    base.iter = w;  // window 0 applies the 1/(||u||+eps) scaling
+    if ((st = group(GG_SYRK, base))) return st;
+    bool q_in_a = true;  // the window's Q lives in Q_a
+    for (int k = cuts[w]; k < cuts[w + 1]; ++k) {
+      const float* c = cfg->coeffs ? cfg->coeffs + 3 * k : kQuintic;
+      IterArgs pa = base;
+      pa.a = c[0];
+      pa.b = c[1];
+      pa.c = c[2];
+      const bool first = k == cuts[w];
+      if ((st = group(first ? GG_P_QA : GG_P_PM, pa))) return st;
+      if (!first) {
+        if ((st = group(q_in_a ? GG_Q_AB : GG_Q_BA, base))) return st;
+        q_in_a = !q_in_a;
+      }
+      if (k + 1 < cuts[w + 1]) {
+        if ((st = group(first ? GG_PA_QA : GG_PA_PM, base))) return st;
+        if ((st = group(first ? GG_A_QA : GG_A_PM, base))) return st;
+      }
+    }
+    IterArgs qx = base;  // a = 0: X <- s Q X
+    if (w == windows - 1) {
+      qx.fin = ns_only ? FIN_OUTPUT : FIN_UPDATE;
+      qx.lr = lr;
+      qx.decay = decay;
+    }
+    if ((st = group(q_in_a ? GG_QX_QA : GG_QX_QB, qx))) return st;
+  }
+  return DMUON_OK;
 }
 
 dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, float momentum,
@@ -568,6 +793,7 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
                    [&] { return launch_norm(tnorm, plan.nmat, cfg->eps, s); }),
              "norm launch");
   if (st) return st;
+  if (plan.gram) return run_gram(plan, cfg, ns_only, lr, decay, s);
   for (int it = 0; it < cfg->ns_steps; ++it) {
     const float* c = cfg->coeffs ? cfg->coeffs + 3 * it : kQuintic;
     IterArgs args{};
@@ -722,8 +948,9 @@ dmuon_status_t dmuon_ns_workspace_size(const dmuon_batch_t* g, const dmuon_ns_cf
   if (!cfg) return fail(DMUON_E_INVALID, "cfg: null");
   if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_BF16_SPLIT_A)
     return fail(DMUON_E_INVALID, "cfg: unknown precision mode");
+  if ((st = check_backend(cfg))) return st;
   Layout L;
-  st = make_layout(g, cfg->prec, &L);
+  st = make_layout(g, cfg->prec, cfg->backend, &L);
   if (st) return st;
   *bytes = g->count ? L.total : 0;
   return DMUON_OK;
@@ -741,7 +968,7 @@ dmuon_status_t dmuon_ns_orthogonalize(const dmuon_batch_t* g, const dmuon_batch_
   if (g->dtype != out->dtype) return fail(DMUON_E_INVALID, "out dtype must equal g dtype");
   if (g->count == 0) return DMUON_OK;
   Layout L;
-  if ((st = make_layout(g, cfg->prec, &L))) return st;
+  if ((st = make_layout(g, cfg->prec, cfg->backend, &L))) return st;
   if ((st = check_ws(L, ws, ws_bytes))) return st;
   // out[i] may be exactly g[i]; nothing else may overlap.
   std::vector<Span> spans;
@@ -780,7 +1007,7 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t*
     return fail(DMUON_E_INVALID, "momentum, lr and weight_decay must be finite");
   if (params->count == 0) return DMUON_OK;
   Layout L;
-  if ((st = make_layout(grads, cfg->prec, &L))) return st;
+  if ((st = make_layout(grads, cfg->prec, cfg->backend, &L))) return st;
   if ((st = check_ws(L, ws, ws_bytes))) return st;
   std::vector<Span> spans;
   add_spans(spans, params, 0);

@@ -21,6 +21,8 @@ enum Kind : int {
   KIND_CLIP_NORM,     // gradient clipping: norm partials + per-bucket finalize
   KIND_CLIP_SCALE,    // gradient clipping: g <- g * factor
   KIND_ADAMW,         // AdamW update of non-Muon parameters
+  KIND_GRAMMUL,       // Gram-space NS: a product of two commuting symmetric
+                      // p x p matrices (P A, P (P A), P Q), fp32 operands
   KIND_COUNT
 };
 
@@ -87,6 +89,8 @@ struct GemmTask {
   int32_t pv, qv;          // valid oriented extents p x q
   int32_t dst_trans;
   int32_t dst_dtype;
+  int32_t add_diag;        // POLY (Gram-space P): add the iteration's a on the diagonal
+  int32_t pad1_;
 };
 
 // What the UPDX epilogue does with the new X.

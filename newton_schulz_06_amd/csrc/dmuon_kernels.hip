@@ -232,8 +232,9 @@ __device__ __forceinline__ void full_decode(int t, int tiles_m, int tiles_n, int
 // load of that row issued before the first use (no branch in between), so
 // the loads overlap instead of costing one round trip each.
 
-// SYRK (A = s X X^T) and POLY (B = b A + c A A^T) tiles of the upper
-// triangle; off-diagonal tiles are also written mirrored.  AHL: POLY reads
+// SYRK (A = s X X^T), POLY (B = b A + c A A^T, plus a I for Gram-space P)
+// and GRAMMUL (C = L R^T) tiles of the upper triangle; off-diagonal tiles
+// are also written mirrored.  AHL: POLY reads
 // A as hi + lo from the split operand rows instead of the fp32 A.
 template <int KIND, int T, bool F32, int NT, bool AHL>
 __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
@@ -321,9 +322,21 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
               }
             }
           }
+        } else if constexpr (KIND == KIND_GRAMMUL) {
+          // C = L R^T (L, R symmetric and commuting, so C is symmetric)
+          float* o0 = static_cast<float*>(G.out0);
+          const int ld0 = G.ld0;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) st_f32(o0 + (size_t)(gi + rr) * ld0 + gj, v[rr]);
+          if (mirror) st_f32x4(o0 + (size_t)gj * ld0 + gi, v);
         } else {  // KIND_POLY
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(cb, av[j][g][rr], cc * v[rr]);
+          if (G.add_diag) {  // Gram-space P = a I + b A + c A^2
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              if (gi + rr == gj) v[rr] += A.a;
+          }
           if constexpr (F32) {
             float* o0 = static_cast<float*>(G.out0);
             const int ld0 = G.ld0;
@@ -921,6 +934,11 @@ hipError_t launch_gemm(int kind, int tile, int f32_ops, const GemmTask* tasks, i
       return launch_gemm_k<KIND_POLY>(tile, f32_ops, tasks, ntasks, total_tiles, A, s);
     case KIND_UPDX:
       return launch_gemm_k<KIND_UPDX>(tile, f32_ops, tasks, ntasks, total_tiles, A, s);
+    case KIND_GRAMMUL:  // fp32 operands only
+      if (!f32_ops) return hipErrorInvalidValue;
+      if (tile == 64) return launch_gemm_f32<KIND_GRAMMUL, 64>(tasks, ntasks, total_tiles, A, s);
+      if (tile == 128) return launch_gemm_f32<KIND_GRAMMUL, 128>(tasks, ntasks, total_tiles, A, s);
+      return hipErrorInvalidValue;
     default:
       return hipErrorInvalidValue;
   }

@@ -104,6 +104,24 @@ def _expected_ws(shapes, prec):
     return a(4 * tiles) + a(16 * len(shapes)) + a(16) + sum(per)
 
 
+def test_workspace_size_gram():
+    """Gram-space layout (fp32 operands): partials, scales, sink, then per
+    matrix fp32 X, two fp32 X^T, and five fp32 P x P buffers (A, P, P A and
+    the Q pair)."""
+    a = lambda x: _pad(x, 256)  # noqa: E731
+    shapes = [(1024, 256), (256, 1024), (100, 37), (700, 900)]
+    tiles, per = 0, 0
+    for m, n in shapes:
+        p, q = min(m, n), max(m, n)
+        t = _tile(p, "f32")
+        P, Q = _pad(p, t), _pad(q, t)
+        tiles += (P // 64) * (Q // 64)
+        per += a(4 * P * _ld(Q, 4)) + 2 * a(4 * Q * _ld(P, 4)) + 5 * a(4 * P * _ld(P, 4))
+    want = a(4 * tiles) + a(16 * len(shapes)) + a(16) + per
+    for prec in ("f32", "auto"):
+        assert dm.workspace_size(shapes, prec, backend="gram") == want
+
+
 @pytest.mark.parametrize("prec", ["f32", "bf16", "bf16_split", "auto", "bf16_split_a"])
 def test_workspace_size(prec):
     shapes = [(1024, 256), (256, 1024), (100, 37), (4096, 14336), (32, 480), (544, 800),
@@ -134,6 +152,31 @@ def _call_step(p, g, b, cfg, mu=0.95, lr=0.02, wd=0.0, ws=FAKE_WS, ws_bytes=1 <<
 
 def _err():
     return dm.lib().dmuon_last_error().decode()
+
+
+_KEEP = []
+
+
+def _keep_cfg(**kw):
+    cfg, keep = dm.make_cfg(**kw)
+    _KEEP.append(keep)
+    return cfg
+
+
+def _cfg_with(**fields):
+    cfg = _keep_cfg(prec="f32", backend="gram")
+    for k, v in fields.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+def test_gram_needs_fp32_operands():
+    g, k1 = _mats([(64, 96, FAKE_G)])
+    o, k2 = _mats([(64, 96, FAKE_O)])
+    for prec in ("bf16", "bf16_split", "bf16_split_a"):
+        cfg = _keep_cfg(prec=prec, backend="gram")
+        assert _call_ns(g, o, cfg) == dm.DMUON_E_UNSUPPORTED, _err()
+        assert "fp32" in _err()
 
 
 def test_valid_call_reaches_the_device():
@@ -192,6 +235,14 @@ NS_BAD = {
                               dm.make_cfg(prec=9)[0], {}),
     "partial overlap": lambda: (_mats([(4, 4, FAKE_G)])[0], _mats([(4, 4, FAKE_G + 16)])[0],
                                 dm.make_cfg()[0], {}),
+    "unknown backend": lambda: (_mats([(4, 4, FAKE_G)])[0], _mats([(4, 4, FAKE_O)])[0],
+                                dm.make_cfg(backend=7)[0], {}),
+    "negative restart": lambda: (_mats([(4, 4, FAKE_G)])[0], _mats([(4, 4, FAKE_O)])[0],
+                                 _keep_cfg(prec="f32", backend="gram",
+                                           restart_iterations=[2, -1]), {}),
+    "restarts count without list": lambda: (_mats([(4, 4, FAKE_G)])[0],
+                                            _mats([(4, 4, FAKE_O)])[0],
+                                            _cfg_with(nrestarts=2), {}),
     "two inputs overlap": lambda: (_mats([(4, 4, FAKE_G), (4, 4, FAKE_G + 32)])[0],
                                    _mats([(4, 4, FAKE_O), (4, 4, FAKE_O + 4096)])[0],
                                    dm.make_cfg()[0], {}),
