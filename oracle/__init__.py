@@ -21,6 +21,7 @@ from .muon_ref import (  # noqa: F401
     gram_windows,
     gram_newton_schulz_factors,
     gram_newton_schulz,
+    gram_newton_schulz_distributed_local,
     muon_step,
     round_to_bf16,
 )

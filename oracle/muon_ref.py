@@ -36,7 +36,20 @@ documentation pages; readings of unstated points are marked READING):
    window's end X <- Q X_s.  A restart at step r starts a new window there
    (restart indices outside 1..steps-1 have no effect).  Exactly equal to
    step 4 in exact arithmetic.
-6. update (DMuon "HSDP Training (Multi-Node)", "What Happens Under the Hood":
+6. Gram-space NS on a local shard (DMuon "API Reference",
+   ``gram_newton_schulz_distributed_local`` and its ``_batched`` variant:
+   orientation comes from the full logical matrix through the
+   ``transposed`` argument; the oriented local block is a column block of
+   the full oriented matrix; only the small Gram matrix is rebuilt by an
+   all-reduce over the shard group; each rank gets its block of the full
+   output and momentum / scaling / weight decay stay with the caller).
+   READING: the Frobenius norm is needed before the first Gram factor and
+   is also a sum over the shards, so it is reduced too; every reduction is
+   a plain sum over the group, and each restart window reduces the Gram
+   matrix of the current X once.  The oracle stands for the whole group at
+   once: it takes every rank's block and writes each all-reduce as a sum
+   over the list.
+7. update (DMuon "HSDP Training (Multi-Node)", "What Happens Under the Hood":
    the owner runs NS + momentum + weight decay + update; "API Reference",
    ``Muon`` signature: lr=0.02, momentum=0.95, weight_decay=0.0).
    READING: decoupled weight decay ``p <- p - lr*wd*p - lr*O`` on the
@@ -213,6 +226,39 @@ def gram_newton_schulz(G, steps: int = 5, eps: float = DEFAULT_EPS, coefficients
     for Q in segments:
         X = Q @ X
     return X.T if transposed else X
+
+
+def gram_newton_schulz_distributed_local(shards, transposed: bool, steps: int = 5,
+                                         eps: float = DEFAULT_EPS, coefficients=None,
+                                         restart_iterations=None):
+    """Gram-space NS of a matrix held as column shards of its oriented view
+    (DMuon "API Reference", ``gram_newton_schulz_distributed_local``;
+    READING 6 in the header).
+
+    ``shards`` lists every rank's local block in the stored layout; with
+    ``transposed`` its transpose is the rank's column block X_r (p x q_r) of
+    the oriented matrix, else the block itself is.  Every rank's result is
+    returned, each in its block's layout, float64.
+    """
+    table = coefficient_table(coefficients, steps)
+    blocks = [np.asarray(g, dtype=np.float64) for g in shards]
+    Xs = [B.T if transposed else B for B in blocks]
+    p = Xs[0].shape[0]
+    if any(X.shape[0] != p for X in Xs):
+        raise ValueError("every oriented shard has the full matrix's p rows")
+    # all-reduce of the squared norm, then every rank scales its block
+    normalizer = np.sqrt(sum(float(np.sum(X * X)) for X in Xs)) + eps
+    Xs = [X / normalizer for X in Xs]
+    for s, e in gram_windows(len(table), restart_iterations):
+        A = sum(X @ X.T for X in Xs)  # all-reduce of the local Gram matrices
+        Q = np.eye(p)
+        for k in range(s, e):
+            a, b, c = table[k]
+            P = a * np.eye(p) + b * A + c * (A @ A)
+            Q = P @ Q
+            A = P @ A @ P
+        Xs = [Q @ X for X in Xs]
+    return [X.T if transposed else X for X in Xs]
 
 
 def muon_step(param, grad, buf, *, lr: float = 0.02, momentum: float = 0.95,
