@@ -175,6 +175,60 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params,
                                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Gram-space NS of matrices held as column shards of their oriented view
+ * (DMuon "API Reference", gram_newton_schulz_distributed_local and its
+ * batched variant: the shard group rebuilds only the small Gram matrix by
+ * an all-reduce, and each rank gets its own block of the full NS output).
+ *
+ * g[i] is this rank's block of matrix i in the stored layout.  transposed
+ * (0 or 1, one flag for the batch) is the FULL matrix's orientation: when 1,
+ * g[i]^T is the block of the oriented matrix, so p = g[i].n and the block's
+ * width is g[i].m; when 0, p = g[i].m.  Every rank of a group passes the same
+ * flag, the same p per matrix and the same batch order; block widths may
+ * differ.  cfg->backend must be DMUON_NS_GRAM (prec F32 or AUTO).
+ *
+ * The sums over the group are the caller's: the library keeps them in one
+ * fp32 "bucket" inside the workspace (every matrix's sum of squares, then
+ * every p x p Gram matrix, padded; see dmuon_gram_local_bucket), and the
+ * caller sums it in place over the group (e.g. an all-reduce enqueued on
+ * the same stream) between the calls:
+ *
+ *   dmuon_gram_local_begin(...)                     bucket <- local sums
+ *   for w in 0 .. windows-1:
+ *     <sum the bucket over the group, in place>
+ *     dmuon_gram_local_advance(..., w, ...)          w < windows-1: bucket <-
+ *                                                    local sums for w+1;
+ *                                                    last: out <- result
+ *
+ * With one rank (or no sum) the block is the whole matrix and the result is
+ * dmuon_ns_orthogonalize's with the Gram backend.  The state between calls
+ * lives in the workspace: keep ws, g, out and cfg the same through one
+ * sequence and do not start another on the same workspace before it ends
+ * (a wrong order gives wrong values, never an out-of-bounds access).
+ * Momentum, the lr and weight decay stay with the caller (as on the pages).
+ * out may be exactly g (it is written by the last advance only).
+ */
+dmuon_status_t dmuon_gram_local_workspace_size(const dmuon_batch_t* g, int32_t transposed,
+                                               const dmuon_ns_cfg_t* cfg, size_t* bytes);
+
+/* Where the bucket lies: `count` floats at byte `offset` of the workspace
+ * (256-byte aligned), and the number of restart windows (sums per call
+ * sequence).  Only shapes, transposed and cfg are read. */
+dmuon_status_t dmuon_gram_local_bucket(const dmuon_batch_t* g, int32_t transposed,
+                                       const dmuon_ns_cfg_t* cfg, size_t* offset,
+                                       int64_t* count, int32_t* windows);
+
+dmuon_status_t dmuon_gram_local_begin(const dmuon_batch_t* g, const dmuon_batch_t* out,
+                                      int32_t transposed, const dmuon_ns_cfg_t* cfg,
+                                      void* ws, size_t ws_bytes, void* stream);
+
+/* window: 0 .. windows-1, in order; anything else is DMUON_E_INVALID. */
+dmuon_status_t dmuon_gram_local_advance(const dmuon_batch_t* g, const dmuon_batch_t* out,
+                                        int32_t transposed, const dmuon_ns_cfg_t* cfg,
+                                        int32_t window, void* ws, size_t ws_bytes,
+                                        void* stream);
+
+/*
  * Gradient-norm clipping of Muon gradients (DMuon "API Reference",
  * clip_grad_norm_: only DMuon's Muon gradients, norm_type 2.0 by default,
  * the stats of MuonGradClipStats; clip_grad_norm_buckets_: every bucket

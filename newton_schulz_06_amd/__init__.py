@@ -61,6 +61,8 @@ class ClipStats(ctypes.Structure):
 
 
 EXPORTS = ("dmuon_ns_workspace_size", "dmuon_ns_orthogonalize", "dmuon_muon_step",
+           "dmuon_gram_local_workspace_size", "dmuon_gram_local_bucket",
+           "dmuon_gram_local_begin", "dmuon_gram_local_advance",
            "dmuon_clip_workspace_size", "dmuon_clip_grad_norm", "dmuon_adamw_step",
            "dmuon_status_str", "dmuon_last_error", "dmuon_backend_info",
            "dmuon_profile_begin", "dmuon_profile_end")
@@ -91,6 +93,24 @@ def lib():
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p]
     L.dmuon_muon_step.restype = st
+    L.dmuon_gram_local_workspace_size.argtypes = [ctypes.POINTER(Batch), ctypes.c_int32,
+                                                  ctypes.POINTER(NsCfg),
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+    L.dmuon_gram_local_workspace_size.restype = st
+    L.dmuon_gram_local_bucket.argtypes = [ctypes.POINTER(Batch), ctypes.c_int32,
+                                          ctypes.POINTER(NsCfg), ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int32)]
+    L.dmuon_gram_local_bucket.restype = st
+    L.dmuon_gram_local_begin.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(Batch),
+                                         ctypes.c_int32, ctypes.POINTER(NsCfg), ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]
+    L.dmuon_gram_local_begin.restype = st
+    L.dmuon_gram_local_advance.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(Batch),
+                                           ctypes.c_int32, ctypes.POINTER(NsCfg),
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]
+    L.dmuon_gram_local_advance.restype = st
     L.dmuon_clip_workspace_size.argtypes = [ctypes.POINTER(Batch), ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_size_t)]
     L.dmuon_clip_workspace_size.restype = st
@@ -365,6 +385,94 @@ class PreparedNs:
                      self.wptr, self.wbytes, self.stream)
         if st:
             _check(st)
+
+
+# --------------------------------------------- Gram-space NS on shards --
+
+def gram_local_workspace_size(shapes, transposed, prec="f32") -> int:
+    """dmuon_gram_local_workspace_size for blocks of these (m, n) shapes."""
+    b, keep = shape_batch(shapes)
+    cfg, ck = make_cfg(prec=prec, backend="gram")
+    out = ctypes.c_size_t(0)
+    _check(lib().dmuon_gram_local_workspace_size(ctypes.byref(b), int(transposed),
+                                                 ctypes.byref(cfg), ctypes.byref(out)))
+    return int(out.value)
+
+
+def gram_local_bucket(shapes, transposed, *, coefficients=None, ns_steps=5, prec="f32",
+                      restart_iterations=None):
+    """dmuon_gram_local_bucket: (byte offset, float count, windows)."""
+    b, keep = shape_batch(shapes)
+    cfg, ck = make_cfg(coefficients, ns_steps, 1e-7, prec, "gram", restart_iterations)
+    off, cnt, win = ctypes.c_size_t(0), ctypes.c_int64(0), ctypes.c_int32(0)
+    _check(lib().dmuon_gram_local_bucket(ctypes.byref(b), int(transposed), ctypes.byref(cfg),
+                                         ctypes.byref(off), ctypes.byref(cnt), ctypes.byref(win)))
+    return int(off.value), int(cnt.value), int(win.value)
+
+
+class GramLocal:
+    """dmuon_gram_local_begin / dmuon_gram_local_advance on fixed buffers:
+    Gram-space NS of this rank's blocks (DMuon "API Reference",
+    gram_newton_schulz_distributed_local, batched).  ``bucket`` is a float32
+    view of the workspace that must be summed over the shard group before
+    each ``advance``; ``__call__`` runs the whole sequence with an optional
+    ``all_reduce(bucket)`` (None: one rank, the block is the whole matrix)."""
+
+    def __init__(self, g_locals, outs, *, transposed, coefficients=None, ns_steps=5, eps=1e-7,
+                 prec="f32", restart_iterations=None, workspace=None, stream=None):
+        import torch
+        self.bg, self._kg = make_batch(g_locals)
+        self.bo, self._ko = make_batch(outs)
+        self.transposed = int(bool(transposed))
+        self.cfg, self._kc = make_cfg(coefficients, ns_steps, eps, prec, "gram",
+                                      restart_iterations)
+        shapes = [tuple(g.shape) for g in g_locals]
+        if workspace is None:
+            device = g_locals[0].device if g_locals else "cuda"
+            workspace = torch.empty(max(1, gram_local_workspace_size(shapes, transposed, prec)),
+                                    dtype=torch.uint8, device=device)
+        self.ws = workspace
+        self.wptr = ctypes.c_void_p(int(workspace.data_ptr()))
+        self.wbytes = int(workspace.numel())
+        off, cnt, self.windows = gram_local_bucket(
+            shapes, transposed, coefficients=coefficients, ns_steps=ns_steps, prec=prec,
+            restart_iterations=restart_iterations)
+        self.bucket = workspace[off:off + 4 * cnt].view(torch.float32)
+        self.stream = _stream_handle(stream)
+        self.L = lib()
+
+    def begin(self):
+        _check(self.L.dmuon_gram_local_begin(ctypes.byref(self.bg), ctypes.byref(self.bo),
+                                             self.transposed, ctypes.byref(self.cfg), self.wptr,
+                                             self.wbytes, self.stream))
+
+    def advance(self, window):
+        _check(self.L.dmuon_gram_local_advance(ctypes.byref(self.bg), ctypes.byref(self.bo),
+                                               self.transposed, ctypes.byref(self.cfg),
+                                               int(window), self.wptr, self.wbytes,
+                                               self.stream))
+
+    def __call__(self, all_reduce=None):
+        self.begin()
+        for w in range(self.windows):
+            if all_reduce is not None:
+                all_reduce(self.bucket)
+            self.advance(w)
+
+
+def gram_ns_distributed_local(g_locals, outs=None, *, transposed, all_reduce=None,
+                              coefficients=None, ns_steps=5, eps=1e-7, prec="f32",
+                              restart_iterations=None, workspace=None, stream=None):
+    """Gram-space NS of this rank's column blocks (see :class:`GramLocal`);
+    returns ``outs`` (new tensors by default; ``outs=g_locals`` works in
+    place)."""
+    import torch
+    g_locals = list(g_locals)
+    outs = [torch.empty_like(g) for g in g_locals] if outs is None else list(outs)
+    GramLocal(g_locals, outs, transposed=transposed, coefficients=coefficients,
+              ns_steps=ns_steps, eps=eps, prec=prec, restart_iterations=restart_iterations,
+              workspace=workspace, stream=stream)(all_reduce)
+    return outs
 
 
 # ------------------------------------------------- element-wise companions --

@@ -82,11 +82,21 @@ struct Layout {
   int64_t in_tiles = 0;
   int f32_ops = 0;
   int gram = 0;  // Gram-space NS layout (fp32 operands)
+  // Gram NS on column shards: every matrix's sum of squares (one float
+  // each, padded to kWsAlign), then every fp32 Gram matrix back to back, so
+  // one in-place sum over the shard group covers the whole batch.
+  int local = 0;
+  size_t bucket_off = 0, bucket_bytes = 0;
 };
 
-dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout* out) {
+// `orient` < 0: transpose iff m > n; 0 / 1 force it (a shard takes the full
+// matrix's orientation, so its p may exceed its q).  `local`: the shard
+// layout (Gram backend only).
+dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout* out,
+                           int orient = -1, bool local = false) {
   Layout L;
   L.gram = backend == DMUON_NS_GRAM;
+  L.local = local;
   L.f32_ops = (prec == DMUON_NS_F32) || L.gram;
   const int n = b->count;
   L.g.resize(n);
@@ -95,9 +105,9 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
     Geom& G = L.g[i];
     G.m = b->mats[i].m;
     G.n = b->mats[i].n;
-    G.transposed = G.m > G.n;
-    G.p = std::min(G.m, G.n);
-    G.q = std::max(G.m, G.n);
+    G.transposed = orient < 0 ? G.m > G.n : orient;
+    G.p = G.transposed ? G.n : G.m;
+    G.q = G.transposed ? G.m : G.n;
     G.tile = tile_class(G.p, L.f32_ops != 0);
     G.P = round_up(G.p, G.tile);
     G.Q = round_up(G.q, G.tile);
@@ -121,6 +131,17 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
   off = align_up(off + sizeof(float) * 4 * (size_t)n, kWsAlign);
   L.sink_off = off;  // writable bytes nothing reads (padding lanes' stores)
   off = align_up(off + 16, kWsAlign);
+  if (L.local) {
+    L.bucket_off = off;
+    off = align_up(off + sizeof(float) * (size_t)n, kWsAlign);
+    for (int i = 0; i < n; ++i) {  // whole multiples of kWsAlign: no gaps
+      Geom& G = L.g[i];
+      G.ld_a32 = ld_for(G.P, 4);
+      G.a32 = off;
+      off = align_up(off + 4 * (size_t)G.P * G.ld_a32, kWsAlign);
+    }
+    L.bucket_bytes = off - L.bucket_off;
+  }
   const int64_t e = L.f32_ops ? 4 : 2;
   for (int i = 0; i < n; ++i) {
     Geom& G = L.g[i];
@@ -134,7 +155,8 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
     G.ld_xb = ld_for(G.Q, 2);
     G.ld_xt = ld_for(G.P, e);
     G.ld_a32 = ld_for(G.P, 4);
-    G.xm = G.xb = G.xlo = G.a32 = 0;
+    G.xm = G.xb = G.xlo = 0;
+    if (!L.local) G.a32 = 0;
     // Same rule as the kernels' kHiLoMaster: tiles below 256.
     G.hilo = !L.f32_ops && G.tile < 256;
     if (!G.hilo) G.xm = take(4 * P * G.ld_xm);       // fp32 X
@@ -142,7 +164,7 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
     if (G.hilo) G.xlo = take(2 * P * G.ld_xb);       // bf16 (X - bf16 X)
     G.xt0 = take(e * Q * G.ld_xt);
     G.xt1 = take(e * Q * G.ld_xt);
-    if (L.f32_ops || !G.split_a) G.a32 = take(4 * P * G.ld_a32);
+    if (!L.local && (L.f32_ops || !G.split_a)) G.a32 = take(4 * P * G.ld_a32);
     G.pm = G.pa = G.qa = G.qb = 0;
     if (L.gram) {
       G.aop = G.a32;
@@ -298,9 +320,10 @@ struct Plan {
   void* dtab = nullptr;
   int f32_ops = 0;
   int gram = 0;
-  size_t in_off = 0, norm_off = 0;
-  int nmat = 0, in_tiles = 0;
-  double in_bytes = 0, norm_bytes = 0;
+  int local = 0;
+  size_t in_off = 0, norm_off = 0, fin_off = 0;
+  int nmat = 0, in_tiles = 0, fin_blocks = 0;
+  double in_bytes = 0, norm_bytes = 0, fin_bytes = 0;
   std::vector<GemmLaunch> gemms;  // SYRK launches, then POLY, then UPDX
   ~Plan() {
     if (dtab) {
@@ -445,6 +468,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   plan->device = device;
   plan->f32_ops = L.f32_ops;
   plan->gram = L.gram;
+  plan->local = L.local;
   const int n = src->count;
   plan->nmat = n;
   float* partial = reinterpret_cast<float*>(ws + L.partial_off);
@@ -482,12 +506,27 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
     a.vec = vec_ok(t.src, src->dtype, G.n) && (!bufs || vec_ok(t.buf, DMUON_F32, G.n));
     in_begin += a.tile_count;
     tin[i] = a;
-    tnorm[i] = NormTask{a.tile_begin, a.tile_count, partial, scale + 4 * i};
+    tnorm[i] = NormTask{a.tile_begin, a.tile_count, partial, scale + 4 * i,
+                        L.local ? reinterpret_cast<float*>(ws + L.bucket_off) + i : nullptr};
     const double mn = (double)G.m * (double)G.n;
     plan->in_bytes += ns_only ? mn * esize(src->dtype) : mn * (esize(src->dtype) + 8.0);
     plan->norm_bytes += 4.0 * a.tile_count;
   }
   plan->in_tiles = in_begin;
+  std::vector<FinTask> tfin;
+  if (L.local) {
+    int blk = 0;
+    for (int i = 0; i < n; ++i) {
+      const Geom& G = L.g[i];
+      const int nb = (int)((G.P + FIN_ROWS - 1) / FIN_ROWS);
+      tfin.push_back(FinTask{blk, nb, (int32_t)G.P, (int32_t)G.ld_a32,
+                             reinterpret_cast<float*>(ws + G.a32),
+                             reinterpret_cast<float*>(ws + L.bucket_off) + i, scale + 4 * i});
+      blk += nb;
+      plan->fin_bytes += 8.0 * (double)G.p * (double)G.p;
+    }
+    plan->fin_blocks = blk;
+  }
 
   // GEMM tasks, grouped by (kind, tile class).
   std::vector<GemmTask> gtasks;
@@ -607,12 +646,15 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   };
   plan->in_off = place(sizeof(EwTask) * n);
   plan->norm_off = place(sizeof(NormTask) * n);
+  plan->fin_off = place(sizeof(FinTask) * tfin.size());
   const size_t g_off = place(sizeof(GemmTask) * gtasks.size());
   for (size_t k = 0; k < plan->gemms.size(); ++k)
     plan->gemms[k].off = g_off + sizeof(GemmTask) * ranges[k].first;
   std::vector<char> host(off);
   std::memcpy(host.data() + plan->in_off, tin.data(), sizeof(EwTask) * n);
   std::memcpy(host.data() + plan->norm_off, tnorm.data(), sizeof(NormTask) * n);
+  if (!tfin.empty())
+    std::memcpy(host.data() + plan->fin_off, tfin.data(), sizeof(FinTask) * tfin.size());
   if (!gtasks.empty())
     std::memcpy(host.data() + g_off, gtasks.data(), sizeof(GemmTask) * gtasks.size());
   hipError_t e = hipMalloc(&plan->dtab, off);
@@ -639,6 +681,7 @@ dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_b
   key.push_back(ns_only);
   key.push_back(L.f32_ops);
   key.push_back(L.gram);
+  key.push_back(L.local);
   key.push_back(src->dtype);
   key.push_back(dst->dtype);
   key.push_back((int64_t)reinterpret_cast<uintptr_t>(ws));
@@ -649,7 +692,7 @@ dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_b
     key.push_back((int64_t)reinterpret_cast<uintptr_t>(src->mats[i].ptr));
     key.push_back((int64_t)reinterpret_cast<uintptr_t>(dst->mats[i].ptr));
     key.push_back(bufs ? (int64_t)reinterpret_cast<uintptr_t>(bufs->mats[i].ptr) : 0);
-    key.push_back(L.g[i].split_a + 2 * L.g[i].split_b);
+    key.push_back(L.g[i].split_a + 2 * L.g[i].split_b + 4 * L.g[i].transposed);
   }
   for (size_t k = 0; k < g_plans.size(); ++k) {
     if (g_plans[k]->key == key) {
@@ -710,25 +753,8 @@ hipError_t timed(int kind, double flops, double bytes, hipStream_t s, F&& launch
   return err;
 }
 
-// Gram-space NS: per restart window, A = X X^T; per step P, then Q <- P Q
-// and A <- P (P A) (not after the window's last step); X <- Q X at the
-// window's end, the last window into the caller's matrix.
-dmuon_status_t run_gram(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, float lr,
-                        float decay, hipStream_t s) {
-  const char* tab = static_cast<const char*>(plan.dtab);
-  auto group = [&](int gid, const IterArgs& args) -> dmuon_status_t {
-    for (const GemmLaunch& gl : plan.gemms) {
-      if (gl.group != gid) continue;
-      const GemmTask* tasks = reinterpret_cast<const GemmTask*>(tab + gl.off);
-      const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
-      const hipError_t e = timed(gl.kind, gl.flops, bytes, s, [&] {
-        return launch_gemm(gl.kind, gl.tile, 1, tasks, gl.ntasks, gl.total, args, s);
-      });
-      if (e != hipSuccess)
-        return fail(DMUON_E_HIP, std::string("Gram NS product launch: ") + hipGetErrorString(e));
-    }
-    return DMUON_OK;
-  };
+// Step indices where Gram-space NS windows start, plus ns_steps at the end.
+std::vector<int> gram_cuts(const dmuon_ns_cfg_t* cfg) {
   const int n = cfg->ns_steps;
   std::vector<int> cuts = {0, n};
   if (cfg->restarts) {
@@ -739,37 +765,77 @@ dmuon_status_t run_gram(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_onl
   }
   std::sort(cuts.begin(), cuts.end());
   cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+  return cuts;
+}
+
+// Launches every group `gid` of a Gram-space plan.
+dmuon_status_t gram_group(const Plan& plan, int gid, const IterArgs& args, hipStream_t s) {
+  const char* tab = static_cast<const char*>(plan.dtab);
+  for (const GemmLaunch& gl : plan.gemms) {
+    if (gl.group != gid) continue;
+    const GemmTask* tasks = reinterpret_cast<const GemmTask*>(tab + gl.off);
+    const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
+    const hipError_t e = timed(gl.kind, gl.flops, bytes, s, [&] {
+      return launch_gemm(gl.kind, gl.tile, 1, tasks, gl.ntasks, gl.total, args, s);
+    });
+    if (e != hipSuccess)
+      return fail(DMUON_E_HIP, std::string("Gram NS product launch: ") + hipGetErrorString(e));
+  }
+  return DMUON_OK;
+}
+
+// A = X X^T at the start of window w (window 0 scales by 1/(||u||+eps)^2
+// through the norm's scale, which is 1 for a shard until the group sum).
+dmuon_status_t gram_syrk(const Plan& plan, int w, hipStream_t s) {
+  IterArgs base{};
+  base.iter = w;
+  return gram_group(plan, GG_SYRK, base, s);
+}
+
+// The steps of window w on its A: per step P, then Q <- P Q and A <- P (P A)
+// (not after the window's last step); then X <- Q X, which on the last
+// window writes the caller's matrix (`fin`).
+dmuon_status_t gram_window(const Plan& plan, const dmuon_ns_cfg_t* cfg,
+                           const std::vector<int>& cuts, int w, int fin, float lr, float decay,
+                           hipStream_t s) {
+  IterArgs base{};
+  base.iter = w;  // window 0's X update applies 1/(||u||+eps); X^T ping-pong
+  dmuon_status_t st;
+  bool q_in_a = true;  // the window's Q lives in Q_a
+  for (int k = cuts[w]; k < cuts[w + 1]; ++k) {
+    const float* c = cfg->coeffs ? cfg->coeffs + 3 * k : kQuintic;
+    IterArgs pa = base;
+    pa.a = c[0];
+    pa.b = c[1];
+    pa.c = c[2];
+    const bool first = k == cuts[w];
+    if ((st = gram_group(plan, first ? GG_P_QA : GG_P_PM, pa, s))) return st;
+    if (!first) {
+      if ((st = gram_group(plan, q_in_a ? GG_Q_AB : GG_Q_BA, base, s))) return st;
+      q_in_a = !q_in_a;
+    }
+    if (k + 1 < cuts[w + 1]) {
+      if ((st = gram_group(plan, first ? GG_PA_QA : GG_PA_PM, base, s))) return st;
+      if ((st = gram_group(plan, first ? GG_A_QA : GG_A_PM, base, s))) return st;
+    }
+  }
+  IterArgs qx = base;  // a = 0: X <- s Q X
+  qx.fin = fin;
+  qx.lr = lr;
+  qx.decay = decay;
+  return gram_group(plan, q_in_a ? GG_QX_QA : GG_QX_QB, qx, s);
+}
+
+// Gram-space NS on whole matrices: every window in turn.
+dmuon_status_t run_gram(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, float lr,
+                        float decay, hipStream_t s) {
+  const std::vector<int> cuts = gram_cuts(cfg);
   const int windows = (int)cuts.size() - 1;
   dmuon_status_t st;
   for (int w = 0; w < windows; ++w) {
-    IterArgs base{};
-    base.iter = w;  // window 0 applies the 1/(||u||+eps) scaling
-    if ((st = group(GG_SYRK, base))) return st;
-    bool q_in_a = true;  // the window's Q lives in Q_a
-    for (int k = cuts[w]; k < cuts[w + 1]; ++k) {
-      const float* c = cfg->coeffs ? cfg->coeffs + 3 * k : kQuintic;
-      IterArgs pa = base;
-      pa.a = c[0];
-      pa.b = c[1];
-      pa.c = c[2];
-      const bool first = k == cuts[w];
-      if ((st = group(first ? GG_P_QA : GG_P_PM, pa))) return st;
-      if (!first) {
-        if ((st = group(q_in_a ? GG_Q_AB : GG_Q_BA, base))) return st;
-        q_in_a = !q_in_a;
-      }
-      if (k + 1 < cuts[w + 1]) {
-        if ((st = group(first ? GG_PA_QA : GG_PA_PM, base))) return st;
-        if ((st = group(first ? GG_A_QA : GG_A_PM, base))) return st;
-      }
-    }
-    IterArgs qx = base;  // a = 0: X <- s Q X
-    if (w == windows - 1) {
-      qx.fin = ns_only ? FIN_OUTPUT : FIN_UPDATE;
-      qx.lr = lr;
-      qx.decay = decay;
-    }
-    if ((st = group(q_in_a ? GG_QX_QA : GG_QX_QB, qx))) return st;
+    if ((st = gram_syrk(plan, w, s))) return st;
+    const int fin = w == windows - 1 ? (ns_only ? FIN_OUTPUT : FIN_UPDATE) : FIN_NONE;
+    if ((st = gram_window(plan, cfg, cuts, w, fin, lr, decay, s))) return st;
   }
   return DMUON_OK;
 }
@@ -793,6 +859,8 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
                    [&] { return launch_norm(tnorm, plan.nmat, cfg->eps, s); }),
              "norm launch");
   if (st) return st;
+  // a shard stops at its first partial Gram matrix: the group sums come next
+  if (plan.local) return gram_syrk(plan, 0, s);
   if (plan.gram) return run_gram(plan, cfg, ns_only, lr, decay, s);
   for (int it = 0; it < cfg->ns_steps; ++it) {
     const float* c = cfg->coeffs ? cfg->coeffs + 3 * it : kQuintic;
@@ -820,6 +888,29 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
     }
   }
   return DMUON_OK;
+}
+
+// Gram NS on a shard, window w, once the bucket holds the group's sums:
+// (window 0) the normalization, the window's steps and X <- Q X, then the
+// next window's partial Gram matrix, or (last window) the output.
+dmuon_status_t run_local_advance(const Plan& plan, const dmuon_ns_cfg_t* cfg, int w,
+                                 hipStream_t s) {
+  const std::vector<int> cuts = gram_cuts(cfg);
+  const int windows = (int)cuts.size() - 1;
+  dmuon_status_t st;
+  if (w == 0) {
+    const FinTask* tfin =
+        reinterpret_cast<const FinTask*>(static_cast<const char*>(plan.dtab) + plan.fin_off);
+    const hipError_t e = timed(KIND_NORM, 0, plan.fin_bytes, s, [&] {
+      return launch_gram_finalize(tfin, plan.nmat, plan.fin_blocks, cfg->eps, s);
+    });
+    if (e != hipSuccess)
+      return fail(DMUON_E_HIP, std::string("Gram finalize launch: ") + hipGetErrorString(e));
+  }
+  const bool last = w == windows - 1;
+  if ((st = gram_window(plan, cfg, cuts, w, last ? FIN_OUTPUT : FIN_NONE, 0.f, 1.f, s)))
+    return st;
+  return last ? DMUON_OK : gram_syrk(plan, w + 1, s);
 }
 
 dmuon_status_t check_ws(const Layout& L, void* ws, size_t ws_bytes) {
@@ -929,6 +1020,44 @@ size_t clip_ws_bytes(int nblocks, int nbuckets) {
          align_up(sizeof(float) * (size_t)nbuckets, kWsAlign);
 }
 
+// Gram NS on shards: the flag and backend checks shared by every entry point.
+dmuon_status_t check_local(const dmuon_ns_cfg_t* cfg, int32_t transposed) {
+  if (transposed != 0 && transposed != 1) return fail(DMUON_E_INVALID, "transposed must be 0 or 1");
+  if (!cfg) return fail(DMUON_E_INVALID, "cfg: null");
+  if (cfg->backend != DMUON_NS_GRAM)
+    return fail(DMUON_E_INVALID, "cfg: the shard entry points run Gram-space NS "
+                                 "(backend DMUON_NS_GRAM)");
+  return DMUON_OK;
+}
+
+// Validation and layout of a begin / advance call (the shapes, pointers and
+// workspace are those of dmuon_ns_orthogonalize).
+dmuon_status_t local_setup(const dmuon_batch_t* g, const dmuon_batch_t* out, int32_t transposed,
+                           const dmuon_ns_cfg_t* cfg, void* ws, size_t ws_bytes, Layout* L) {
+  dmuon_status_t st = check_local(cfg, transposed);
+  if (st) return st;
+  if ((st = check_batch(g, "g", true))) return st;
+  if ((st = check_batch(out, "out", true))) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = same_shapes(g, out, "g", "out"))) return st;
+  if (g->dtype != out->dtype) return fail(DMUON_E_INVALID, "out dtype must equal g dtype");
+  if (g->count == 0) return DMUON_OK;
+  if ((st = make_layout(g, cfg->prec, cfg->backend, L, transposed, true))) return st;
+  if ((st = check_ws(*L, ws, ws_bytes))) return st;
+  std::vector<Span> spans;
+  add_spans(spans, g, 0);
+  for (int i = 0; i < out->count; ++i)
+    if (out->mats[i].ptr != g->mats[i].ptr) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(out->mats[i].ptr);
+      spans.push_back({lo, lo + (uintptr_t)(out->mats[i].m * out->mats[i].n * esize(out->dtype)),
+                       1, i});
+    }
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(ws);
+  spans.push_back({wlo, wlo + L->total, 2, 0});
+  static const char* const names[] = {"g", "out", "ws"};
+  return check_disjoint(spans, names);
+}
+
 }  // namespace
 
 static_assert(sizeof(dmuon_clip_stats_t) == sizeof(dmuon::ClipStats), "clip stats layout");
@@ -1025,6 +1154,70 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t*
   if ((st = get_plan(L, grads, params, bufs, false, static_cast<char*>(ws), &plan))) return st;
   return run(*plan, cfg, false, momentum, nesterov ? 1 : 0, lr, decay,
              static_cast<hipStream_t>(stream));
+}
+
+dmuon_status_t dmuon_gram_local_workspace_size(const dmuon_batch_t* g, int32_t transposed,
+                                               const dmuon_ns_cfg_t* cfg, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DMUON_E_INVALID, "bytes: null");
+  dmuon_status_t st = check_local(cfg, transposed);
+  if (st) return st;
+  if ((st = check_batch(g, "g", false))) return st;
+  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_BF16_SPLIT_A)
+    return fail(DMUON_E_INVALID, "cfg: unknown precision mode");
+  if ((st = check_backend(cfg))) return st;
+  Layout L;
+  if ((st = make_layout(g, cfg->prec, cfg->backend, &L, transposed, true))) return st;
+  *bytes = g->count ? L.total : 0;
+  return DMUON_OK;
+}
+
+dmuon_status_t dmuon_gram_local_bucket(const dmuon_batch_t* g, int32_t transposed,
+                                       const dmuon_ns_cfg_t* cfg, size_t* offset,
+                                       int64_t* count, int32_t* windows) {
+  g_last_error.clear();
+  if (!offset || !count || !windows) return fail(DMUON_E_INVALID, "offset, count, windows: null");
+  dmuon_status_t st = check_local(cfg, transposed);
+  if (st) return st;
+  if ((st = check_batch(g, "g", false))) return st;
+  if ((st = check_cfg(cfg))) return st;
+  Layout L;
+  if ((st = make_layout(g, cfg->prec, cfg->backend, &L, transposed, true))) return st;
+  *offset = g->count ? L.bucket_off : 0;
+  *count = g->count ? (int64_t)(L.bucket_bytes / sizeof(float)) : 0;
+  *windows = (int32_t)gram_cuts(cfg).size() - 1;
+  return DMUON_OK;
+}
+
+dmuon_status_t dmuon_gram_local_begin(const dmuon_batch_t* g, const dmuon_batch_t* out,
+                                      int32_t transposed, const dmuon_ns_cfg_t* cfg, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Layout L;
+  dmuon_status_t st = local_setup(g, out, transposed, cfg, ws, ws_bytes, &L);
+  if (st || g->count == 0) return st;
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  Plan* plan = nullptr;
+  if ((st = get_plan(L, g, out, nullptr, true, static_cast<char*>(ws), &plan))) return st;
+  return run(*plan, cfg, true, 0.f, 0, 0.f, 1.f, static_cast<hipStream_t>(stream));
+}
+
+dmuon_status_t dmuon_gram_local_advance(const dmuon_batch_t* g, const dmuon_batch_t* out,
+                                        int32_t transposed, const dmuon_ns_cfg_t* cfg,
+                                        int32_t window, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  g_last_error.clear();
+  Layout L;
+  dmuon_status_t st = local_setup(g, out, transposed, cfg, ws, ws_bytes, &L);
+  if (st) return st;
+  const int windows = (int)gram_cuts(cfg).size() - 1;
+  if (window < 0 || window >= windows)
+    return fail(DMUON_E_INVALID, "window must be in [0, " + std::to_string(windows) + ")");
+  if (g->count == 0) return DMUON_OK;
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  Plan* plan = nullptr;
+  if ((st = get_plan(L, g, out, nullptr, true, static_cast<char*>(ws), &plan))) return st;
+  return run_local_advance(*plan, cfg, window, static_cast<hipStream_t>(stream));
 }
 
 dmuon_status_t dmuon_clip_workspace_size(const dmuon_batch_t* grads, int32_t nbuckets,

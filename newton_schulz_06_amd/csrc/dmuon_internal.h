@@ -112,6 +112,22 @@ struct NormTask {
   int32_t tile_begin, tile_count;
   const float* partial;
   float* scale;
+  // Gram NS on a shard: the shard's sum of squares goes here (to be summed
+  // over the shard group) and the scales stay 1 until the group's norm is
+  // known.
+  float* sumsq;
+};
+
+// Gram NS on a shard, once the group's sums are in: the normalization from
+// the summed squared norm, and the summed raw Gram matrix A (P x P rows of
+// stride ld) scaled by its square.  FIN_ROWS rows of A per block.
+constexpr int FIN_ROWS = 16;
+struct FinTask {
+  int32_t tile_begin, tile_count;  // blocks
+  int32_t P, ld;
+  float* a;
+  const float* sumsq;
+  float* scale;
 };
 
 // ---------------------------------------------------------------------------
@@ -179,6 +195,8 @@ hipError_t launch_adamw(const FlatTask* tasks, int ntasks, int total_blocks,
 hipError_t launch_momentum(const EwTask* tasks, int ntasks, int total_tiles,
                            float momentum, int nesterov, int ns_only,
                            hipStream_t s);
+hipError_t launch_gram_finalize(const FinTask* tasks, int ntasks, int nblocks, float eps,
+                                hipStream_t s);
 hipError_t launch_norm(const NormTask* tasks, int ntasks, float eps,
                        hipStream_t s);
 // kind in {KIND_SYRK, KIND_POLY, KIND_UPDX}; tile in {64, 128, 256}

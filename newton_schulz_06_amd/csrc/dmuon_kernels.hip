@@ -165,10 +165,46 @@ __global__ __launch_bounds__(256) void norm_kernel(const NormTask* __restrict__ 
   __syncthreads();
   if (threadIdx.x == 0) {
     const double tot = (wpart[0] + wpart[1]) + (wpart[2] + wpart[3]);
-    const double s = sqrt(tot);
-    const double inv = 1.0 / (s + (double)eps);
+    if (T.sumsq) {  // a shard: the group's norm is not known yet
+      st_f32(T.sumsq, (float)tot);
+      st_f32(T.scale + 0, 1.f);
+      st_f32(T.scale + 1, 1.f);
+      st_f32(T.scale + 2, 0.f);
+    } else {
+      const double s = sqrt(tot);
+      const double inv = 1.0 / (s + (double)eps);
+      st_f32(T.scale + 0, (float)inv);
+      st_f32(T.scale + 1, (float)(inv * inv));
+      st_f32(T.scale + 2, (float)s);
+    }
+  }
+}
+
+// Gram NS on a shard, after the group sum: inv = 1/(sqrt(sumsq) + eps) as in
+// norm_kernel, A *= inv^2 (the same fp32 factor the SYRK epilogue applies
+// when the norm is known up front), and the scales for the X update.
+__global__ __launch_bounds__(256) void gram_finalize_kernel(const FinTask* __restrict__ tasks,
+                                                            int ntasks, float eps) {
+  const int b = blockIdx.x;
+  const FinTask T = tasks[find_task(tasks, ntasks, b)];
+  const double tot = (double)ld_f32(T.sumsq);
+  const double s = sqrt(tot);
+  const double inv = 1.0 / (s + (double)eps);
+  const float s2 = (float)(inv * inv);
+  const int r0 = (b - T.tile_begin) * FIN_ROWS;
+  const int r1 = min(r0 + FIN_ROWS, T.P);
+  for (int r = r0; r < r1; ++r) {
+    float* row = T.a + (size_t)r * T.ld;
+    for (int c = 4 * threadIdx.x; c < T.P; c += 4 * 256) {
+      f32x4 v = ld_f32x4(row + c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] *= s2;
+      st_f32x4(row + c, v);
+    }
+  }
+  if (b == T.tile_begin && threadIdx.x == 0) {
     st_f32(T.scale + 0, (float)inv);
-    st_f32(T.scale + 1, (float)(inv * inv));
+    st_f32(T.scale + 1, s2);
     st_f32(T.scale + 2, (float)s);
   }
 }
@@ -917,6 +953,12 @@ hipError_t launch_momentum(const EwTask* tasks, int ntasks, int total_tiles, flo
                            int nesterov, int ns_only, hipStream_t s) {
   hipLaunchKernelGGL(momentum_kernel, dim3(total_tiles), dim3(EW_THREADS), 0, s, tasks, ntasks,
                      total_tiles, momentum, nesterov, ns_only);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_finalize(const FinTask* tasks, int ntasks, int nblocks, float eps,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(gram_finalize_kernel, dim3(nblocks), dim3(256), 0, s, tasks, ntasks, eps);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ import os
 import re
 import sys
 
-KINDS = {"3": "syrk", "4": "poly", "5": "update_x"}
+KINDS = {"3": "syrk", "4": "poly", "5": "update_x", "9": "gram_mul"}
 
 
 def short_name(name: str) -> str:

@@ -413,3 +413,98 @@ def test_adamw_shape_mismatch_rejected():
     p, g, m, v = _adam_mats()
     g2 = _mats([(16, 9, FAKE_G)])[0]
     assert _call_adamw(p, g2, m, v) == dm.DMUON_E_INVALID, _err()
+
+
+# --- Gram-space NS on shards (dmuon_gram_local_*) ---------------------------
+
+def _expected_local(shapes, transposed):
+    """Shard layout: partials, scales, sink, then the bucket (sums of squares
+    padded to 256 bytes, every fp32 A back to back), then per matrix fp32 X,
+    two fp32 X^T and the four other P x P buffers.  p comes from the flag."""
+    a = lambda x: _pad(x, 256)  # noqa: E731
+    tiles, per, bucket = 0, 0, a(4 * len(shapes))
+    for m, n in shapes:
+        p, q = (n, m) if transposed else (m, n)
+        t = _tile(p, "f32")
+        P, Q = _pad(p, t), _pad(q, t)
+        tiles += (P // 64) * (Q // 64)
+        bucket += a(4 * P * _ld(P, 4))
+        per += a(4 * P * _ld(Q, 4)) + 2 * a(4 * Q * _ld(P, 4)) + 4 * a(4 * P * _ld(P, 4))
+    head = a(4 * tiles) + a(16 * len(shapes)) + a(16)
+    return head + bucket + per, head, bucket
+
+
+LOCAL_SHAPES = [(1792, 4096), (512, 1024), (100, 37), (37, 300)]
+
+
+@pytest.mark.parametrize("transposed", [0, 1])
+def test_gram_local_layout(transposed):
+    total, head, bucket = _expected_local(LOCAL_SHAPES, transposed)
+    for prec in ("f32", "auto"):
+        assert dm.gram_local_workspace_size(LOCAL_SHAPES, transposed, prec) == total
+    off, cnt, win = dm.gram_local_bucket(LOCAL_SHAPES, transposed)
+    assert (off, 4 * cnt, win) == (head, bucket, 2)
+    assert dm.gram_local_bucket(LOCAL_SHAPES, transposed, restart_iterations=[])[2] == 1
+    assert dm.gram_local_bucket(LOCAL_SHAPES, transposed, restart_iterations=[3, 1, 9])[2] == 3
+    assert dm.gram_local_bucket(LOCAL_SHAPES, transposed, ns_steps=2)[2] == 1
+    assert dm.gram_local_workspace_size([], transposed) == 0
+    assert dm.gram_local_bucket([], transposed)[:2] == (0, 0)
+
+
+def test_gram_local_one_rank_matches_gram_sizes():
+    # with the auto orientation, the shard layout is the Gram layout plus the
+    # sums of squares
+    shapes = [(1024, 256), (256, 1024)]
+    got = dm.gram_local_workspace_size(shapes[:1], 1) + dm.gram_local_workspace_size(shapes[1:], 0)
+    want = dm.workspace_size(shapes[:1], "f32", "gram") + dm.workspace_size(shapes[1:], "f32", "gram")
+    assert got == want + 2 * 256
+
+
+def _call_local(fn, g, o, transposed, cfg, window=0, ws=FAKE_WS, ws_bytes=1 << 40):
+    L = dm.lib()
+    args = [ctypes.byref(g), ctypes.byref(o), transposed, ctypes.byref(cfg)]
+    if fn == "advance":
+        return L.dmuon_gram_local_advance(*args, window, ctypes.c_void_p(ws), ws_bytes, None)
+    return L.dmuon_gram_local_begin(*args, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+LOCAL_BAD = {
+    "transposed 2": (dict(transposed=2), dm.DMUON_E_INVALID),
+    "direct backend": (dict(cfg=dict(prec="f32")), dm.DMUON_E_INVALID),
+    "bf16 operands": (dict(cfg=dict(prec="bf16", backend="gram")), dm.DMUON_E_UNSUPPORTED),
+    "window -1": (dict(fn="advance", window=-1), dm.DMUON_E_INVALID),
+    "window past the last": (dict(fn="advance", window=2), dm.DMUON_E_INVALID),
+    "one window only": (dict(fn="advance", window=1,
+                             cfg=dict(prec="f32", backend="gram", restart_iterations=[])),
+                        dm.DMUON_E_INVALID),
+    "small workspace": (dict(ws_bytes=4096), dm.DMUON_E_WORKSPACE),
+    "shape differs": (dict(o=[(64, 97, FAKE_O)]), dm.DMUON_E_INVALID),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LOCAL_BAD))
+@pytest.mark.parametrize("fn", ["begin", "advance"])
+def test_gram_local_rejects(name, fn):
+    spec, want = LOCAL_BAD[name]
+    fn = spec.get("fn", fn)
+    g, k1 = _mats([(64, 96, FAKE_G)])
+    o, k2 = _mats(spec.get("o", [(64, 96, FAKE_O)]))
+    cfg = _keep_cfg(**spec.get("cfg", dict(prec="f32", backend="gram")))
+    st = _call_local(fn, g, o, spec.get("transposed", 0), cfg, window=spec.get("window", 0),
+                     ws_bytes=spec.get("ws_bytes", 1 << 40))
+    assert st == want, (name, st, _err())
+    assert _err()
+
+
+def test_gram_local_valid_call_reaches_the_device():
+    g, k1 = _mats([(64, 96, FAKE_G)])
+    o, k2 = _mats([(64, 96, FAKE_O)])
+    cfg = _keep_cfg(prec="f32", backend="gram")
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if not has_gpu:
+        for fn in ("begin", "advance"):
+            assert _call_local(fn, g, o, 1, cfg, window=1) == dm.DMUON_E_HIP, _err()
