@@ -7,7 +7,10 @@ every matrix (5 iterations of A = X X^T, B = bA + cA^2, X = aX + BX) and the
 lr-scaled update, all in libdmuon's HIP kernels.  The default workload is
 the 4-layer TinyMLP of DMuon's Quick Start (d=512, ff=2048: 12 matrices);
 ``--config 3`` / ``--config 5`` run the Llama-8B projection and 70B-MLP
-batches, ``--config 4`` the 512-matrix NS-only batch.
+batches, ``--config 4`` the 512-matrix NS-only batch.  ``--ns-backend gram``
+runs the Gram-space iteration with restarts instead (fp32 operands); the
+value stays the direct method's algorithmic flops per second, so the two
+backends compare on the same work.
 
 Prints ONE JSON line: NS TFLOP/s (algorithmic, symmetry-aware flops) as the
 value, ms per step, the dominant kernel's roofline (timed with HIP events
@@ -70,9 +73,16 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--op", default="muon", choices=["muon", "clip", "adamw"],
+    ap.add_argument("--op", default="muon", choices=["muon", "clip", "adamw", "gram_local"],
                     help="muon: the Muon step (default); clip / adamw: the element-wise "
-                         "companions (gradient clipping, AdamW) on their own workloads")
+                         "companions (gradient clipping, AdamW) on their own workloads; "
+                         "gram_local: Gram-space NS of one tensor-parallel rank's blocks")
+    ap.add_argument("--ns-backend", default="direct", choices=["direct", "gram"],
+                    help="direct: X <- aX + BX every iteration (default); gram: the "
+                         "Gram-space iteration with restarts (fp32 operands)")
+    ap.add_argument("--restarts", default=None, metavar="K,K,...",
+                    help="Gram backend: iterations that start a new window (default: 2; "
+                         "'' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's host timing (0 disables it)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -129,9 +139,10 @@ def traffic_for(kind, workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, budget_s):
+def cpu_baseline(cfg, budget_s, backend="direct", restarts=None):
     """The fp64 oracle as it stands, on the host, over the same recipe:
-    whole matrices of the workload in order until the budget is used."""
+    whole matrices of the workload in order until the budget is used.  With
+    the Gram backend the oracle's Gram iteration replaces its direct one."""
     import numpy as np
     import oracle
     import workloads
@@ -149,7 +160,12 @@ def cpu_baseline(cfg, budget_s):
         p = workloads.param_np(m, n, cfg.cfg_id, i)
         buf = np.zeros((m, n))
         t0 = time.perf_counter()
-        if cfg.ns_only:
+        if backend == "gram":
+            u = g if cfg.ns_only else oracle.momentum_update(buf, g, cfg.momentum, cfg.nesterov)[1]
+            O = oracle.gram_newton_schulz(u, steps=cfg.ns_steps, restart_iterations=restarts)
+            if not cfg.ns_only:
+                _ = p - cfg.lr * cfg.weight_decay * p - cfg.lr * O
+        elif cfg.ns_only:
             oracle.direct_newton_schulz(g, steps=cfg.ns_steps)
         else:
             oracle.muon_step(p, g, buf, lr=cfg.lr, momentum=cfg.momentum,
@@ -167,7 +183,8 @@ def cpu_baseline(cfg, budget_s):
         "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"{len(done)} of {len(cfg.shapes)} matrices of one step "
-                   f"({frac:.0%}), {t_total:.1f} s; numpy fp64 BLAS"),
+                   f"({frac:.0%}), {t_total:.1f} s; numpy fp64 BLAS"
+                   + ("; Gram-space NS" if backend == "gram" else "")),
         "ms_per_step_estimate": t_total / frac * 1e3,
     }
 
@@ -186,9 +203,140 @@ def calib_copy(mib, device):
     del src, dst
 
 
+def gram_flops(p, q, ns_steps=5, restarts=None):
+    """Flops of Gram-space NS on a p x q oriented block, counted like the
+    library's profile: per window, p(p+1)q for A = X X^T, p^2(p+1) for each
+    symmetric p x p product (P's A A, Q <- P Q, P A, P (P A)) and 2p^2q
+    for X <- Q X."""
+    cuts = sorted({0, ns_steps} | {r for r in ([2] if restarts is None else restarts)
+                                   if 0 < r < ns_steps})
+    sym = p * p * (p + 1.0)
+    tot = 0.0
+    for s, e in zip(cuts[:-1], cuts[1:]):
+        k = e - s
+        tot += p * (p + 1.0) * q + k * sym + 3 * (k - 1) * sym + 2.0 * p * p * q
+    return tot
+
+
+def run_gram_local(args):
+    """Gram-space NS of one tensor-parallel rank's blocks (one batch per
+    orientation), with the shard group's all-reduce stubbed as identity:
+    K timed calls; value = flops per second (fp32 MFMA)."""
+    import numpy as np
+    import torch
+    import workloads
+    import newton_schulz_06_amd as dm
+
+    oc = workloads.OP_CONFIGS["gram_local"]
+    steps = args.steps if args.steps is not None else 10
+    warmup = args.warmup if args.warmup is not None else 2
+    device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
+    calib_copy(args.calib_copy, device)
+    gen = torch.Generator(device=device).manual_seed(19)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[oc.dtype]
+    batches = []
+    flops = 0.0
+    for t in (0, 1):
+        shapes = [s for s, tt in zip(oc.shapes, oc.transposed) if tt == t]
+        if not shapes:
+            continue
+        gs = [torch.randn(s, device=device, generator=gen).to(dt) for s in shapes]
+        outs = [torch.empty_like(g) for g in gs]
+        batches.append(dm.GramLocal(gs, outs, transposed=t, prec="f32"))
+        for m, n in shapes:
+            p, q = (n, m) if t else (m, n)
+            flops += gram_flops(p, q)
+    log(f"gram_local on {oc.name}: {len(oc.shapes)} blocks in {len(batches)} batches")
+
+    def run():
+        for b in batches:
+            b()
+
+    for _ in range(max(warmup - 1, 0)):
+        run()
+    with dm.profile() as prof_all:
+        run()
+    torch.cuda.synchronize()
+    dominant = max(prof_all.rows, key=lambda k: prof_all.rows[k]["ms"])
+    charged = sum(v["flops"] for v in prof_all.rows.values())
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with dm.profile(kinds=[dominant]) as prof:
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    log(f"timed {steps} calls: {ms_step:.4f} ms/call, {tflops:.1f} TFLOP/s")
+    row = prof.rows[dominant]
+    roof = roofline(row, "f32")
+    roof.update({"kernel": dominant,
+                 "flops_per_launch": row["flops"] / row["launches"],
+                 "bytes_per_launch": row["bytes"] / row["launches"],
+                 "avg_launch_ms": round(row["ms"] / row["launches"], 5),
+                 "launches": row["launches"],
+                 "traffic": traffic_for(dominant, oc.name)})
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = gram_local_cpu_baseline(oc, min(args.cpu_seconds, 30.0))
+    out = {
+        "metric": OP_METRIC["gram_local"],
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": oc.name, "blocks": len(oc.shapes),
+                   "shapes": sorted({f"{m}x{n}" for m, n in oc.shapes}),
+                   "block_dtype": oc.dtype, "ns_steps": 5, "restarts": [2],
+                   "group_sum": "identity (one GPU's share)",
+                   "parallelism": "1 GPU (one rank of a TP-8 group)"},
+        "tflop_per_step": round(flops / 1e12, 6),
+        "kernel_tflop_one_step": round(charged / 1e12, 6),
+        "kernel_ms_one_step": {k: round(v["ms"], 4) for k, v in prof_all.rows.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def gram_local_cpu_baseline(oc, budget_s):
+    """The fp64 oracle's shard NS on the host, block by block (one rank, the
+    group sum a no-op) until the budget is used."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+    t_total, flops, done = 0.0, 0.0, 0
+    for (m, n), t in zip(oc.shapes, oc.transposed):
+        g = rng.standard_normal((m, n))
+        t0 = time.perf_counter()
+        oracle.gram_newton_schulz_distributed_local([g], bool(t))
+        t_total += time.perf_counter() - t0
+        p, q = (n, m) if t else (m, n)
+        flops += gram_flops(p, q)
+        done += 1
+        if t_total >= budget_s:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{done} of {len(oc.shapes)} blocks, {t_total:.1f} s; numpy fp64 BLAS"}
+
+
 OP_METRIC = {
     "clip": "Muon gradient clipping (norm + scale) ms & HBM GB/s, 1 GPU",
     "adamw": "AdamW update of non-Muon params ms & HBM GB/s, 1 GPU",
+    "gram_local": "Gram NS of one TP rank's blocks ms & TFLOP/s (fp32 MFMA), 1 GPU",
 }
 
 
@@ -325,6 +473,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.op == "gram_local":
+        run_gram_local(args)
+        return
     if args.op != "muon":
         run_op(args)
         return
@@ -343,16 +494,23 @@ def main():
     params, bufs, sets = make_inputs(cfg, n_sets, device)
     shapes = list(cfg.shapes)
     flops_step = ns_flops(shapes, cfg.ns_steps)
-    arith = "f32" if cfg.ns_prec == "f32" else "bf16"
+    backend = args.ns_backend
+    restarts = None
+    if args.restarts is not None:
+        restarts = [int(v) for v in args.restarts.split(",") if v.strip()]
+    # The Gram backend runs on fp32 operands only.
+    prec = "f32" if backend == "gram" else cfg.ns_prec
+    arith = "f32" if prec == "f32" else "bf16"
+    ns_kw = dict(ns_steps=cfg.ns_steps, prec=prec, backend=backend, restart_iterations=restarts)
 
     if cfg.ns_only:
         outs = [torch.empty_like(g) for g in sets[0]]
-        call = dm.PreparedNs(sets[0], outs, ns_steps=cfg.ns_steps, prec=cfg.ns_prec)
+        call = dm.PreparedNs(sets[0], outs, **ns_kw)
         run = lambda i: call()  # noqa: E731
     else:
         call = dm.PreparedMuonStep(params, bufs, sets, lr=cfg.lr, momentum=cfg.momentum,
                                    weight_decay=cfg.weight_decay, nesterov=cfg.nesterov,
-                                   ns_steps=cfg.ns_steps, prec=cfg.ns_prec)
+                                   **ns_kw)
         run = call
 
     # Warm-up; the last warm-up step times every kernel kind once to find
@@ -397,7 +555,7 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         log("timing the fp64 oracle on the host")
-        cpu = cpu_baseline(cfg, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, args.cpu_seconds, backend, restarts)
 
     out = {
         "metric": METRIC,
@@ -417,7 +575,8 @@ def main():
             "matrices": len(shapes),
             "shapes": sorted({f"{m}x{n}" for m, n in shapes}) if len(shapes) <= 32 else "512 small",
             "ns_steps": cfg.ns_steps,
-            "ns_precision": cfg.ns_prec,
+            "ns_precision": prec,
+            "ns_backend": backend,
             "param_dtype": cfg.param_dtype,
             "grad_dtype": cfg.grad_dtype,
             "nesterov": cfg.nesterov,
@@ -426,6 +585,9 @@ def main():
             "parallelism": "1 GPU (owner-local batch)",
         },
         "ns_tflop_per_step": round(flops_step / 1e12, 6),
+        # flops the library's kernels were charged with in one step (for the
+        # Gram backend these differ from the direct count the value is based on)
+        "kernel_tflop_one_step": round(sum(v["flops"] for v in prof_all.rows.values()) / 1e12, 6),
         "ns_mfma_frac": round(ns_tflops / PEAK_TFLOPS[arith], 4),
         "matrices_per_s": round(len(shapes) / (ms_step * 1e-3), 1),
         "kernel_ms_one_step": {k: round(v["ms"], 4) for k, v in prof_all.rows.items()},

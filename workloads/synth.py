@@ -237,6 +237,7 @@ class OpConfig:
     dtype: str               # param / gradient dtype
     buckets: tuple = ()      # clipping: bucket of each tensor
     max_norm: float = 0.0    # clipping: chosen below the gradients' norm
+    transposed: tuple = ()   # Gram NS on shards: the full matrix's orientation
     notes: str = field(default="", compare=False)
 
 
@@ -247,4 +248,11 @@ OP_CONFIGS = {
                      buckets=tuple(i // 7 for i in range(28)), max_norm=100.0),
     # AdamW's share of a Llama-8B: token embedding and LM head (vocab 128256)
     "adamw": OpConfig("llama8b_embed_lmhead", ((128256, 4096),) * 2, "bf16"),
+    # One rank's blocks of a Llama-8B tensor-parallel group of 8, for the
+    # matrices whose Megatron shard is a column block of the oriented matrix:
+    # o (4096 x 4096, split along its input side), down (4096 x 14336, same),
+    # gate and up (14336 x 4096, split along their output side, transposed).
+    "gram_local": OpConfig("llama8b_o_mlp_tp8_rank_blocks",
+                           ((4096, 512), (4096, 1792), (1792, 4096), (1792, 4096)) * 4,
+                           "bf16", transposed=(0, 0, 1, 1) * 4),
 }
