@@ -601,13 +601,125 @@ __device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][
 }
 
 // Dispatch of a finished tile to its epilogue.
+// UPDX, not the last iteration, bf16 hi/lo master (tiles below 256): the
+// accumulators pass through LDS in slabs of R rows, so that every thread
+// then owns 8-column row chunks and the master's two bf16 halves move in
+// 16-byte loads and stores (in the 32x32 output layout each lane holds 4
+// rows of one column, which costs one 2-byte access per element and
+// half).  The chunks' master loads go out before the barrier that
+// publishes the slab.  The new hi X also goes, transposed, into the bf16
+// stage the X^T rows are written from (same swizzle as updx_epilogue).
+// LDS: T*T bf16 stage, then R x (T+8) fp32 rows (row stride T+8 puts the
+// two half-waves' rows on disjoint banks): 26 KB (T=64), 49 KB (T=128).
+template <int T, int NT>
+__device__ __forceinline__ void updx_epilogue_hl(const GemmTask& G, f32x16 (&acc)[NT][NT],
+                                                 int tm, int tn, int wr, int wc, int lane,
+                                                 const IterArgs& A, uint16_t* lds) {
+  constexpr int WT = T / 2;
+  constexpr int RB = T == 64 ? 2 : 1;  // 32-row blocks per slab
+  constexpr int R = 32 * RB;
+  constexpr int LDR = T + 8;
+  constexpr int CPR = T / 8;            // 8-column chunks per row
+  constexpr int CPT = R * CPR / 256;    // chunks per thread per slab
+  static_assert(CPT >= 1 && (R * CPR) % 256 == 0, "slab shape");
+  uint16_t* stage = lds;
+  float* rows = reinterpret_cast<float*>(lds + T * T);
+  const int tid = threadIdx.x;
+  const float s = A.iter == 0 ? G.scale[0] : 1.f;
+  const float ca = A.a;
+  const int ld0 = G.ld0;
+  uint16_t* xb = static_cast<uint16_t*>(G.out0);
+  uint16_t* xlo = G.xlo;
+  __syncthreads();  // main-loop LDS reads are done
+
+#pragma unroll
+  for (int r0 = 0; r0 < T; r0 += R) {
+    u32x4 hv[CPT], lv[CPT];
+    size_t go[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int id = tid + 256 * k;
+      go[k] = (size_t)(tm * T + r0 + id / CPR) * ld0 + tn * T + 8 * (id % CPR);
+      hv[k] = *(const GMEM u32x4*)(xb + go[k]);
+      lv[k] = *(const GMEM u32x4*)(xlo + go[k]);
+    }
+    // the waves holding the slab's rows write them
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int br = r0 + 32 * b;  // tile row of this 32-row block
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        if (wr + 32 * i == br) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr)
+                rows[(32 * b + 8 * g + 4 * (lane >> 5) + rr) * LDR + wc + 32 * j + (lane & 31)] =
+                    acc[i][j][4 * g + rr];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int id = tid + 256 * k;
+      const int rl = id / CPR, c = 8 * (id % CPR);
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(rows + rl * LDR + c);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(rows + rl * LDR + c + 4);
+      const uint32_t hw[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
+      const uint32_t lw[4] = {lv[k].x, lv[k].y, lv[k].z, lv[k].w};
+      uint32_t ho[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __uint_as_float(hw[e] << 16) + __uint_as_float(lw[e] << 16);
+        const float x1 = __uint_as_float(hw[e] & 0xffff0000u) + __uint_as_float(lw[e] & 0xffff0000u);
+        const float acc0 = e < 2 ? a0[2 * e] : a1[2 * e - 4];
+        const float acc1 = e < 2 ? a0[2 * e + 1] : a1[2 * e - 3];
+        const float v0 = s * fmaf(ca, x0, acc0), v1 = s * fmaf(ca, x1, acc1);
+        ho[e] = to_bf16x2(v0, v1);
+        lo[e] = to_bf16x2(v0 - __uint_as_float(ho[e] << 16),
+                          v1 - __uint_as_float(ho[e] & 0xffff0000u));
+      }
+      *(GMEM u32x4*)(xb + go[k]) = u32x4{ho[0], ho[1], ho[2], ho[3]};
+      *(GMEM u32x4*)(xlo + go[k]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      const int il = r0 + rl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jl = c + e;
+        const int x = 4 * (jl & (T / 4 - 1));
+        stage[jl * T + (il ^ x)] = (uint16_t)(e & 1 ? ho[e >> 1] >> 16 : ho[e >> 1] & 0xffffu);
+      }
+    }
+    __syncthreads();  // the slab is read before the next one is written
+  }
+
+  // X^T from the stage, as full rows
+  uint16_t* xt = static_cast<uint16_t*>((A.iter & 1) ? G.out1 : G.out2);
+  const int ld1 = G.ld1;
+  constexpr int RPP = 256 / CPR;  // rows per pass of the block
+  const int c = tid % CPR;
+#pragma unroll 4
+  for (int jl = tid / CPR; jl < T; jl += RPP) {
+    const int x = 4 * (jl & (T / 4 - 1));
+    const int pos = (8 * c) ^ x;
+    u32x4 w = *reinterpret_cast<const u32x4*>(stage + jl * T + (pos & ~7));
+    if (pos & 4) { const uint32_t a = w.x, b = w.y; w.x = w.z; w.y = w.w; w.z = a; w.w = b; }
+    st_u32x4(xt + (size_t)(tn * T + jl) * ld1 + tm * T + 8 * c, w);
+  }
+}
+
 template <int KIND, int T, bool F32, int NT>
 __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm, int tn,
                                          int wr, int wc, int lane, const IterArgs& A,
                                          uint16_t* stage) {
   if constexpr (KIND == KIND_UPDX) {
-    if (A.fin == FIN_NONE)
-      updx_epilogue<T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A, stage);
+    if (A.fin == FIN_NONE) {
+      if constexpr (!F32 && kHiLoMaster<T>)
+        updx_epilogue_hl<T, NT>(G, acc, tm, tn, wr, wc, lane, A, stage);
+      else
+        updx_epilogue<T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A, stage);
+    }
     else if (G.dst_dtype == 0)
       updx_final<T, F32, NT, 0>(G, acc, tm, tn, wr, wc, lane, A);
     else
