@@ -54,6 +54,10 @@ int tile_class(int64_t p, bool f32_ops) {
 constexpr int kAutoSplitMaxP = 128;
 constexpr int kAutoSplitAMaxP = 1024;
 constexpr float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
+// Shortest K for 128-deep main-loop stages (see build_plan).  Measured: the
+// TinyMLP SYRK (K 2048) and polynomial (1536) run 10% faster with them, the
+// packed batch's short-K products slower.
+constexpr int64_t kDeepMinK = 1536;
 
 
 // Row stride (elements) for a workspace matrix with `n` columns of `esz`
@@ -295,6 +299,7 @@ struct GemmLaunch {
   // iteration (caller's param or output instead of the next X copies).
   double bytes, bytes_fin;
   int group;  // direct NS: the kind; Gram-space NS: a GramGroup
+  int bk = 64;  // K depth of a main-loop stage (bf16 kernels)
 };
 
 // Launch groups of Gram-space NS: one product with its buffers.  P of a
@@ -535,6 +540,20 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   if (L.gram) build_gram_groups(L, dst, ns_only, ws, scale, plan.get(), gtasks, ranges);
   for (int kind : (L.gram ? std::vector<int>() : std::vector<int>(kinds_direct, kinds_direct + 3))) {
     for (int tile : kTiles) {
+      // 128-deep stages for a 64-wide SYRK or polynomial launch (bf16) whose
+      // every K is a multiple of 128 and at least kDeepMinK (long loops at
+      // few blocks per CU); otherwise 64.  Never two launches per group.
+      int bk = 64;
+      if (!L.f32_ops && tile == 64 && kind != KIND_UPDX) {
+        bool deep = false;
+        for (const Geom& G : L.g) {
+          if (G.tile != tile) continue;
+          const int64_t Kt = kind == KIND_SYRK ? G.Q : (G.split_a ? 3 * G.P : G.P);
+          deep = Kt % 128 == 0 && Kt >= kDeepMinK;
+          if (!deep) break;
+        }
+        if (deep) bk = 128;
+      }
       const size_t begin = gtasks.size();
       int acc = 0;
       double flops = 0, bytes = 0, bytes_fin = 0;
@@ -630,7 +649,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
       }
       if (gtasks.size() > begin) {
         GemmLaunch gl{kind, tile, 0, (int)(gtasks.size() - begin), acc, flops, bytes,
-                      kind == KIND_UPDX ? bytes_fin : bytes, kind};
+                      kind == KIND_UPDX ? bytes_fin : bytes, kind, bk};
         plan->gemms.push_back(gl);
         ranges.push_back({begin, gtasks.size()});
       }
@@ -776,7 +795,7 @@ dmuon_status_t gram_group(const Plan& plan, int gid, const IterArgs& args, hipSt
     const GemmTask* tasks = reinterpret_cast<const GemmTask*>(tab + gl.off);
     const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
     const hipError_t e = timed(gl.kind, gl.flops, bytes, s, [&] {
-      return launch_gemm(gl.kind, gl.tile, 1, tasks, gl.ntasks, gl.total, args, s);
+      return launch_gemm(gl.kind, gl.tile, 1, gl.bk, tasks, gl.ntasks, gl.total, args, s);
     });
     if (e != hipSuccess)
       return fail(DMUON_E_HIP, std::string("Gram NS product launch: ") + hipGetErrorString(e));
@@ -880,7 +899,7 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
       const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
       st = check(timed(gl.kind, gl.flops, bytes, s,
                        [&] {
-                         return launch_gemm(gl.kind, gl.tile, plan.f32_ops, tasks, gl.ntasks,
+                         return launch_gemm(gl.kind, gl.tile, plan.f32_ops, gl.bk, tasks, gl.ntasks,
                                             gl.total, args, s);
                        }),
                  "NS product launch");

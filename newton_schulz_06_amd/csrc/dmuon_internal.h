@@ -200,8 +200,10 @@ hipError_t launch_gram_finalize(const FinTask* tasks, int ntasks, int nblocks, f
 hipError_t launch_norm(const NormTask* tasks, int ntasks, float eps,
                        hipStream_t s);
 // kind in {KIND_SYRK, KIND_POLY, KIND_UPDX}; tile in {64, 128, 256}
-// (bf16 operands) or {64, 128} (fp32 operands)
-hipError_t launch_gemm(int kind, int tile, int f32_ops,
+// (bf16 operands) or {64, 128} (fp32 operands); bk, the K depth of a bf16
+// main-loop stage: 64, or 128 for the 64-wide SYRK and polynomial (every
+// task's K then a multiple of 128)
+hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk,
                        const GemmTask* tasks, int ntasks, int total_tiles,
                        const IterArgs& args, hipStream_t s);
 

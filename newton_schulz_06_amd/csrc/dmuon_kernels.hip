@@ -904,21 +904,22 @@ __device__ __forceinline__ void wait_stages(int younger) {
   }
 }
 
-// K depth of a stage (bf16 per row) and stages in flight, per tile size.
-// LDS holds STAGES x 2 operands x T rows x 2*BK bytes: 48 KB (T = 64),
-// 64 KB (128), 128 KB (256).  128-byte rows halve the number of L2
-// requests against 64-byte rows; measured on the NS shapes, that beats
-// keeping more (shallower) stages in flight.
-template <int T>
-constexpr int kBK = 64;
-template <int T>
-constexpr int kStages = T == 64 ? 3 : 2;
+// Stages in flight per K depth BK of a stage (bf16 per row) and tile size.
+// LDS holds STAGES x 2 operands x T rows x 2*BK bytes: 48 KB (T = 64,
+// BK = 64), 64 KB (T = 64, BK = 128; T = 128), 128 KB (T = 256).  128-byte
+// rows halve the number of L2 requests against 64-byte rows; measured on
+// the NS shapes, that beats keeping more (shallower) stages in flight.
+// BK = 128 (256-byte rows, half the stages and waits) serves the 64-wide
+// SYRK and polynomial products, whose long K loops run at under two blocks
+// per CU: 10% faster there, slower for the X update's short K.  The host
+// gives it only tasks whose K is a multiple of 128.
+template <int T, int BK>
+constexpr int kStages = (T == 64 && BK == 64) ? 3 : 2;
 
-template <int KIND, int T>
+template <int KIND, int T, int BK>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restrict__ tasks,
                                                         int ntasks, int total_tiles, IterArgs A) {
-  constexpr int STAGES = kStages<T>;
-  constexpr int BK = kBK<T>;              // bf16 per row per stage
+  constexpr int STAGES = kStages<T, BK>;
   constexpr int CPR = BK / 8;             // 16-byte chunks per row
   constexpr int WT = T / 2;               // wave tile (2 x 2 waves)
   constexpr int NT = WT / 32;             // 32x32 MFMA blocks per wave side
@@ -1036,26 +1037,31 @@ hipError_t launch_gemm_f32(const GemmTask* tasks, int ntasks, int total_tiles, c
   return hipGetLastError();
 }
 
-template <int KIND, int T>
+template <int KIND, int T, int BK>
 hipError_t launch_gemm_bf16(const GemmTask* tasks, int ntasks, int total_tiles, const IterArgs& A,
                             hipStream_t s) {
   const int grid = (total_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_bf16_kernel<KIND, T>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
+  hipLaunchKernelGGL((gemm_bf16_kernel<KIND, T, BK>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
                      total_tiles, A);
   return hipGetLastError();
 }
 
 template <int KIND>
-hipError_t launch_gemm_k(int tile, int f32_ops, const GemmTask* tasks, int ntasks,
+hipError_t launch_gemm_k(int tile, int f32_ops, int bk, const GemmTask* tasks, int ntasks,
                          int total_tiles, const IterArgs& A, hipStream_t s) {
   if (f32_ops) {
     if (tile == 64) return launch_gemm_f32<KIND, 64>(tasks, ntasks, total_tiles, A, s);
     if (tile == 128) return launch_gemm_f32<KIND, 128>(tasks, ntasks, total_tiles, A, s);
     return hipErrorInvalidValue;
   }
-  if (tile == 64) return launch_gemm_bf16<KIND, 64>(tasks, ntasks, total_tiles, A, s);
-  if (tile == 128) return launch_gemm_bf16<KIND, 128>(tasks, ntasks, total_tiles, A, s);
-  if (tile == 256) return launch_gemm_bf16<KIND, 256>(tasks, ntasks, total_tiles, A, s);
+  if constexpr (KIND != KIND_UPDX) {
+    if (tile == 64 && bk == 128)
+      return launch_gemm_bf16<KIND, 64, 128>(tasks, ntasks, total_tiles, A, s);
+  }
+  if (bk != 64) return hipErrorInvalidValue;
+  if (tile == 64) return launch_gemm_bf16<KIND, 64, 64>(tasks, ntasks, total_tiles, A, s);
+  if (tile == 128) return launch_gemm_bf16<KIND, 128, 64>(tasks, ntasks, total_tiles, A, s);
+  if (tile == 256) return launch_gemm_bf16<KIND, 256, 64>(tasks, ntasks, total_tiles, A, s);
   return hipErrorInvalidValue;
 }
 
@@ -1079,15 +1085,15 @@ hipError_t launch_norm(const NormTask* tasks, int ntasks, float eps, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int kind, int tile, int f32_ops, const GemmTask* tasks, int ntasks,
+hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk, const GemmTask* tasks, int ntasks,
                        int total_tiles, const IterArgs& A, hipStream_t s) {
   switch (kind) {
     case KIND_SYRK:
-      return launch_gemm_k<KIND_SYRK>(tile, f32_ops, tasks, ntasks, total_tiles, A, s);
+      return launch_gemm_k<KIND_SYRK>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, s);
     case KIND_POLY:
-      return launch_gemm_k<KIND_POLY>(tile, f32_ops, tasks, ntasks, total_tiles, A, s);
+      return launch_gemm_k<KIND_POLY>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, s);
     case KIND_UPDX:
-      return launch_gemm_k<KIND_UPDX>(tile, f32_ops, tasks, ntasks, total_tiles, A, s);
+      return launch_gemm_k<KIND_UPDX>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, s);
     case KIND_GRAMMUL:  // fp32 operands only
       if (!f32_ops) return hipErrorInvalidValue;
       if (tile == 64) return launch_gemm_f32<KIND_GRAMMUL, 64>(tasks, ntasks, total_tiles, A, s);

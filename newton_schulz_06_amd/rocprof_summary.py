@@ -24,9 +24,10 @@ def short_name(name: str) -> str:
     m = re.search(r"dmuon::\(anonymous namespace\)::(\w+)(<[^>]*>)?", name)
     if m:
         kern, targs = m.group(1), m.group(2) or ""
-        t = re.match(r"<(\d+), (\d+)", targs)
+        t = re.match(r"<(\d+), (\d+)(?:, (\d+))?", targs)
         if t and kern.startswith("gemm"):
-            return f"{KINDS.get(t.group(1), t.group(1))}[{kern}<T={t.group(2)}>]"
+            bk = f",BK={t.group(3)}" if kern == "gemm_bf16_kernel" and t.group(3) not in (None, "64") else ""
+            return f"{KINDS.get(t.group(1), t.group(1))}[{kern}<T={t.group(2)}{bk}>]"
         return kern
     if "elementwise" in name and ("copy" in name.lower() or "direct_copy" in name):
         return "torch_copy"

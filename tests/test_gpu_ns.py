@@ -196,3 +196,33 @@ def test_bf16_output_is_rne_of_fp32_output(prec):
         want = oracle.round_to_bf16(exact64(b))
         got = exact64(a)
         assert np.array_equal(got, want), (s, int(np.sum(got != want)))
+
+
+# Batches whose 64-wide products take 128-deep main-loop stages (every K of
+# the launch a multiple of 128 and >= 1536).  DEEP_SYRK: the SYRK, with
+# several K values, both orientations and a ragged row count.  DEEP_BOTH:
+# the SYRK and the split-A polynomial (K = 3P = 1536, 1920).
+DEEP_SYRK = [(512, 2048), (2048, 448), (320, 1536), (1664, 200)]
+DEEP_BOTH = [(512, 2048), (640, 1536), (2048, 512)]
+
+
+@pytest.mark.parametrize("shapes", ["syrk", "both"])
+@pytest.mark.parametrize("table", ["syrk", "poly"])
+def test_deep_stage_products(table, shapes):
+    sh = DEEP_SYRK if shapes == "syrk" else DEEP_BOTH
+    coeffs = UNIT_TABLES[table]
+    gs_np = [_gen(s, 40 + i) for i, s in enumerate(sh)]
+    gin, outs = _run_ns(gs_np, "f32", "bf16_split_a", coefficients=coeffs)
+    for s, g, o in zip(sh, gin, outs):
+        want = oracle.direct_newton_schulz(g, coefficients=coeffs)
+        assert rel_frobenius(o, want) <= 1.5e-2, (s, table)
+
+
+def test_deep_stage_full_table():
+    sh = DEEP_SYRK + DEEP_BOTH
+    gs_np = [_gen(s, 50 + i) for i, s in enumerate(sh)]
+    gin, outs = _run_ns(gs_np, "f32", "auto")
+    for s, g, o in zip(sh, gin, outs):
+        want = oracle.direct_newton_schulz(g)
+        assert rel_frobenius(o, want) <= 2e-2, s
+        assert sigma_dev(o, want) <= 2e-2, s
