@@ -31,3 +31,17 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_gram_flops_hand_count():
+    # p=2, q=3.  SYRK p(p+1)q = 18, a symmetric p x p product p^2(p+1) = 12,
+    # Q X 2p^2q = 24.  One window of one step: SYRK, P, Q X.
+    assert bench.gram_flops(2, 3, ns_steps=1) == 18 + 12 + 24
+    # One window of 3 steps: SYRK, 3 P, 2 Q <- P Q, 2 x (P A, P (P A)), Q X.
+    assert bench.gram_flops(2, 3, ns_steps=3, restarts=[]) == 18 + (3 + 2 + 4) * 12 + 24
+    # Default restart [2] over 5 steps: windows of 2 and 3 steps.
+    two = 18 + (2 + 1 + 2) * 12 + 24
+    three = 18 + (3 + 2 + 4) * 12 + 24
+    assert bench.gram_flops(2, 3) == two + three
+    # restarts outside 1..steps-1 have no effect
+    assert bench.gram_flops(2, 3, restarts=[0, 5, 9]) == bench.gram_flops(2, 3, restarts=[])
