@@ -709,6 +709,88 @@ __device__ __forceinline__ void updx_epilogue_hl(const GemmTask& G, f32x16 (&acc
   }
 }
 
+// SYRK epilogue with A split into [hi | lo | hi | hi] bf16 rows (tiles
+// below 256): the scaled tile passes through LDS in slabs of 64 rows; each
+// thread then writes 8-column row chunks of the four segments, and for an
+// off-diagonal tile 8-row column chunks of the mirrored tile, as 16-byte
+// stores (in the 32x32 output layout each element costs four 2-byte stores
+// and the mirror 8-byte ones).  Same values as sym_epilogue.  LDS: 64 x
+// (T+8) fp32 (T+8: the two half-waves' rows on disjoint banks).
+template <int T, int NT>
+__device__ __forceinline__ void syrk_split_epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT],
+                                                    int tm, int tn, int wr, int wc, int lane,
+                                                    const IterArgs& A, uint16_t* lds) {
+  constexpr int R = 64;
+  constexpr int LDR = T + 8;
+  constexpr int CPT = R * T / 8 / 256;  // chunks per thread per slab, each direction
+  static_assert((R * T / 8) % 256 == 0 && R % 32 == 0, "slab shape");
+  float* rows = reinterpret_cast<float*>(lds);
+  const int tid = threadIdx.x;
+  const float s = A.iter == 0 ? G.scale[1] : 1.f;
+  const bool mirror = tm != tn;
+  const int P = G.P;
+  const int ld0 = G.ld0;
+  uint16_t* o0 = static_cast<uint16_t*>(G.out0);
+  auto put = [&](size_t o, const float (&v)[8]) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = to_bf16x2(v[2 * e], v[2 * e + 1]);
+      l[e] = to_bf16x2(v[2 * e] - __uint_as_float(h[e] << 16),
+                       v[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
+    }
+    const u32x4 hv = {h[0], h[1], h[2], h[3]}, lv = {l[0], l[1], l[2], l[3]};
+    st_u32x4(o0 + o, hv);
+    st_u32x4(o0 + o + P, lv);
+    st_u32x4(o0 + o + 2 * P, hv);
+    st_u32x4(o0 + o + 3 * P, hv);
+  };
+  __syncthreads();  // main-loop LDS reads are done
+#pragma unroll
+  for (int r0 = 0; r0 < T; r0 += R) {
+#pragma unroll
+    for (int b = 0; b < R / 32; ++b)
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        if (wr + 32 * i == r0 + 32 * b) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr)
+                rows[(32 * b + 8 * g + 4 * (lane >> 5) + rr) * LDR + wc + 32 * j + (lane & 31)] =
+                    s * acc[i][j][4 * g + rr];
+        }
+    __syncthreads();
+    // row chunks: tile row r0 + rl, columns c .. c+7
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int id = tid + 256 * k;
+      const int rl = id / (T / 8), c = 8 * (id % (T / 8));
+      float v[8];
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(rows + rl * LDR + c);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(rows + rl * LDR + c + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v[e] = a0[e]; v[4 + e] = a1[e]; }
+      put((size_t)(tm * T + r0 + rl) * ld0 + tn * T + c, v);
+    }
+    // mirrored tile: row tn*T + c, columns tm*T + r0 + r8 .. +7
+    if (mirror) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int id = tid + 256 * k;
+        const int c = id % T, r8 = 8 * (id / T);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = rows[(r8 + e) * LDR + c];
+        put((size_t)(tn * T + c) * ld0 + tm * T + r0 + r8, v);
+      }
+    }
+    __syncthreads();  // the slab is read before the next one is written
+  }
+}
+
 template <int KIND, int T, bool F32, int NT>
 __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm, int tn,
                                          int wr, int wc, int lane, const IterArgs& A,
@@ -724,6 +806,11 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
       updx_final<T, F32, NT, 0>(G, acc, tm, tn, wr, wc, lane, A);
     else
       updx_final<T, F32, NT, 1>(G, acc, tm, tn, wr, wc, lane, A);
+  } else if constexpr (KIND == KIND_SYRK && !F32 && T < 256) {
+    if (G.split)
+      syrk_split_epilogue<T, NT>(G, acc, tm, tn, wr, wc, lane, A, stage);
+    else
+      sym_epilogue<KIND, T, F32, NT, false>(G, acc, tm, tn, wr, wc, lane, A);
   } else if constexpr (KIND == KIND_POLY && !F32) {
     if (G.ahl)
       sym_epilogue<KIND, T, F32, NT, true>(G, acc, tm, tn, wr, wc, lane, A);
