@@ -35,8 +35,8 @@ def _say(msg):
     print(f"[fullsize] {msg}", flush=True)
 
 
-def _full_run(cfg_id, steps, ns_check):
-    cfg = workloads.CONFIGS[cfg_id]
+def _full_run(name, steps, ns_check):
+    cfg = workloads.BY_NAME[name]
     dev = torch.device("cuda", 0)
     params, bufs, sets = bench.make_inputs(cfg, steps, dev)
     call = dm.PreparedMuonStep(params, bufs, sets, lr=cfg.lr, momentum=cfg.momentum,
@@ -47,7 +47,7 @@ def _full_run(cfg_id, steps, ns_check):
         p_before = {i: exact64(params[i]) for i in ns_check} if step == 0 else {}
         call(step)
         torch.cuda.synchronize()
-        _say(f"config {cfg_id} step {step} done on the GPU")
+        _say(f"{name} step {step} done on the GPU")
         us = {}
         for i, (m, n) in enumerate(cfg.shapes):
             if step == 0:
@@ -85,10 +85,10 @@ def _full_run(cfg_id, steps, ns_check):
 def test_llama8b_projections_full_size():
     """28 matrices, two steps; NS of q (4096x4096), k (1024x4096), gate
     (14336x4096, tall) and the last down (4096x14336, wide) vs the oracle."""
-    _full_run(3, 2, ns_check=(0, 1, 4, 27))
+    _full_run("llama8b_proj_x4", 2, ns_check=(0, 1, 4, 27))
 
 
 def test_llama70b_mlp_full_size():
     """6 matrices with Nesterov, two steps; NS of one tall (28672x8192) and
     one wide (8192x28672) matrix vs the oracle."""
-    _full_run(5, 2, ns_check=(0, 5))
+    _full_run("llama70b_mlp", 2, ns_check=(0, 5))

@@ -68,7 +68,7 @@ def test_gram_structured_and_auto_precision():
 
 
 def test_gram_muon_step_matches_oracle():
-    cfg = workloads.CONFIGS[1]
+    cfg = workloads.BY_NAME["tinymlp_d256_ff1024_fp32"]
     shapes = cfg.shapes
     params = [to_dev(workloads.param_np(m, n, 1, i), "f32") for i, (m, n) in enumerate(shapes)]
     bufs = [torch.zeros(m, n, device="cuda") for m, n in shapes]
@@ -91,7 +91,7 @@ def test_gram_muon_step_matches_oracle():
 def test_gram_tinymlp_batch_and_llama_matrix_full_size():
     """The 12-matrix TinyMLP batch (512 x 2048 oriented) and one Llama-8B
     gate matrix (14336 x 4096), NS only, against the oracle."""
-    shapes = list(workloads.CONFIGS[2].shapes) + [(14336, 4096)]
+    shapes = list(workloads.BY_NAME["tinymlp_d512_ff2048_x4"].shapes) + [(14336, 4096)]
     gs_np = [workloads.grad_np("gauss", m, n, 92, 0, i) for i, (m, n) in enumerate(shapes)]
     gin, outs = _gram_gpu(gs_np)
     for i in (0, 2, len(shapes) - 1):

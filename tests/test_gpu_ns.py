@@ -118,7 +118,7 @@ def test_ns_plain_bf16_large_gaussian(prec):
 def test_ns_c4_packed_batch():
     """512 small matrices (sides log-uniform in [32, 1024], multiples of 32)
     in one call, per-matrix tolerance, automatic precision."""
-    cfg = workloads.CONFIGS[4]
+    cfg = workloads.BY_NAME["packed_small_512"]
     gs_np = [workloads.grad_np(cfg.grad_kind, m, n, 4, 0, i) for i, (m, n) in enumerate(cfg.shapes)]
     gin, outs = _run_ns(gs_np, "bf16", "auto")
     worst_e = worst_d = 0.0

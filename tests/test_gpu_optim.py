@@ -128,7 +128,7 @@ def test_clip_llama8b_projection_grads_full_size():
     elements), one bucket per layer; every bucket's norm and a sample of
     scaled rows against the oracle."""
     import workloads
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.BY_NAME["llama8b_proj_x4"]
     gs = [workloads.grad_torch("gauss", m, n, 3, 0, i, "cuda", torch.bfloat16)
           for i, (m, n) in enumerate(cfg.shapes)]
     buckets = [i // 7 for i in range(len(gs))]

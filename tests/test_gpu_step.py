@@ -91,32 +91,32 @@ def _run(cfg, steps, check_ns_steps, shapes=None, cfg_id=None, nesterov=None):
 
 def test_c1_tinymlp_fp32():
     """3 fp32 matrices (1024x256, 1024x256, 256x1024), one step, fp32 NS."""
-    cfg = workloads.CONFIGS[1]
+    cfg = workloads.BY_NAME["tinymlp_d256_ff1024_fp32"]
     _run(cfg, 1, {0})
 
 
 @pytest.mark.parametrize("nesterov", [False, True])
 def test_c1_both_nesterov(nesterov):
-    cfg = workloads.CONFIGS[1]
+    cfg = workloads.BY_NAME["tinymlp_d256_ff1024_fp32"]
     _run(cfg, 3, {0, 2}, nesterov=nesterov)
 
 
 def test_c2_tinymlp_20_steps():
     """12 matrices of the 4-layer TinyMLP (d=512, ff=2048), 20 steps, fp32
     momentum, bf16 NS; NS checked on the first, second and last steps."""
-    cfg = workloads.CONFIGS[2]
+    cfg = workloads.BY_NAME["tinymlp_d512_ff2048_x4"]
     _run(cfg, 20, {0, 1, 19})
 
 
 def test_c2_nesterov_on():
-    cfg = workloads.CONFIGS[2]
+    cfg = workloads.BY_NAME["tinymlp_d512_ff2048_x4"]
     _run(cfg, 2, {1}, nesterov=True)
 
 
 def test_c3_like_bf16_params():
     """Llama-8B projection recipe (low rank + noise, bf16 storage) at a
     quarter of the sizes: 1024x1024, 256x1024, 3584x1024, 1024x3584."""
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.BY_NAME["llama8b_proj_x4"]
     shapes = [(1024, 1024), (256, 1024), (3584, 1024), (1024, 3584)]
     _run(cfg, 2, {0, 1}, shapes=shapes, cfg_id=93)
 
@@ -124,7 +124,7 @@ def test_c3_like_bf16_params():
 def test_c5_like_nesterov_bf16_params():
     """70B-MLP recipe (power law + Student-t, Nesterov) at an eighth of the
     sizes: 3584x1024 (x2) and 1024x3584, three steps."""
-    cfg = workloads.CONFIGS[5]
+    cfg = workloads.BY_NAME["llama70b_mlp"]
     shapes = [(3584, 1024), (3584, 1024), (1024, 3584)]
     _run(cfg, 3, {0, 2}, shapes=shapes, cfg_id=95)
 
@@ -144,7 +144,7 @@ def test_zero_gradient_only_decays():
 def test_step_is_deterministic_and_resumable():
     """Two runs from the same state agree bit for bit; a run that is stopped,
     copied to the host and restored continues bit-identically."""
-    cfg = workloads.CONFIGS[2]
+    cfg = workloads.BY_NAME["tinymlp_d512_ff2048_x4"]
     shapes = cfg.shapes[:3]
 
     def run(steps, state=None):

@@ -6,6 +6,7 @@ none of the Muon / Newton-Schulz arithmetic lives here.  Both the fp64
 oracle and the HIP path read their inputs from it.
 """
 from .synth import (  # noqa: F401
+    BY_NAME,
     CONFIGS,
     OP_CONFIGS,
     Config,

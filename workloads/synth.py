@@ -241,6 +241,10 @@ class OpConfig:
     notes: str = field(default="", compare=False)
 
 
+# The workloads by name.
+BY_NAME = {c.name: c for c in CONFIGS.values()}
+
+
 OP_CONFIGS = {
     # the 28 projection gradients of the Llama-8B batch, one bucket per layer
     # (bench.py lowers max_norm from call to call so that every call clips)
