@@ -216,10 +216,22 @@ __global__ __launch_bounds__(256) void gram_finalize_kernel(const FinTask* __res
 // 128 bytes per stage (64 bf16 or 32 fp32) through double-buffered LDS rows
 // padded by 16 bytes so that the 16-byte operand reads are conflict free.
 
-// Workgroups are handed to the 8 XCDs round robin; give each XCD one
-// contiguous range of the tile order so its L2 sees neighbouring tiles.
-__device__ __forceinline__ int xcd_remap(int b, int grid) {
-  return (b & 7) * (grid >> 3) + (b >> 3);
+// Workgroups are handed to the 8 XCDs round robin (workgroup b runs on XCD
+// b % 8).  Tile order: windows of 8 * kXcdChunk consecutive tiles, XCD x
+// taking the x-th contiguous chunk of each window, so that each XCD's L2
+// sees neighbouring tiles while all XCDs work in the same region of the
+// launch, whose operands the Infinity Cache (shared by the XCDs) then holds
+// once.  The last, partial window is split evenly; a launch of less than
+// one window gets one contiguous range per XCD.  Measured against giving
+// each XCD one contiguous eighth of the launch: Llama-8B step 83.2 -> 74.0
+// ms, 70B MLP step 218 -> 209 ms.  `grid` is total rounded up to 8.
+constexpr int kXcdChunk = 32;
+__device__ __forceinline__ int xcd_remap(int b, int grid, int total) {
+  constexpr int W = 8 * kXcdChunk;
+  const int full = total / W * W;
+  if (b < full) return b / W * W + (b & 7) * kXcdChunk + ((b >> 3) & (kXcdChunk - 1));
+  const int c = (grid - full) >> 3;  // chunk per XCD in the last window
+  return full + (b & 7) * c + ((b - full) >> 3);
 }
 
 constexpr int GROUP = 8;  // tile rows per group of the full-product order
@@ -834,7 +846,7 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
   constexpr int LOADS = T * 8 / 256;      // 16-byte chunks per thread per operand
   __shared__ __attribute__((aligned(16))) E lds[2][2][T * STRIDE];
 
-  const int vb = xcd_remap(blockIdx.x, gridDim.x);
+  const int vb = xcd_remap(blockIdx.x, gridDim.x, total_tiles);
   if (vb >= total_tiles) return;
   // By value (see momentum_kernel): the epilogue's stores must not force
   // reloads of the descriptor.
@@ -1015,7 +1027,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
   constexpr int LOADS = 2 * LPW;          // loads per thread per stage
   __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES][2][T * BK];
 
-  const int vb = xcd_remap(blockIdx.x, gridDim.x);
+  const int vb = xcd_remap(blockIdx.x, gridDim.x, total_tiles);
   if (vb >= total_tiles) return;
   // By value (see momentum_kernel): the epilogue's stores must not force
   // reloads of the descriptor.
