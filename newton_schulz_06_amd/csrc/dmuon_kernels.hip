@@ -991,6 +991,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0) only: every LDS read of this wave has returned.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Waits until at most `younger` stages of LOADS loads each are outstanding
 // (younger <= MAXY; a wave-uniform value, so the branches are scalar).
 template <int LOADS, int MAXY>
@@ -1085,6 +1090,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
 
   // Operand read offsets (elements) inside a stage buffer, per k-substep.
   constexpr int KS = BK / 16;  // MFMA k-substeps per stage
+  static_assert(KS % 2 == 0, "operand register sets alternate per substep");
   int offA[KS][NT], offB[KS][NT];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -1097,31 +1103,87 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
       offB[ks][t] = rb * BK + 8 * (kc ^ swz<CPR>(rb));
     }
 
+  // Two operand register sets: the LDS reads of substep ks+1 (or of the
+  // next stage's first substep) are in flight while substep ks's MFMAs run,
+  // so the LDS latency is not paid once per MFMA row.
+  bf16x8 ra[2][NT], rb[2][NT];
+  auto read_ops = [&](int set, const uint16_t* sa, const uint16_t* sb, int ks) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      ra[set][t] = *reinterpret_cast<const bf16x8*>(sa + offA[ks][t]);
+      rb[set][t] = *reinterpret_cast<const bf16x8*>(sb + offB[ks][t]);
+    }
+  };
+  // MFMAs [first, last) of one substep, row-major over the NT x NT blocks.
+  auto mfmas = [&](int set, int first, int last) {
+#pragma unroll
+    for (int x = first; x < last; ++x)
+      acc[x / NT][x % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          ra[set][x / NT], rb[set][x % NT], acc[x / NT][x % NT], 0, 0, 0);
+  };
+  // Interleave a substep's MFMAs with the next substep's 2*NT LDS reads.
+  auto interleave = [&]() {
+    constexpr int R = 2 * NT, M = NT * NT;
+    constexpr int PER = (R + M - 1) / M;  // reads after each MFMA
+#pragma unroll
+    for (int x = 0; x < M; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (x * PER < R) __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);  // DS reads
+    }
+  };
+
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < nk) issue(st);
+  if constexpr (NT == 1) {
+    // 64-wide tiles run three blocks per CU, whose waves hide each other's
+    // LDS latency: one operand set, read right before its MFMA (measured
+    // faster here than the prefetching loop below).
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_stages<LOADS, STAGES - 2>(min(nk - 1 - kt, STAGES - 2));
+      __builtin_amdgcn_s_barrier();
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+      const uint16_t* sa = lds[kt % STAGES][0];
+      const uint16_t* sb = lds[kt % STAGES][1];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        read_ops(0, sa, sb, ks);
+        mfmas(0, 0, 1);
+      }
+    }
+    epilogue<KIND, T, false, NT>(G, acc, tm, tn, wr, wc, lane, A, &lds[0][0][0]);
+    return;
+  }
+  wait_stages<LOADS, STAGES - 2>(min(nk - 1, STAGES - 2));
+  __builtin_amdgcn_s_barrier();
+  if (STAGES - 1 < nk) issue(STAGES - 1);
+  read_ops(0, lds[0][0], lds[0][1], 0);
 
+  // Split of the last substep's MFMAs around the hand-over to the next
+  // stage: the first half keeps the matrix cores busy through the wait and
+  // the barrier, the second covers the first LDS reads of the next stage.
+  constexpr int HALF = NT * NT / 2;
   for (int kt = 0; kt < nk; ++kt) {
-    // Stage kt must have landed: allow the younger stages to stay in flight.
-    wait_stages<LOADS, STAGES - 2>(min(nk - 1 - kt, STAGES - 2));
-    __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     const uint16_t* sa = lds[kt % STAGES][0];
     const uint16_t* sb = lds[kt % STAGES][1];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 a[NT], b[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        a[t] = *reinterpret_cast<const bf16x8*>(sa + offA[ks][t]);
-        b[t] = *reinterpret_cast<const bf16x8*>(sb + offB[ks][t]);
-      }
-#pragma unroll
-      for (int i = 0; i < NT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      read_ops((ks + 1) & 1, sa, sb, ks + 1);
+      mfmas(ks & 1, 0, NT * NT);
+      interleave();
     }
+    mfmas(1, 0, HALF);
+    if (kt + 1 < nk) {
+      // Stage kt+1 must have landed (the younger stages stay in flight) and
+      // every wave's reads of stage kt must be complete before its buffer is
+      // refilled with stage kt+STAGES.
+      wait_stages<LOADS, STAGES - 2>(min(nk - 2 - kt, STAGES - 2));
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      if (kt + STAGES < nk) issue(kt + STAGES);
+      read_ops(0, lds[(kt + 1) % STAGES][0], lds[(kt + 1) % STAGES][1], 0);
+    }
+    mfmas(1, HALF, NT * NT);
   }
 
   epilogue<KIND, T, false, NT>(G, acc, tm, tn, wr, wc, lane, A, &lds[0][0][0]);
