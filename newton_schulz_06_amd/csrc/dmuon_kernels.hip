@@ -65,7 +65,23 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
   const bool f32ops = T.f32_ops != 0;
   float ss = 0.f;
 
-  for (int k = 0; k < EW_TILE / 16; ++k) {
+  // A whole tile inside the matrix (the common case) issues all its loads
+  // before the first store: the stores to buf could alias later loads for
+  // all the compiler knows, which would serialize the rows' round trips.
+  constexpr int RK = EW_TILE / 16;  // rows per thread
+  const bool interior = T.vec && r0 + EW_TILE <= T.m && c0 + EW_TILE <= T.n;
+  f32x4 gpre[RK], bpre[RK];
+  if (interior) {
+#pragma unroll
+    for (int k = 0; k < RK; ++k) {
+      const size_t idx = (size_t)(r0 + ry + 16 * k) * T.n + c0 + cx;
+      gpre[k] = load4(T.src, T.in_dtype, idx);
+      if (!ns_only) bpre[k] = ld_f32x4(T.buf + idx);
+    }
+  }
+
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
     const int r = ry + 16 * k;
     const int gr = r0 + r;
     const int gc = c0 + cx;
@@ -73,11 +89,11 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
     if (gr < T.m && gc < T.n) {
       const size_t idx = (size_t)gr * T.n + gc;
       if (T.vec && gc + 3 < T.n) {
-        const f32x4 g = load4(T.src, T.in_dtype, idx);
+        const f32x4 g = interior ? gpre[k] : load4(T.src, T.in_dtype, idx);
         if (ns_only) {
           u = g;
         } else {
-          const f32x4 b = ld_f32x4(T.buf + idx);
+          const f32x4 b = interior ? bpre[k] : ld_f32x4(T.buf + idx);
           f32x4 bn;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -120,7 +136,8 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
   }
   __syncthreads();
   // Transposed copy: X^T for a wide matrix, X (and its bf16 copy) for a tall one.
-  for (int k = 0; k < EW_TILE / 16; ++k) {
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
     const int oc = ry + 16 * k;  // column of the tile = row of the output
     f32x4 v;
 #pragma unroll

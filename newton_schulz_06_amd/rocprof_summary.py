@@ -2,13 +2,20 @@
 
     python -m newton_schulz_06_amd.rocprof_summary trace  <dir>   # --kernel-trace --stats run
     python -m newton_schulz_06_amd.rocprof_summary counter <dir> [copy_mib]  # --pmc run
+    python -m newton_schulz_06_amd.rocprof_summary traffic <fetch_dir> <write_dir> \
+        <copy_mib> <kind> <kernel_prefix> <workload> <summary.md>
 
 `trace` prints per-kernel dispatch counts and average durations from the
 kernel trace; `counter` prints per-kernel averages of every collected
 counter.  With `copy_mib`, the plain copy of that many MiB that
 ``bench.py --calib-copy`` runs (the largest dispatch of the runtime's copy
 kernel) gives the ratio known / measured, printed as the scale factor for
-FETCH_SIZE and WRITE_SIZE (KiB per dispatch).
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch).  `traffic` takes one
+FETCH_SIZE run and one WRITE_SIZE run (each with the calibration copy),
+averages both counters over the dispatches of the kernels whose short name
+starts with `kernel_prefix`, scales them, and records the HBM bytes per
+launch in profiles/traffic.json under "<kind>@<workload>", with the hash of
+the kernel sources the counters were taken on.
 """
 import collections
 import csv
@@ -78,7 +85,51 @@ def counter(dirname, copy_mib=None):
                   f"scale {known_kib / v:.4f}")
 
 
+def _counter_avg(dirname, counter_name, prefix):
+    """(average over the matching dispatches, the calibration copy's value)."""
+    path = _csv(dirname, "counter_collection.csv")
+    per = collections.defaultdict(float)  # dispatch -> summed value
+    copy = 0.0
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter_name:
+            continue
+        v = float(r["Counter_Value"])
+        if short_name(r["Kernel_Name"]).startswith(prefix):
+            per[r["Dispatch_Id"]] += v
+        elif "copyBuffer" in r["Kernel_Name"]:
+            copy = max(copy, v)
+    if not per or not copy:
+        raise SystemExit(f"{counter_name}: no dispatch of {prefix} or no calibration copy in {dirname}")
+    return sum(per.values()) / len(per), copy
+
+
+def traffic(fetch_dir, write_dir, copy_mib, kind, prefix, workload, summary):
+    import json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    known_kib = float(copy_mib) * 1024.0
+    fetch, fcopy = _counter_avg(fetch_dir, "FETCH_SIZE", prefix)
+    write, wcopy = _counter_avg(write_dir, "WRITE_SIZE", prefix)
+    fs, ws = known_kib / fcopy, known_kib / wcopy
+    entry = {"kernel": prefix, "kernel_source_sha256": bench.kernel_sha(),
+             "fetch_kib_per_dispatch": round(fetch, 1), "write_kib_per_dispatch": round(write, 1),
+             "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+             "hbm_bytes_per_launch": int(round((fetch * fs + write * ws) * 1024.0)),
+             "source": summary}
+    path = os.path.join(root, "profiles", "traffic.json")
+    tab = json.load(open(path)) if os.path.exists(path) else {}
+    tab[f"{kind}@{workload}"] = entry
+    with open(path, "w") as f:
+        json.dump(tab, f, indent=1)
+        f.write("\n")
+    print(json.dumps({f"{kind}@{workload}": entry}, indent=1))
+
+
 if __name__ == "__main__":
+    if len(sys.argv) >= 2 and sys.argv[1] == "traffic" and len(sys.argv) == 9:
+        traffic(*sys.argv[2:9])
+        sys.exit(0)
     if len(sys.argv) < 3 or sys.argv[1] not in ("trace", "counter"):
         print(__doc__)
         sys.exit(2)
