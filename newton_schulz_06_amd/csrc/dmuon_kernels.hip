@@ -983,13 +983,17 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
 // STAGES buffers of BK k-values per row are kept in flight, so each K-step's
 // loads were issued STAGES-1 steps before they are consumed.  Rows are
 // stored without padding as CPR = BK/8 chunks of 16 bytes; k-chunk `kc` of
-// row r lives at slot kc ^ swz(r), which makes the 16-byte operand reads of
-// 8 consecutive rows (one LDS access phase) hit distinct banks: with 64-byte
-// rows two rows share a 128-byte bank line, with 128-byte rows each row
-// spans all banks.
+// row r lives at slot kc ^ swz(r).  The LDS has 64 banks of 4 bytes (a
+// 256-byte bank line) and serves a 16-byte read 16 lanes at a time, so the
+// reads of 16 consecutive rows must cover the 16 groups of 4 banks once:
+// 128-byte rows pair up in a bank line (row parity picks the half), so the
+// slot is swizzled by r/2; a 256-byte row spans the whole line, swizzled by
+// r.  (Swizzling 128-byte rows by r mod 8 left a 2-way conflict: rocprofv3
+// counted 4 conflict cycles per 16-byte read.)
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (CPR == 4) return ((r >> 1) ^ (r >> 2)) & 3;
+  else if constexpr (CPR == 8) return (r >> 1) & 7;
   else return r & (CPR - 1);
 }
 
