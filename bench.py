@@ -153,39 +153,48 @@ def cpu_baseline(cfg, budget_s, backend="direct", restarts=None):
     except Exception:
         threads = None
     flops = 0.0
-    done = []
+    done = 0
     t_total = 0.0
-    for i, (m, n) in enumerate(cfg.shapes):
-        g = workloads.grad_np(cfg.grad_kind, m, n, cfg.cfg_id, 0, i)
-        p = workloads.param_np(m, n, cfg.cfg_id, i)
-        buf = np.zeros((m, n))
-        t0 = time.perf_counter()
-        if backend == "gram":
-            u = g if cfg.ns_only else oracle.momentum_update(buf, g, cfg.momentum, cfg.nesterov)[1]
-            O = oracle.gram_newton_schulz(u, steps=cfg.ns_steps, restart_iterations=restarts)
-            if not cfg.ns_only:
-                _ = p - cfg.lr * cfg.weight_decay * p - cfg.lr * O
-        elif cfg.ns_only:
-            oracle.direct_newton_schulz(g, steps=cfg.ns_steps)
-        else:
-            oracle.muon_step(p, g, buf, lr=cfg.lr, momentum=cfg.momentum,
-                             weight_decay=cfg.weight_decay, nesterov=cfg.nesterov,
-                             ns_steps=cfg.ns_steps)
-        t_total += time.perf_counter() - t0
-        flops += ns_flops([(m, n)], cfg.ns_steps)
-        done.append((m, n))
-        if t_total >= budget_s:
-            break
-    frac = len(done) / len(cfg.shapes)
+    bufs, params = {}, {}
+    step = 0
+    # Whole steps of the workload (fresh seeded gradients each step, the
+    # momentum carried over) until the budget is spent.
+    while t_total < budget_s:
+        for i, (m, n) in enumerate(cfg.shapes):
+            g = workloads.grad_np(cfg.grad_kind, m, n, cfg.cfg_id, step, i)
+            if i not in params:
+                params[i] = workloads.param_np(m, n, cfg.cfg_id, i)
+                bufs[i] = np.zeros((m, n))
+            t0 = time.perf_counter()
+            if backend == "gram":
+                u = g
+                if not cfg.ns_only:
+                    bufs[i], u = oracle.momentum_update(bufs[i], g, cfg.momentum, cfg.nesterov)
+                O = oracle.gram_newton_schulz(u, steps=cfg.ns_steps, restart_iterations=restarts)
+                if not cfg.ns_only:
+                    params[i] = params[i] - cfg.lr * cfg.weight_decay * params[i] - cfg.lr * O
+            elif cfg.ns_only:
+                oracle.direct_newton_schulz(g, steps=cfg.ns_steps)
+            else:
+                params[i], bufs[i], _ = oracle.muon_step(
+                    params[i], g, bufs[i], lr=cfg.lr, momentum=cfg.momentum,
+                    weight_decay=cfg.weight_decay, nesterov=cfg.nesterov, ns_steps=cfg.ns_steps)
+            t_total += time.perf_counter() - t0
+            flops += ns_flops([(m, n)], cfg.ns_steps)
+            done += 1
+            if t_total >= budget_s:
+                break
+        step += 1
+    nmat = len(cfg.shapes)
     return {
         "value": flops / t_total / 1e12,
         "unit": "NS TFLOP/s",
         "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": (f"{len(done)} of {len(cfg.shapes)} matrices of one step "
-                   f"({frac:.0%}), {t_total:.1f} s; numpy fp64 BLAS"
+        "sample": (f"{done} matrices = {done // nmat} whole steps + {done % nmat} of the "
+                   f"{nmat} matrices of a step, {t_total:.1f} s; numpy fp64 BLAS"
                    + ("; Gram-space NS" if backend == "gram" else "")),
-        "ms_per_step_estimate": t_total / frac * 1e3,
+        "ms_per_step_estimate": t_total / (done / nmat) * 1e3,
     }
 
 
