@@ -76,7 +76,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
     for (int k = 0; k < RK; ++k) {
       const size_t idx = (size_t)(r0 + ry + 16 * k) * T.n + c0 + cx;
       gpre[k] = load4(T.src, T.in_dtype, idx);
-      if (!ns_only) bpre[k] = ld_f32x4(T.buf + idx);
+      if (!ns_only) bpre[k] = ld_f32x4_nt(T.buf + idx);
     }
   }
 
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
             bn[e] = fmaf(mu, b[e], g[e]);
             u[e] = nesterov ? fmaf(mu, bn[e], g[e]) : bn[e];
           }
-          st_f32x4(T.buf + idx, bn);
+          st_f32x4_nt(T.buf + idx, bn);
         }
       } else {
 #pragma unroll
@@ -988,11 +988,12 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
 // reads of 16 consecutive rows must cover the 16 groups of 4 banks once:
 // 128-byte rows pair up in a bank line (row parity picks the half), so the
 // slot is swizzled by r/2; a 256-byte row spans the whole line, swizzled by
-// r.  (Swizzling 128-byte rows by r mod 8 left a 2-way conflict: rocprofv3
-// counted 4 conflict cycles per 16-byte read.)
+// r; 64-byte rows (four to a line) by r/4.  (Swizzling 128-byte rows by
+// r mod 8 left a 2-way conflict: rocprofv3 counted 4 conflict cycles per
+// 16-byte read.)
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (CPR == 4) return ((r >> 1) ^ (r >> 2)) & 3;
+  if constexpr (CPR == 4) return (r >> 2) & 3;
   else if constexpr (CPR == 8) return (r >> 1) & 7;
   else return r & (CPR - 1);
 }

@@ -63,9 +63,9 @@ __device__ __forceinline__ void store4_tail(void* base, int dtype, int64_t i, in
                                             f32x4 x) {
   if (vec && i + 3 < n) {
     if (dtype == 0)
-      st_f32x4(static_cast<float*>(base) + i, x);
+      st_f32x4_nt(static_cast<float*>(base) + i, x);
     else
-      st_u32x2(static_cast<uint16_t*>(base) + i, pack_bf16x4(x[0], x[1], x[2], x[3]));
+      st_u32x2_nt(static_cast<uint16_t*>(base) + i, pack_bf16x4(x[0], x[1], x[2], x[3]));
     return;
   }
 #pragma unroll
