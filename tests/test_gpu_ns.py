@@ -74,6 +74,33 @@ def test_ns_f32_matches_oracle(coef):
         assert rel_frobenius(o, want) <= 1e-4, (s, rel_frobenius(o, want))
 
 
+@pytest.mark.parametrize("steps", [1, 2, 3, 4, 16])
+def test_ns_iteration_counts(steps):
+    """Odd and even iteration counts, 1 to the maximum of 16 (the quintic at
+    every step): the X operand buffers alternate between iterations and the
+    last iteration writes the output, so a wrong parity would show as an
+    O(1) error.  fp32 operands on 64- and 128-wide tiles; bf16 (automatic
+    mode) on 64-, 128- and 256-wide tiles for up to 4 steps.  Tolerances:
+    1e-4 (fp32; 1e-3 at 16 steps, where small singular values are amplified
+    by up to 3.44 per step before they converge) and 2e-2 (bf16)."""
+    f32_shapes = [(300, 200), (200, 300), (800, 1000), (1000, 800), (129, 129)]
+    gs_np = [_gen(s, 100 + i) for i, s in enumerate(f32_shapes)]
+    gin, outs = _run_ns(gs_np, "f32", "f32", ns_steps=steps)
+    for s, g, o in zip(f32_shapes, gin, outs):
+        want = oracle.direct_newton_schulz(g, steps=steps)
+        e = rel_frobenius(o, want)
+        assert e <= (1e-3 if steps > 5 else 1e-4), (s, steps, e)
+    if steps > 4:
+        return
+    bf_shapes = [(300, 200), (800, 1000), (1024, 1300), (1300, 1024)]
+    gs_np = [_gen(s, 110 + i) for i, s in enumerate(bf_shapes)]
+    gin, outs = _run_ns(gs_np, "bf16", "auto", ns_steps=steps)
+    for s, g, o in zip(bf_shapes, gin, outs):
+        want = oracle.direct_newton_schulz(g, steps=steps)
+        e = rel_frobenius(o, want)
+        assert e <= 2e-2, (s, steps, e)
+
+
 @pytest.mark.parametrize("prec", ["bf16_split", "auto"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ns_bf16_matches_oracle(prec, dtype):
