@@ -598,6 +598,14 @@ def main():
         # Gram backend these differ from the direct count the value is based on)
         "kernel_tflop_one_step": round(sum(v["flops"] for v in prof_all.rows.values()) / 1e12, 6),
         "ns_mfma_frac": round(ns_tflops / PEAK_TFLOPS[arith], 4),
+        # every kernel kind of one profiled warm-up step (HIP events around
+        # each launch): time, algorithmic rates and both roofline fractions
+        "kernels_one_step": {
+            k: {"ms": round(v["ms"], 4), "launches": v["launches"],
+                "tflop_s": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] else None,
+                "gb_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["ms"] else None,
+                **{f: roofline(v, arith)[f] for f in ("bound", "mfma_frac", "hbm_frac")}}
+            for k, v in prof_all.rows.items() if v["ms"] > 0},
         "matrices_per_s": round(len(shapes) / (ms_step * 1e-3), 1),
         "kernel_ms_one_step": {k: round(v["ms"], 4) for k, v in prof_all.rows.items()},
         "roofline": roof,
