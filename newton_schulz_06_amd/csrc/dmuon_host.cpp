@@ -580,9 +580,11 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.out0 = L.f32_ops ? nullptr : ws + G.aop;
           t.ld0 = (int32_t)G.ld_aop;
           flops += p * (p + 1) * q;
-          // X operand in; fp32 A and/or its operand form out
+          // X operand in; fp32 A (bf16 operands: upper triangle only) and/or
+          // its operand form out
           bytes += (L.f32_ops ? 4.0 : 2.0) * p * q +
-                   p * p * (L.f32_ops ? 4.0 : G.split_a ? 8.0 : 6.0);
+                   (L.f32_ops ? 4.0 * p * p
+                              : G.split_a ? 8.0 * p * p : 2.0 * p * p + 2.0 * p * (p + 1));
         } else if (kind == KIND_POLY) {
           t.split = G.split_b;  // writes B as [hi|lo]
           // Split A: L = columns 0..3P of the [hi|lo|hi|hi] rows, R =

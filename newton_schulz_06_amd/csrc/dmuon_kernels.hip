@@ -349,10 +349,13 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
         if constexpr (KIND == KIND_SYRK) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) v[rr] *= s;
-          if (!G.split) {  // fp32 A, read back by the polynomial epilogue
+          if (!G.split) {
+            // fp32 A: with bf16 operands only the polynomial epilogue reads
+            // it, on upper tiles, so the mirrored tile is written only when
+            // A is itself the fp32 operand
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) st_f32(F + (size_t)(gi + rr) * ldf + gj, v[rr]);
-            if (mirror) st_f32x4(F + (size_t)gj * ldf + gi, v);
+            if (F32 && mirror) st_f32x4(F + (size_t)gj * ldf + gi, v);
           }
           if constexpr (!F32) {
             uint16_t* o0 = static_cast<uint16_t*>(G.out0);
