@@ -457,7 +457,9 @@ constexpr bool kHiLoMaster = T < 256;
 // The master X at (r, c): fp32, or xb + xlo (both bf16).
 template <bool F32, bool HL>
 __device__ __forceinline__ float load_master(const GemmTask& G, int r, int c) {
-  if constexpr (F32 || !HL) {
+  if constexpr (!F32 && !HL) {  // 256-wide tiles: streamed (see ld_f32_nt)
+    return ld_f32_nt(G.fbuf + (size_t)r * G.ld_f + c);
+  } else if constexpr (F32) {
     return ld_f32(G.fbuf + (size_t)r * G.ld_f + c);
   } else {
     const size_t o = (size_t)r * G.ld0 + c;
@@ -513,11 +515,11 @@ __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[N
           st_f32x4(static_cast<float*>(xt_next) + (size_t)gj * ld1 + gi, v);
         } else if constexpr (!HL) {
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) st_f32(X + (size_t)(gi + rr) * ldf + gj, v[rr]);
+          for (int rr = 0; rr < 4; ++rr) st_f32_nt(X + (size_t)(gi + rr) * ldf + gj, v[rr]);
           uint16_t* xb = static_cast<uint16_t*>(G.out0);
           const int ld0 = G.ld0;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) st_u16(xb + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
+          for (int rr = 0; rr < 4; ++rr) st_u16_nt(xb + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
           const int il = gi - tm * T, jl = gj - tn * T;
           const int x = 4 * (jl & (T / 4 - 1));
           *reinterpret_cast<u32x2*>(stage + jl * T + (il ^ x)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
