@@ -14,10 +14,16 @@
  *   argument).  Pointers are device pointers on the current HIP device,
  *   aligned at least to their element size.
  * - The caller owns every buffer (params, grads, momentum buffers, outputs,
- *   workspace).  The library keeps no pointer after the enqueued work ends,
- *   except a small per-device cache of launch tables keyed by the shapes and
- *   pointers of a call (allocated on the first call with a new key, reused
- *   afterwards).
+ *   workspace).  The library keeps no pointer after the enqueued work ends.
+ *   It keeps one per-device cache of launch tables keyed by the shapes and
+ *   options of a call (never by its pointers): the first call with a new
+ *   batch layout allocates and uploads that layout's table (a hipMalloc and
+ *   a blocking copy); every later call with the same layout, whatever its
+ *   buffers and workspace, allocates nothing and does not synchronize.  The
+ *   call's buffer pointers travel to the device in kernel arguments (a
+ *   small upload kernel writes them into the workspace) ahead of the
+ *   call's kernels on `stream`.  Past 256 distinct layouts per process the
+ *   least recently used table is freed (after a device synchronization).
  * - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *   the default stream).  The workspace must stay alive until that work
  *   completes.
@@ -297,6 +303,11 @@ dmuon_status_t dmuon_adamw_step(const dmuon_batch_t* params,
                                 int64_t step, double lr, double beta1, double beta2,
                                 double eps, double weight_decay, void* stream);
 
+/* Number of launch tables built so far in this process (see the cache
+ * described at the top): a caller can check that its steady state builds
+ * none.  Thread-safe. */
+int64_t dmuon_plan_builds(void);
+
 /* Static string for a status code. */
 const char* dmuon_status_str(dmuon_status_t status);
 
@@ -322,9 +333,10 @@ const char* dmuon_backend_info(void);
  * written once in the library's workspace layout (for the element-wise
  * kernels, the bytes the step must move at minimum).
  * Kinds: 0 momentum, 1 input, 2 norm, 3 syrk, 4 poly, 5 update_x,
- * 6 clip_norm, 7 clip_scale, 8 adamw.  The last update_x launch of a call
- * also applies the parameter update (or writes the NS output), so there is
- * no separate update kind.
+ * 6 clip_norm, 7 clip_scale, 8 adamw, 9 gram_mul (a product of two commuting
+ * symmetric p x p factors of Gram-space NS).  The last update_x launch of a
+ * call also applies the parameter update (or writes the NS output), so there
+ * is no separate update kind.
  */
 typedef struct {
   char name[24];

@@ -65,7 +65,7 @@ EXPORTS = ("dmuon_ns_workspace_size", "dmuon_ns_orthogonalize", "dmuon_muon_step
            "dmuon_gram_local_begin", "dmuon_gram_local_advance",
            "dmuon_clip_workspace_size", "dmuon_clip_grad_norm", "dmuon_adamw_step",
            "dmuon_status_str", "dmuon_last_error", "dmuon_backend_info",
-           "dmuon_profile_begin", "dmuon_profile_end")
+           "dmuon_profile_begin", "dmuon_profile_end", "dmuon_plan_builds")
 
 _lib = None
 
@@ -133,6 +133,8 @@ def lib():
     L.dmuon_profile_begin.restype = ctypes.c_int32
     L.dmuon_profile_end.argtypes = [ctypes.POINTER(ProfileRow), ctypes.c_int32]
     L.dmuon_profile_end.restype = ctypes.c_int32
+    L.dmuon_plan_builds.argtypes = []
+    L.dmuon_plan_builds.restype = ctypes.c_int64
     _lib = L
     return L
 
@@ -262,10 +264,25 @@ def alloc_workspace(shapes, prec="bf16", device="cuda", backend="direct"):
                        device=device)
 
 
-def _ws(workspace, shapes, prec, device, backend="direct"):
+def _ws(workspace, shapes, prec, device, backend="direct", stream=None):
+    """The caller's workspace, or a new one for this call.  A new one is
+    allocated with `stream` current, so torch's caching allocator keeps the
+    block for work on that stream: the kernels still use it after the call
+    returns, and a block freed from another stream could be handed out again
+    while they run."""
     if workspace is None:
-        workspace = alloc_workspace(shapes, prec, device, backend)
+        import torch
+        if stream is None:
+            workspace = alloc_workspace(shapes, prec, device, backend)
+        else:
+            with torch.cuda.stream(stream):
+                workspace = alloc_workspace(shapes, prec, device, backend)
     return workspace, ctypes.c_void_p(int(workspace.data_ptr())), int(workspace.numel())
+
+
+def plan_builds() -> int:
+    """dmuon_plan_builds: launch tables built so far in this process."""
+    return int(lib().dmuon_plan_builds())
 
 
 def ns_orthogonalize(gs, outs=None, *, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
@@ -281,7 +298,8 @@ def ns_orthogonalize(gs, outs=None, *, coefficients=None, ns_steps=5, eps=1e-7, 
     bo, ko = make_batch(outs)
     cfg, kc = make_cfg(coefficients, ns_steps, eps, prec, backend, restart_iterations)
     device = gs[0].device if gs else "cuda"
-    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in gs], prec, device, backend)
+    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in gs], prec, device, backend,
+                           stream)
     _check(lib().dmuon_ns_orthogonalize(ctypes.byref(bg), ctypes.byref(bo), ctypes.byref(cfg),
                                         wptr, wbytes, _stream_handle(stream)))
     return outs
@@ -298,7 +316,8 @@ def muon_step(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_decay=0.0, 
     bb, kb = make_batch(bufs)
     cfg, kc = make_cfg(coefficients, ns_steps, eps, prec, backend, restart_iterations)
     device = grads[0].device if grads else "cuda"
-    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in grads], prec, device, backend)
+    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in grads], prec, device, backend,
+                           stream)
     _check(lib().dmuon_muon_step(ctypes.byref(bp), ctypes.byref(bg), ctypes.byref(bb),
                                  ctypes.byref(cfg), float(momentum), float(lr),
                                  float(weight_decay), int(bool(nesterov)), wptr, wbytes,
@@ -353,7 +372,8 @@ class PreparedMuonStep:
         self.cfg, k = make_cfg(coefficients, ns_steps, eps, prec, backend, restart_iterations)
         self._keep.append(k)
         shapes = [tuple(p.shape) for p in params]
-        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, params[0].device, backend)
+        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, params[0].device, backend,
+                                              stream)
         self.stream = _stream_handle(stream)
         self.scalars = (ctypes.c_float(momentum), ctypes.c_float(lr),
                         ctypes.c_float(weight_decay), ctypes.c_int32(int(bool(nesterov))))
@@ -376,7 +396,8 @@ class PreparedNs:
         self.cfg, self._kc = make_cfg(coefficients, ns_steps, eps, prec, backend,
                                       restart_iterations)
         shapes = [tuple(g.shape) for g in gs]
-        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, gs[0].device, backend)
+        self.ws, self.wptr, self.wbytes = _ws(workspace, shapes, prec, gs[0].device, backend,
+                                              stream)
         self.stream = _stream_handle(stream)
         self.fn = lib().dmuon_ns_orthogonalize
 
@@ -429,8 +450,11 @@ class GramLocal:
         shapes = [tuple(g.shape) for g in g_locals]
         if workspace is None:
             device = g_locals[0].device if g_locals else "cuda"
-            workspace = torch.empty(max(1, gram_local_workspace_size(shapes, transposed, prec)),
-                                    dtype=torch.uint8, device=device)
+            nbytes = max(1, gram_local_workspace_size(shapes, transposed, prec))
+            # allocated with the launch stream current (see _ws)
+            with torch.cuda.stream(stream if stream is not None
+                                   else torch.cuda.current_stream(device)):
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.ws = workspace
         self.wptr = ctypes.c_void_p(int(workspace.data_ptr()))
         self.wbytes = int(workspace.numel())

@@ -82,7 +82,9 @@ struct Geom {
 
 struct Layout {
   std::vector<Geom> g;
-  size_t partial_off = 0, scale_off = 0, sink_off = 0, total = 0;
+  // slot_off: the call's buffer pointers, kSlotsPerMat per matrix (written
+  // by launch_upload at the start of every call)
+  size_t partial_off = 0, scale_off = 0, sink_off = 0, slot_off = 0, total = 0;
   int64_t in_tiles = 0;
   int f32_ops = 0;
   int gram = 0;  // Gram-space NS layout (fp32 operands)
@@ -135,6 +137,8 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
   off = align_up(off + sizeof(float) * 4 * (size_t)n, kWsAlign);
   L.sink_off = off;  // writable bytes nothing reads (padding lanes' stores)
   off = align_up(off + 16, kWsAlign);
+  L.slot_off = off;
+  off = align_up(off + sizeof(void*) * kSlotsPerMat * (size_t)n, kWsAlign);
   if (L.local) {
     L.bucket_off = off;
     off = align_up(off + sizeof(float) * (size_t)n, kWsAlign);
@@ -321,8 +325,11 @@ enum GramGroup : int {
 
 struct Plan {
   std::vector<int64_t> key;
+  uint64_t hash = 0;
   int device = -1;
-  void* dtab = nullptr;
+  void* dtab = nullptr;            // device copy of `image`
+  bool owns_dtab = true;           // dtab is this plan's own allocation
+  std::vector<char> image;         // the launch tables (host copy)
   int f32_ops = 0;
   int gram = 0;
   int local = 0;
@@ -331,7 +338,7 @@ struct Plan {
   double in_bytes = 0, norm_bytes = 0, fin_bytes = 0;
   std::vector<GemmLaunch> gemms;  // SYRK launches, then POLY, then UPDX
   ~Plan() {
-    if (dtab) {
+    if (dtab && owns_dtab) {
       int cur = -1;
       (void)hipGetDevice(&cur);
       (void)hipSetDevice(device);
@@ -344,9 +351,20 @@ struct Plan {
 
 std::mutex g_plan_mu;
 // Most recently used last.  Never destroyed: freeing device memory from a
-// static destructor could run after the HIP runtime has shut down.
+// static destructor could run after the HIP runtime has shut down.  Plans
+// are keyed by shapes and options only, so a training loop uses one per
+// batch layout; the eviction (a device synchronization and a free) happens
+// only past kMaxPlans distinct layouts.
 std::vector<std::unique_ptr<Plan>>& g_plans = *new std::vector<std::unique_ptr<Plan>>();
-constexpr size_t kMaxPlans = 32;
+constexpr size_t kMaxPlans = 256;
+// Plans built so far (dmuon_plan_builds).
+int64_t g_plan_builds = 0;
+
+// Slot Refs of matrix i's caller buffers.
+Ref src_slot(int i) { return ref_slot(kSlotsPerMat * i + 0); }
+Ref dst_slot(int i) { return ref_slot(kSlotsPerMat * i + 1); }
+Ref buf_slot(int i) { return ref_slot(kSlotsPerMat * i + 2); }
+Ref wsr(size_t off) { return (Ref)off; }
 
 bool vec_ok(const void* p, int dtype, int64_t n) {
   const size_t need = dtype == DMUON_F32 ? 16 : 8;
@@ -355,11 +373,14 @@ bool vec_ok(const void* p, int dtype, int64_t n) {
 
 // Gram-space NS launch groups (fp32 operands), appended to `gtasks`: one
 // group per (product, buffers), split by tile class like the direct kinds.
-void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, char* ws,
-                       float* scale, Plan* plan, std::vector<GemmTask>& gtasks,
+void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, Plan* plan,
+                       std::vector<GemmTab>& gtasks,
                        std::vector<std::pair<size_t, size_t>>& ranges) {
   const int n = (int)L.g.size();
-  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  auto none = [](GemmTab& t) {
+    t.L = t.R0 = t.R1 = t.fbuf = t.out0 = t.out1 = t.out2 = t.scale = t.xlo = t.ahl = t.sink =
+        t.dst = kRefNone;
+  };
   // `fill` sets the product-specific fields of one matrix's task and adds
   // its algorithmic flops and bytes.
   auto add_group = [&](int group, int kind, auto&& fill) {
@@ -370,9 +391,10 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
       for (int i = 0; i < n; ++i) {
         const Geom& G = L.g[i];
         if (G.tile != tile) continue;
-        GemmTask t{};
+        GemmTab t{};
+        none(t);
         t.P = (int)G.P;
-        t.scale = scale + 4 * i;
+        t.scale = wsr(L.scale_off + 16 * (size_t)i);
         const int nt = (int)G.P / tile;
         t.tiles_m = t.tiles_n = nt;
         t.tri = 1;
@@ -393,21 +415,21 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
   };
   using D = double;
   // A = X X^T (scaled by 1/(||u||+eps)^2 on the first window)
-  add_group(GG_SYRK, KIND_SYRK, [&](GemmTask& t, const Geom& G, int, int, D& f, D& b, D&) {
-    t.L = t.R0 = t.R1 = ws + G.xm;
+  add_group(GG_SYRK, KIND_SYRK, [&](GemmTab& t, const Geom& G, int, int, D& f, D& b, D&) {
+    t.L = t.R0 = t.R1 = wsr(G.xm);
     t.ldl = t.ldr = (int32_t)G.ld_xm;
     t.K = t.kper = (int)G.Q;
-    t.fbuf = f32(G.a32);
+    t.fbuf = wsr(G.a32);
     const D p = (D)G.p, q = (D)G.q;
     f += p * (p + 1) * q;
     b += 4 * p * q + 4 * p * p;
   });
   // P = a I + b A + c A^2 (reads A as both operands and for the b A term)
   for (int g : {GG_P_QA, GG_P_PM})
-    add_group(g, KIND_POLY, [&](GemmTask& t, const Geom& G, int, int, D& f, D& b, D&) {
-      t.L = t.R0 = t.R1 = ws + G.a32;
-      t.fbuf = f32(G.a32);
-      t.out0 = ws + (g == GG_P_QA ? G.qa : G.pm);
+    add_group(g, KIND_POLY, [&](GemmTab& t, const Geom& G, int, int, D& f, D& b, D&) {
+      t.L = t.R0 = t.R1 = wsr(G.a32);
+      t.fbuf = wsr(G.a32);
+      t.out0 = wsr(g == GG_P_QA ? G.qa : G.pm);
       t.add_diag = 1;
       const D p = (D)G.p;
       f += p * p * (p + 1);
@@ -422,10 +444,10 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
                       {GG_Q_AB, &Geom::pm, &Geom::qa, &Geom::qb},
                       {GG_Q_BA, &Geom::pm, &Geom::qb, &Geom::qa}};
   for (const Mul& mu : muls)
-    add_group(mu.group, KIND_GRAMMUL, [&](GemmTask& t, const Geom& G, int, int, D& f, D& b, D&) {
-      t.L = ws + G.*mu.l;
-      t.R0 = t.R1 = ws + G.*mu.r;
-      t.out0 = ws + G.*mu.out;
+    add_group(mu.group, KIND_GRAMMUL, [&](GemmTab& t, const Geom& G, int, int, D& f, D& b, D&) {
+      t.L = wsr(G.*mu.l);
+      t.R0 = t.R1 = wsr(G.*mu.r);
+      t.out0 = wsr(G.*mu.out);
       const D p = (D)G.p;
       f += p * p * (p + 1);
       b += 12 * p * p;
@@ -433,11 +455,11 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
   // X = Q X at a window's end (the X update with a = 0); the last window
   // writes the caller's matrix
   for (int g : {GG_QX_QA, GG_QX_QB})
-    add_group(g, KIND_UPDX, [&](GemmTask& t, const Geom& G, int i, int tile, D& f, D& b,
+    add_group(g, KIND_UPDX, [&](GemmTab& t, const Geom& G, int i, int tile, D& f, D& b,
                                 D& bfin) {
-      t.L = ws + (g == GG_QX_QA ? G.qa : G.qb);
-      t.R0 = ws + G.xt0;
-      t.R1 = ws + G.xt1;
+      t.L = wsr(g == GG_QX_QA ? G.qa : G.qb);
+      t.R0 = wsr(G.xt0);
+      t.R1 = wsr(G.xt1);
       t.ldl = (int32_t)G.ld_a32;
       t.ldr = (int32_t)G.ld_xt;
       t.K = t.kper = (int)G.P;
@@ -445,17 +467,17 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
       t.tiles_n = (int)G.Q / tile;
       t.tri = 0;
       t.tile_count = t.tiles_m * t.tiles_n;
-      t.fbuf = f32(G.xm);
+      t.fbuf = wsr(G.xm);
       t.ld_f = (int32_t)G.ld_xm;
-      t.out1 = ws + G.xt0;
-      t.out2 = ws + G.xt1;
+      t.out1 = wsr(G.xt0);
+      t.out2 = wsr(G.xt1);
       t.ld1 = (int32_t)G.ld_xt;
-      t.dst = dst->mats[i].ptr;
+      t.dst = dst_slot(i);
       t.pv = (int32_t)G.p;
       t.qv = (int32_t)G.q;
       t.dst_trans = G.transposed;
       t.dst_dtype = dst->dtype;
-      t.sink = ws + L.sink_off;
+      t.sink = wsr(L.sink_off);
       const D p = (D)G.p, q = (D)G.q;
       f += 2 * p * p * q;
       const D in = 4 * p * p + 8 * p * q;  // Q, X^T, and X (read for the a X term)
@@ -465,26 +487,28 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
 }
 
 // Builds the launch tables for one call shape and uploads them.
+// `upload`: allocate the plan's device copy of its tables and copy them
+// there (blocking); otherwise the caller places plan->image itself.
 dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_batch_t* dst,
-                          const dmuon_batch_t* bufs, bool ns_only, char* ws, int device,
-                          std::vector<int64_t> key, Plan** out) {
+                          const dmuon_batch_t* bufs, bool ns_only, int device,
+                          std::vector<int64_t> key, uint64_t hash, bool upload, Plan** out) {
   auto plan = std::make_unique<Plan>();
   plan->key = std::move(key);
+  plan->hash = hash;
   plan->device = device;
   plan->f32_ops = L.f32_ops;
   plan->gram = L.gram;
   plan->local = L.local;
   const int n = src->count;
   plan->nmat = n;
-  float* partial = reinterpret_cast<float*>(ws + L.partial_off);
-  float* scale = reinterpret_cast<float*>(ws + L.scale_off);
+  auto scale = [&](int i) { return wsr(L.scale_off + 16 * (size_t)i); };
 
-  std::vector<EwTask> tin(n);
-  std::vector<NormTask> tnorm(n);
+  std::vector<EwTab> tin(n);
+  std::vector<NormTab> tnorm(n);
   int in_begin = 0;
   for (int i = 0; i < n; ++i) {
     const Geom& G = L.g[i];
-    EwTask t{};
+    EwTab t{};
     t.m = (int32_t)G.m;
     t.n = (int32_t)G.n;
     t.transposed = G.transposed;
@@ -493,40 +517,38 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
     t.ldxb = (int32_t)G.ld_xb;
     t.ldt = (int32_t)G.ld_xt;
     t.f32_ops = L.f32_ops;
-    t.src = src->mats[i].ptr;
-    t.buf = bufs ? static_cast<float*>(bufs->mats[i].ptr) : nullptr;
-    t.xm = G.hilo ? nullptr : reinterpret_cast<float*>(ws + G.xm);
-    t.xb = L.f32_ops ? nullptr : reinterpret_cast<uint16_t*>(ws + G.xb);
-    t.xlo = G.hilo ? reinterpret_cast<uint16_t*>(ws + G.xlo) : nullptr;
-    t.xt = ws + G.xt0;
-    t.partial = partial;
-    t.scale = scale + 4 * i;
+    t.src = src_slot(i);
+    t.buf = bufs ? buf_slot(i) : kRefNone;
+    t.xm = G.hilo ? kRefNone : wsr(G.xm);
+    t.xb = L.f32_ops ? kRefNone : wsr(G.xb);
+    t.xlo = G.hilo ? wsr(G.xlo) : kRefNone;
+    t.xt = wsr(G.xt0);
+    t.partial = wsr(L.partial_off);
+    t.scale = scale(i);
     // input pass: padded oriented extents, mapped to the caller's layout
-    EwTask a = t;
+    EwTab a = t;
     a.rows = (int32_t)(G.transposed ? G.Q : G.P);
     a.cols = (int32_t)(G.transposed ? G.P : G.Q);
     a.tiles_c = a.cols / EW_TILE;
     a.tile_begin = in_begin;
     a.tile_count = (a.rows / EW_TILE) * a.tiles_c;
-    a.vec = vec_ok(t.src, src->dtype, G.n) && (!bufs || vec_ok(t.buf, DMUON_F32, G.n));
     in_begin += a.tile_count;
     tin[i] = a;
-    tnorm[i] = NormTask{a.tile_begin, a.tile_count, partial, scale + 4 * i,
-                        L.local ? reinterpret_cast<float*>(ws + L.bucket_off) + i : nullptr};
+    tnorm[i] = NormTab{a.tile_begin, a.tile_count, wsr(L.partial_off), scale(i),
+                       L.local ? wsr(L.bucket_off + sizeof(float) * i) : kRefNone};
     const double mn = (double)G.m * (double)G.n;
     plan->in_bytes += ns_only ? mn * esize(src->dtype) : mn * (esize(src->dtype) + 8.0);
     plan->norm_bytes += 4.0 * a.tile_count;
   }
   plan->in_tiles = in_begin;
-  std::vector<FinTask> tfin;
+  std::vector<FinTab> tfin;
   if (L.local) {
     int blk = 0;
     for (int i = 0; i < n; ++i) {
       const Geom& G = L.g[i];
       const int nb = (int)((G.P + FIN_ROWS - 1) / FIN_ROWS);
-      tfin.push_back(FinTask{blk, nb, (int32_t)G.P, (int32_t)G.ld_a32,
-                             reinterpret_cast<float*>(ws + G.a32),
-                             reinterpret_cast<float*>(ws + L.bucket_off) + i, scale + 4 * i});
+      tfin.push_back(FinTab{blk, nb, (int32_t)G.P, (int32_t)G.ld_a32, wsr(G.a32),
+                            wsr(L.bucket_off + sizeof(float) * i), scale(i)});
       blk += nb;
       plan->fin_bytes += 8.0 * (double)G.p * (double)G.p;
     }
@@ -534,10 +556,10 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   }
 
   // GEMM tasks, grouped by (kind, tile class).
-  std::vector<GemmTask> gtasks;
+  std::vector<GemmTab> gtasks;
   const int kinds_direct[3] = {KIND_SYRK, KIND_POLY, KIND_UPDX};
   std::vector<std::pair<size_t, size_t>> ranges;  // [begin, end) in gtasks per launch
-  if (L.gram) build_gram_groups(L, dst, ns_only, ws, scale, plan.get(), gtasks, ranges);
+  if (L.gram) build_gram_groups(L, dst, ns_only, plan.get(), gtasks, ranges);
   for (int kind : (L.gram ? std::vector<int>() : std::vector<int>(kinds_direct, kinds_direct + 3))) {
     for (int tile : kTiles) {
       // 128-deep stages for a 64-wide SYRK or polynomial launch (bf16) whose
@@ -560,14 +582,16 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
       for (int i = 0; i < n; ++i) {
         const Geom& G = L.g[i];
         if (G.tile != tile) continue;
-        GemmTask t{};
+        GemmTab t{};
+        t.L = t.R0 = t.R1 = t.fbuf = t.out0 = t.out1 = t.out2 = t.scale = t.xlo = t.ahl =
+            t.sink = t.dst = kRefNone;
         const int P = (int)G.P, Q = (int)G.Q;
         const int nt = P / tile;
         const double p = (double)G.p, q = (double)G.q;
         t.P = P;
-        t.scale = scale + 4 * i;
+        t.scale = scale(i);
         if (kind == KIND_SYRK) {
-          t.L = ws + (L.f32_ops ? G.xm : G.xb);
+          t.L = wsr(L.f32_ops ? G.xm : G.xb);
           t.R0 = t.R1 = t.L;
           t.ldl = t.ldr = (int32_t)(L.f32_ops ? G.ld_xm : G.ld_xb);
           t.K = t.kper = Q;
@@ -575,9 +599,9 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.tri = 1;
           t.tile_count = nt * (nt + 1) / 2;
           t.split = G.split_a;  // writes A as [hi|lo|hi|hi] rows, no fp32 A
-          t.fbuf = t.split ? nullptr : reinterpret_cast<float*>(ws + G.a32);
+          t.fbuf = t.split ? kRefNone : wsr(G.a32);
           t.ld_f = (int32_t)G.ld_a32;
-          t.out0 = L.f32_ops ? nullptr : ws + G.aop;
+          t.out0 = L.f32_ops ? kRefNone : wsr(G.aop);
           t.ld0 = (int32_t)G.ld_aop;
           flops += p * (p + 1) * q;
           // X operand in; fp32 A (bf16 operands: upper triangle only) and/or
@@ -589,27 +613,27 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.split = G.split_b;  // writes B as [hi|lo]
           // Split A: L = columns 0..3P of the [hi|lo|hi|hi] rows, R =
           // columns P..4P, so L R^T = hi lo^T + lo hi^T + hi hi^T.
-          t.L = ws + G.aop;
-          t.R0 = t.R1 = ws + G.aop + (G.split_a ? 2 * (size_t)P : 0);
+          t.L = wsr(G.aop);
+          t.R0 = t.R1 = wsr(G.aop + (G.split_a ? 2 * (size_t)P : 0));
           t.ldl = t.ldr = (int32_t)G.ld_aop;
           t.K = t.kper = G.split_a ? 3 * P : P;
           t.tiles_m = t.tiles_n = nt;
           t.tri = 1;
           t.tile_count = nt * (nt + 1) / 2;
-          t.fbuf = G.split_a ? nullptr : reinterpret_cast<float*>(ws + G.a32);
+          t.fbuf = G.split_a ? kRefNone : wsr(G.a32);
           t.ld_f = (int32_t)G.ld_a32;
-          t.ahl = G.split_a ? reinterpret_cast<const uint16_t*>(ws + G.aop) : nullptr;
+          t.ahl = G.split_a ? wsr(G.aop) : kRefNone;
           t.ld_ahl = (int32_t)G.ld_aop;
-          t.out0 = ws + G.bop;
+          t.out0 = wsr(G.bop);
           t.ld0 = (int32_t)G.ld_bop;
           flops += p * p * (p + 1);
           // A in (fp32; bf16 + fp32; or the split rows); B operand out
           bytes += p * p * ((L.f32_ops ? 4.0 : G.split_a ? 8.0 : 6.0) +
                             (L.f32_ops ? 4.0 : G.split_b ? 4.0 : 2.0));
         } else {
-          t.L = ws + G.bop;
-          t.R0 = ws + G.xt0;
-          t.R1 = ws + G.xt1;
+          t.L = wsr(G.bop);
+          t.R0 = wsr(G.xt0);
+          t.R1 = wsr(G.xt1);
           t.ldl = (int32_t)G.ld_bop;
           t.ldr = (int32_t)G.ld_xt;
           t.K = G.split_b ? 2 * P : P;
@@ -618,16 +642,16 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.tiles_n = Q / tile;
           t.tri = 0;
           t.tile_count = t.tiles_m * t.tiles_n;
-          t.fbuf = G.hilo ? nullptr : reinterpret_cast<float*>(ws + G.xm);
+          t.fbuf = G.hilo ? kRefNone : wsr(G.xm);
           t.ld_f = (int32_t)G.ld_xm;
-          t.out0 = L.f32_ops ? nullptr : ws + G.xb;
-          t.xlo = G.hilo ? reinterpret_cast<uint16_t*>(ws + G.xlo) : nullptr;
+          t.out0 = L.f32_ops ? kRefNone : wsr(G.xb);
+          t.xlo = G.hilo ? wsr(G.xlo) : kRefNone;
           t.ld0 = (int32_t)G.ld_xb;
-          t.sink = ws + L.sink_off;
-          t.out1 = ws + G.xt0;
-          t.out2 = ws + G.xt1;
+          t.sink = wsr(L.sink_off);
+          t.out1 = wsr(G.xt0);
+          t.out2 = wsr(G.xt1);
           t.ld1 = (int32_t)G.ld_xt;
-          t.dst = dst->mats[i].ptr;
+          t.dst = dst_slot(i);
           t.pv = (int32_t)G.p;
           t.qv = (int32_t)G.q;
           t.dst_trans = G.transposed;
@@ -665,19 +689,25 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
     off = align_up(off + bytes, 64);
     return o;
   };
-  plan->in_off = place(sizeof(EwTask) * n);
-  plan->norm_off = place(sizeof(NormTask) * n);
-  plan->fin_off = place(sizeof(FinTask) * tfin.size());
-  const size_t g_off = place(sizeof(GemmTask) * gtasks.size());
+  plan->in_off = place(sizeof(EwTab) * n);
+  plan->norm_off = place(sizeof(NormTab) * n);
+  plan->fin_off = place(sizeof(FinTab) * tfin.size());
+  const size_t g_off = place(sizeof(GemmTab) * gtasks.size());
   for (size_t k = 0; k < plan->gemms.size(); ++k)
-    plan->gemms[k].off = g_off + sizeof(GemmTask) * ranges[k].first;
-  std::vector<char> host(off);
-  std::memcpy(host.data() + plan->in_off, tin.data(), sizeof(EwTask) * n);
-  std::memcpy(host.data() + plan->norm_off, tnorm.data(), sizeof(NormTask) * n);
+    plan->gemms[k].off = g_off + sizeof(GemmTab) * ranges[k].first;
+  std::vector<char>& host = plan->image;
+  host.assign(off, 0);
+  std::memcpy(host.data() + plan->in_off, tin.data(), sizeof(EwTab) * n);
+  std::memcpy(host.data() + plan->norm_off, tnorm.data(), sizeof(NormTab) * n);
   if (!tfin.empty())
-    std::memcpy(host.data() + plan->fin_off, tfin.data(), sizeof(FinTask) * tfin.size());
+    std::memcpy(host.data() + plan->fin_off, tfin.data(), sizeof(FinTab) * tfin.size());
   if (!gtasks.empty())
-    std::memcpy(host.data() + g_off, gtasks.data(), sizeof(GemmTask) * gtasks.size());
+    std::memcpy(host.data() + g_off, gtasks.data(), sizeof(GemmTab) * gtasks.size());
+  if (!upload) {
+    plan->owns_dtab = false;
+    *out = plan.release();
+    return DMUON_OK;
+  }
   hipError_t e = hipMalloc(&plan->dtab, off);
   if (e != hipSuccess) {
     plan->dtab = nullptr;
@@ -690,14 +720,17 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   return DMUON_OK;
 }
 
-// Looks up (or builds) the plan; caller holds g_plan_mu.
+// Looks up (or builds) the plan of a call's shapes and options; caller
+// holds g_plan_mu.  Nothing in the key depends on the call's pointers: a
+// later call with other buffers (or another workspace) of the same shapes
+// reuses the plan without touching device memory.
 dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_batch_t* dst,
-                        const dmuon_batch_t* bufs, bool ns_only, char* ws, Plan** out) {
+                        const dmuon_batch_t* bufs, bool ns_only, Plan** out) {
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
   std::vector<int64_t> key;
-  key.reserve(8 + 5 * (size_t)src->count);
+  key.reserve(10 + 3 * (size_t)src->count);
   key.push_back(device);
   key.push_back(ns_only);
   key.push_back(L.f32_ops);
@@ -705,31 +738,56 @@ dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_b
   key.push_back(L.local);
   key.push_back(src->dtype);
   key.push_back(dst->dtype);
-  key.push_back((int64_t)reinterpret_cast<uintptr_t>(ws));
+  key.push_back(bufs != nullptr);
   key.push_back(src->count);
   for (int i = 0; i < src->count; ++i) {
     key.push_back(src->mats[i].m);
     key.push_back(src->mats[i].n);
-    key.push_back((int64_t)reinterpret_cast<uintptr_t>(src->mats[i].ptr));
-    key.push_back((int64_t)reinterpret_cast<uintptr_t>(dst->mats[i].ptr));
-    key.push_back(bufs ? (int64_t)reinterpret_cast<uintptr_t>(bufs->mats[i].ptr) : 0);
     key.push_back(L.g[i].split_a + 2 * L.g[i].split_b + 4 * L.g[i].transposed);
   }
-  for (size_t k = 0; k < g_plans.size(); ++k) {
-    if (g_plans[k]->key == key) {
-      std::unique_ptr<Plan> hit = std::move(g_plans[k]);
-      g_plans.erase(g_plans.begin() + (long)k);
-      g_plans.push_back(std::move(hit));
+  uint64_t hash = 1469598103934665603ull;  // FNV-1a over the key words
+  for (int64_t w : key) {
+    hash ^= (uint64_t)w;
+    hash *= 1099511628211ull;
+  }
+  for (size_t k = g_plans.size(); k-- > 0;) {
+    if (g_plans[k]->hash == hash && g_plans[k]->key == key) {
+      if (k + 1 != g_plans.size()) {
+        std::unique_ptr<Plan> hit = std::move(g_plans[k]);
+        g_plans.erase(g_plans.begin() + (long)k);
+        g_plans.push_back(std::move(hit));
+      }
       *out = g_plans.back().get();
       return DMUON_OK;
     }
   }
   Plan* p = nullptr;
-  dmuon_status_t st = build_plan(L, src, dst, bufs, ns_only, ws, device, std::move(key), &p);
+  dmuon_status_t st =
+      build_plan(L, src, dst, bufs, ns_only, device, std::move(key), hash, true, &p);
   if (st != DMUON_OK) return st;
+  ++g_plan_builds;
   if (g_plans.size() >= kMaxPlans) g_plans.erase(g_plans.begin());
   g_plans.emplace_back(p);
   *out = p;
+  return DMUON_OK;
+}
+
+// Uploads the call's buffer pointers into the workspace's slot array (see
+// Bases), stream-ordered before the call's kernels.
+dmuon_status_t upload_slots(const Layout& L, const dmuon_batch_t* src, const dmuon_batch_t* dst,
+                            const dmuon_batch_t* bufs, char* ws, hipStream_t s, Bases* b) {
+  const int n = src->count;
+  std::vector<void*> v((size_t)kSlotsPerMat * n, nullptr);
+  for (int i = 0; i < n; ++i) {
+    v[kSlotsPerMat * i + 0] = src->mats[i].ptr;
+    v[kSlotsPerMat * i + 1] = dst->mats[i].ptr;
+    v[kSlotsPerMat * i + 2] = bufs ? bufs->mats[i].ptr : nullptr;
+  }
+  void** slots = reinterpret_cast<void**>(ws + L.slot_off);
+  const hipError_t e = launch_upload(slots, v.data(), sizeof(void*) * v.size(), s);
+  if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("pointer upload: ") + hipGetErrorString(e));
+  b->ws = ws;
+  b->slots = slots;
   return DMUON_OK;
 }
 
@@ -790,14 +848,15 @@ std::vector<int> gram_cuts(const dmuon_ns_cfg_t* cfg) {
 }
 
 // Launches every group `gid` of a Gram-space plan.
-dmuon_status_t gram_group(const Plan& plan, int gid, const IterArgs& args, hipStream_t s) {
+dmuon_status_t gram_group(const Plan& plan, int gid, const IterArgs& args, Bases b,
+                          hipStream_t s) {
   const char* tab = static_cast<const char*>(plan.dtab);
   for (const GemmLaunch& gl : plan.gemms) {
     if (gl.group != gid) continue;
-    const GemmTask* tasks = reinterpret_cast<const GemmTask*>(tab + gl.off);
+    const GemmTab* tasks = reinterpret_cast<const GemmTab*>(tab + gl.off);
     const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
     const hipError_t e = timed(gl.kind, gl.flops, bytes, s, [&] {
-      return launch_gemm(gl.kind, gl.tile, 1, gl.bk, tasks, gl.ntasks, gl.total, args, s);
+      return launch_gemm(gl.kind, gl.tile, 1, gl.bk, tasks, gl.ntasks, gl.total, args, b, s);
     });
     if (e != hipSuccess)
       return fail(DMUON_E_HIP, std::string("Gram NS product launch: ") + hipGetErrorString(e));
@@ -807,10 +866,10 @@ dmuon_status_t gram_group(const Plan& plan, int gid, const IterArgs& args, hipSt
 
 // A = X X^T at the start of window w (window 0 scales by 1/(||u||+eps)^2
 // through the norm's scale, which is 1 for a shard until the group sum).
-dmuon_status_t gram_syrk(const Plan& plan, int w, hipStream_t s) {
+dmuon_status_t gram_syrk(const Plan& plan, int w, Bases b, hipStream_t s) {
   IterArgs base{};
   base.iter = w;
-  return gram_group(plan, GG_SYRK, base, s);
+  return gram_group(plan, GG_SYRK, base, b, s);
 }
 
 // The steps of window w on its A: per step P, then Q <- P Q and A <- P (P A)
@@ -818,7 +877,7 @@ dmuon_status_t gram_syrk(const Plan& plan, int w, hipStream_t s) {
 // window writes the caller's matrix (`fin`).
 dmuon_status_t gram_window(const Plan& plan, const dmuon_ns_cfg_t* cfg,
                            const std::vector<int>& cuts, int w, int fin, float lr, float decay,
-                           hipStream_t s) {
+                           Bases b, hipStream_t s) {
   IterArgs base{};
   base.iter = w;  // window 0's X update applies 1/(||u||+eps); X^T ping-pong
   dmuon_status_t st;
@@ -830,59 +889,59 @@ dmuon_status_t gram_window(const Plan& plan, const dmuon_ns_cfg_t* cfg,
     pa.b = c[1];
     pa.c = c[2];
     const bool first = k == cuts[w];
-    if ((st = gram_group(plan, first ? GG_P_QA : GG_P_PM, pa, s))) return st;
+    if ((st = gram_group(plan, first ? GG_P_QA : GG_P_PM, pa, b, s))) return st;
     if (!first) {
-      if ((st = gram_group(plan, q_in_a ? GG_Q_AB : GG_Q_BA, base, s))) return st;
+      if ((st = gram_group(plan, q_in_a ? GG_Q_AB : GG_Q_BA, base, b, s))) return st;
       q_in_a = !q_in_a;
     }
     if (k + 1 < cuts[w + 1]) {
-      if ((st = gram_group(plan, first ? GG_PA_QA : GG_PA_PM, base, s))) return st;
-      if ((st = gram_group(plan, first ? GG_A_QA : GG_A_PM, base, s))) return st;
+      if ((st = gram_group(plan, first ? GG_PA_QA : GG_PA_PM, base, b, s))) return st;
+      if ((st = gram_group(plan, first ? GG_A_QA : GG_A_PM, base, b, s))) return st;
     }
   }
   IterArgs qx = base;  // a = 0: X <- s Q X
   qx.fin = fin;
   qx.lr = lr;
   qx.decay = decay;
-  return gram_group(plan, q_in_a ? GG_QX_QA : GG_QX_QB, qx, s);
+  return gram_group(plan, q_in_a ? GG_QX_QA : GG_QX_QB, qx, b, s);
 }
 
 // Gram-space NS on whole matrices: every window in turn.
 dmuon_status_t run_gram(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, float lr,
-                        float decay, hipStream_t s) {
+                        float decay, Bases b, hipStream_t s) {
   const std::vector<int> cuts = gram_cuts(cfg);
   const int windows = (int)cuts.size() - 1;
   dmuon_status_t st;
   for (int w = 0; w < windows; ++w) {
-    if ((st = gram_syrk(plan, w, s))) return st;
+    if ((st = gram_syrk(plan, w, b, s))) return st;
     const int fin = w == windows - 1 ? (ns_only ? FIN_OUTPUT : FIN_UPDATE) : FIN_NONE;
-    if ((st = gram_window(plan, cfg, cuts, w, fin, lr, decay, s))) return st;
+    if ((st = gram_window(plan, cfg, cuts, w, fin, lr, decay, b, s))) return st;
   }
   return DMUON_OK;
 }
 
 dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, float momentum,
-                   int nesterov, float lr, float decay, hipStream_t s) {
+                   int nesterov, float lr, float decay, Bases b, hipStream_t s) {
   const char* tab = static_cast<const char*>(plan.dtab);
   auto check = [](hipError_t e, const char* what) -> dmuon_status_t {
     if (e == hipSuccess) return DMUON_OK;
     return fail(DMUON_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
   };
-  const EwTask* tin = reinterpret_cast<const EwTask*>(tab + plan.in_off);
-  const NormTask* tnorm = reinterpret_cast<const NormTask*>(tab + plan.norm_off);
+  const EwTab* tin = reinterpret_cast<const EwTab*>(tab + plan.in_off);
+  const NormTab* tnorm = reinterpret_cast<const NormTab*>(tab + plan.norm_off);
   dmuon_status_t st = check(
       timed(ns_only ? KIND_INPUT : KIND_MOMENTUM, 0, plan.in_bytes, s,
             [&] { return launch_momentum(tin, plan.nmat, plan.in_tiles, momentum, nesterov,
-                                         ns_only, s); }),
+                                         ns_only, b, s); }),
       "momentum/input launch");
   if (st) return st;
   st = check(timed(KIND_NORM, 0, plan.norm_bytes, s,
-                   [&] { return launch_norm(tnorm, plan.nmat, cfg->eps, s); }),
+                   [&] { return launch_norm(tnorm, plan.nmat, cfg->eps, b, s); }),
              "norm launch");
   if (st) return st;
   // a shard stops at its first partial Gram matrix: the group sums come next
-  if (plan.local) return gram_syrk(plan, 0, s);
-  if (plan.gram) return run_gram(plan, cfg, ns_only, lr, decay, s);
+  if (plan.local) return gram_syrk(plan, 0, b, s);
+  if (plan.gram) return run_gram(plan, cfg, ns_only, lr, decay, b, s);
   for (int it = 0; it < cfg->ns_steps; ++it) {
     const float* c = cfg->coeffs ? cfg->coeffs + 3 * it : kQuintic;
     IterArgs args{};
@@ -897,12 +956,12 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
       args.decay = decay;
     }
     for (const GemmLaunch& gl : plan.gemms) {
-      const GemmTask* tasks = reinterpret_cast<const GemmTask*>(tab + gl.off);
+      const GemmTab* tasks = reinterpret_cast<const GemmTab*>(tab + gl.off);
       const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
       st = check(timed(gl.kind, gl.flops, bytes, s,
                        [&] {
                          return launch_gemm(gl.kind, gl.tile, plan.f32_ops, gl.bk, tasks, gl.ntasks,
-                                            gl.total, args, s);
+                                            gl.total, args, b, s);
                        }),
                  "NS product launch");
       if (st) return st;
@@ -914,24 +973,24 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
 // Gram NS on a shard, window w, once the bucket holds the group's sums:
 // (window 0) the normalization, the window's steps and X <- Q X, then the
 // next window's partial Gram matrix, or (last window) the output.
-dmuon_status_t run_local_advance(const Plan& plan, const dmuon_ns_cfg_t* cfg, int w,
+dmuon_status_t run_local_advance(const Plan& plan, const dmuon_ns_cfg_t* cfg, int w, Bases b,
                                  hipStream_t s) {
   const std::vector<int> cuts = gram_cuts(cfg);
   const int windows = (int)cuts.size() - 1;
   dmuon_status_t st;
   if (w == 0) {
-    const FinTask* tfin =
-        reinterpret_cast<const FinTask*>(static_cast<const char*>(plan.dtab) + plan.fin_off);
+    const FinTab* tfin =
+        reinterpret_cast<const FinTab*>(static_cast<const char*>(plan.dtab) + plan.fin_off);
     const hipError_t e = timed(KIND_NORM, 0, plan.fin_bytes, s, [&] {
-      return launch_gram_finalize(tfin, plan.nmat, plan.fin_blocks, cfg->eps, s);
+      return launch_gram_finalize(tfin, plan.nmat, plan.fin_blocks, cfg->eps, b, s);
     });
     if (e != hipSuccess)
       return fail(DMUON_E_HIP, std::string("Gram finalize launch: ") + hipGetErrorString(e));
   }
   const bool last = w == windows - 1;
-  if ((st = gram_window(plan, cfg, cuts, w, last ? FIN_OUTPUT : FIN_NONE, 0.f, 1.f, s)))
+  if ((st = gram_window(plan, cfg, cuts, w, last ? FIN_OUTPUT : FIN_NONE, 0.f, 1.f, b, s)))
     return st;
-  return last ? DMUON_OK : gram_syrk(plan, w + 1, s);
+  return last ? DMUON_OK : gram_syrk(plan, w + 1, b, s);
 }
 
 dmuon_status_t check_ws(const Layout& L, void* ws, size_t ws_bytes) {
@@ -1079,6 +1138,25 @@ dmuon_status_t local_setup(const dmuon_batch_t* g, const dmuon_batch_t* out, int
   return check_disjoint(spans, names);
 }
 
+// Validation of a Muon step's arguments (everything but the workspace and
+// the overlap check) and its workspace layout (unset when count == 0).
+dmuon_status_t check_step(const dmuon_batch_t* params, const dmuon_batch_t* grads,
+                          const dmuon_batch_t* bufs, const dmuon_ns_cfg_t* cfg, float momentum,
+                          float lr, float weight_decay, Layout* L) {
+  dmuon_status_t st = check_batch(params, "params", true);
+  if (st) return st;
+  if ((st = check_batch(grads, "grads", true))) return st;
+  if ((st = check_batch(bufs, "bufs", true))) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = same_shapes(params, grads, "params", "grads"))) return st;
+  if ((st = same_shapes(params, bufs, "params", "bufs"))) return st;
+  if (bufs->dtype != DMUON_F32) return fail(DMUON_E_INVALID, "bufs must be F32");
+  if (!std::isfinite(momentum) || !std::isfinite(lr) || !std::isfinite(weight_decay))
+    return fail(DMUON_E_INVALID, "momentum, lr and weight_decay must be finite");
+  if (params->count == 0) return DMUON_OK;
+  return make_layout(grads, cfg->prec, cfg->backend, L);
+}
+
 }  // namespace
 
 static_assert(sizeof(dmuon_clip_stats_t) == sizeof(dmuon::ClipStats), "clip stats layout");
@@ -1136,8 +1214,11 @@ dmuon_status_t dmuon_ns_orthogonalize(const dmuon_batch_t* g, const dmuon_batch_
 
   std::lock_guard<std::mutex> lock(g_plan_mu);
   Plan* plan = nullptr;
-  if ((st = get_plan(L, g, out, nullptr, true, static_cast<char*>(ws), &plan))) return st;
-  return run(*plan, cfg, true, 0.f, 0, 0.f, 1.f, static_cast<hipStream_t>(stream));
+  if ((st = get_plan(L, g, out, nullptr, true, &plan))) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Bases b;
+  if ((st = upload_slots(L, g, out, nullptr, static_cast<char*>(ws), s, &b))) return st;
+  return run(*plan, cfg, true, 0.f, 0, 0.f, 1.f, b, s);
 }
 
 dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t* grads,
@@ -1145,19 +1226,9 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t*
                                float momentum, float lr, float weight_decay, int32_t nesterov,
                                void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  dmuon_status_t st = check_batch(params, "params", true);
-  if (st) return st;
-  if ((st = check_batch(grads, "grads", true))) return st;
-  if ((st = check_batch(bufs, "bufs", true))) return st;
-  if ((st = check_cfg(cfg))) return st;
-  if ((st = same_shapes(params, grads, "params", "grads"))) return st;
-  if ((st = same_shapes(params, bufs, "params", "bufs"))) return st;
-  if (bufs->dtype != DMUON_F32) return fail(DMUON_E_INVALID, "bufs must be F32");
-  if (!std::isfinite(momentum) || !std::isfinite(lr) || !std::isfinite(weight_decay))
-    return fail(DMUON_E_INVALID, "momentum, lr and weight_decay must be finite");
-  if (params->count == 0) return DMUON_OK;
   Layout L;
-  if ((st = make_layout(grads, cfg->prec, cfg->backend, &L))) return st;
+  dmuon_status_t st = check_step(params, grads, bufs, cfg, momentum, lr, weight_decay, &L);
+  if (st || params->count == 0) return st;
   if ((st = check_ws(L, ws, ws_bytes))) return st;
   std::vector<Span> spans;
   add_spans(spans, params, 0);
@@ -1172,9 +1243,11 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t*
   const float decay = (float)(1.0 - (double)lr * (double)weight_decay);
   std::lock_guard<std::mutex> lock(g_plan_mu);
   Plan* plan = nullptr;
-  if ((st = get_plan(L, grads, params, bufs, false, static_cast<char*>(ws), &plan))) return st;
-  return run(*plan, cfg, false, momentum, nesterov ? 1 : 0, lr, decay,
-             static_cast<hipStream_t>(stream));
+  if ((st = get_plan(L, grads, params, bufs, false, &plan))) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Bases b;
+  if ((st = upload_slots(L, grads, params, bufs, static_cast<char*>(ws), s, &b))) return st;
+  return run(*plan, cfg, false, momentum, nesterov ? 1 : 0, lr, decay, b, s);
 }
 
 dmuon_status_t dmuon_gram_local_workspace_size(const dmuon_batch_t* g, int32_t transposed,
@@ -1219,8 +1292,11 @@ dmuon_status_t dmuon_gram_local_begin(const dmuon_batch_t* g, const dmuon_batch_
   if (st || g->count == 0) return st;
   std::lock_guard<std::mutex> lock(g_plan_mu);
   Plan* plan = nullptr;
-  if ((st = get_plan(L, g, out, nullptr, true, static_cast<char*>(ws), &plan))) return st;
-  return run(*plan, cfg, true, 0.f, 0, 0.f, 1.f, static_cast<hipStream_t>(stream));
+  if ((st = get_plan(L, g, out, nullptr, true, &plan))) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Bases b;
+  if ((st = upload_slots(L, g, out, nullptr, static_cast<char*>(ws), s, &b))) return st;
+  return run(*plan, cfg, true, 0.f, 0, 0.f, 1.f, b, s);
 }
 
 dmuon_status_t dmuon_gram_local_advance(const dmuon_batch_t* g, const dmuon_batch_t* out,
@@ -1237,8 +1313,11 @@ dmuon_status_t dmuon_gram_local_advance(const dmuon_batch_t* g, const dmuon_batc
   if (g->count == 0) return DMUON_OK;
   std::lock_guard<std::mutex> lock(g_plan_mu);
   Plan* plan = nullptr;
-  if ((st = get_plan(L, g, out, nullptr, true, static_cast<char*>(ws), &plan))) return st;
-  return run_local_advance(*plan, cfg, window, static_cast<hipStream_t>(stream));
+  if ((st = get_plan(L, g, out, nullptr, true, &plan))) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Bases b;
+  if ((st = upload_slots(L, g, out, nullptr, static_cast<char*>(ws), s, &b))) return st;
+  return run_local_advance(*plan, cfg, window, b, s);
 }
 
 dmuon_status_t dmuon_clip_workspace_size(const dmuon_batch_t* grads, int32_t nbuckets,
@@ -1421,6 +1500,11 @@ const char* dmuon_status_str(dmuon_status_t s) {
 }
 
 const char* dmuon_last_error(void) { return g_last_error.c_str(); }
+
+int64_t dmuon_plan_builds(void) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  return g_plan_builds;
+}
 
 const char* dmuon_backend_info(void) {
   return "direct NS (SYRK + symmetric poly + update-X) . gfx950 MFMA "

@@ -26,6 +26,31 @@ enum Kind : int {
   KIND_COUNT
 };
 
+// Device addresses in launch tables.  A table depends only on the shapes
+// and options of a call, so it is built once per device and shape set and
+// reused by every later call: each address in it is a Ref, either a byte
+// offset into the call's workspace (>= 0), one of the call's pointer slots
+// (the caller's buffers, ref_slot(s)), or none.  Kernels turn Refs into
+// pointers once per block from the call's Bases.
+typedef int64_t Ref;
+constexpr Ref kRefNone = -1;
+__host__ __device__ constexpr Ref ref_slot(int s) { return -2 - (Ref)s; }
+
+// Per-call bases of the Refs: the workspace and its pointer-slot array,
+// which launch_upload fills from the call's buffer pointers before the
+// first kernel of the call.  Slots per matrix: [source, destination,
+// momentum buffer].
+struct Bases {
+  char* ws;
+  void* const* slots;
+};
+constexpr int kSlotsPerMat = 3;
+
+// Maps an address field of a launch table (Ref) or of its resolved form
+// (a pointer of type T).
+template <class T> using Ptr = T*;
+template <class T> using RefOf = Ref;
+
 // Element-wise tile size (original-layout tiles of EW_TILE x EW_TILE).
 constexpr int EW_TILE = 64;
 constexpr int EW_THREADS = 256;
@@ -33,7 +58,8 @@ constexpr int EW_THREADS = 256;
 // One matrix of an element-wise launch.  Tiles cover `rows` x `cols` in
 // the caller's layout; for the input passes these are the padded extents of
 // the oriented workspace mapped back to the caller's layout.
-struct EwTask {
+template <template <class> class A>
+struct EwTaskT {
   int32_t m, n;            // caller's shape
   int32_t rows, cols;      // extent covered by this launch's tiles
   int32_t tiles_c;         // tiles along cols
@@ -45,53 +71,58 @@ struct EwTask {
   int32_t ldxb;            // row stride of xb (elements)
   int32_t ldt;             // row stride of xt (elements)
   int32_t f32_ops;         // 1: xt holds fp32 (NS in fp32), 0: bf16
-  int32_t vec;             // 1: caller buffers allow 16-byte (4-element) access
-  const void* src;         // grad (step) or G (NS only)
-  float* buf;              // momentum buffer (step) or null
-  float* xm;               // fp32 X, P x Q (f32_ops only)
-  uint16_t* xb;            // bf16 X = high part of X, P x Q (bf16 modes)
-  uint16_t* xlo;           // bf16 X - xb, P x Q, stride ldxb (bf16 modes)
-  void* xt;                // X^T, Q x P (bf16 or fp32)
-  float* partial;          // per-tile sums of squares (indexed by global tile)
-  float* scale;            // per-matrix scalars: [0]=1/(s+eps) [1]=its square
+  int32_t pad0_;
+  A<const void> src;       // grad (step) or G (NS only)
+  A<float> buf;            // momentum buffer (step) or none
+  A<float> xm;             // fp32 X, P x Q (f32_ops only)
+  A<uint16_t> xb;          // bf16 X = high part of X, P x Q (bf16 modes)
+  A<uint16_t> xlo;         // bf16 X - xb, P x Q, stride ldxb (bf16 modes)
+  A<void> xt;              // X^T, Q x P (bf16 or fp32)
+  A<float> partial;        // per-tile sums of squares (indexed by global tile)
+  A<float> scale;          // per-matrix scalars: [0]=1/(s+eps) [1]=its square
 };
+using EwTask = EwTaskT<Ptr>;
+using EwTab = EwTaskT<RefOf>;
 
 // One matrix of a grouped NT-GEMM launch: C = L * R^T over K, tile T x T.
 // L is (tiles_m*T) x K row-major with stride ldl; R is (tiles_n*T) x K with
 // stride ldr and column index taken modulo kper (for hi/lo split operands
 // that reuse one R for two K segments).
-struct GemmTask {
-  const void* L;
-  const void* R0;          // R on even NS iterations
-  const void* R1;          // R on odd NS iterations
+template <template <class> class A>
+struct GemmTaskT {
+  A<const void> L;
+  A<const void> R0;        // R on even NS iterations
+  A<const void> R1;        // R on odd NS iterations
   int32_t ldl, ldr, K, kper;
   int32_t tiles_m, tiles_n, tile_begin, tile_count;
   int32_t tri;             // 1: upper-triangle tiles only (+ mirrored write)
   int32_t split;           // SYRK: write A as [hi|lo|hi|hi]; POLY: write B as [hi|lo]
   int32_t P;               // padded p (segment offset of split layouts)
   int32_t ld_f;            // stride of fbuf
-  float* fbuf;             // fp32 A (SYRK out, POLY in; null when A is split)
+  A<float> fbuf;           // fp32 A (SYRK out, POLY in; none when A is split)
                            // or fp32 X (UPDX, fp32 operands)
-  void* out0;              // SYRK: A operand  POLY: B operand  UPDX: bf16 X
-  void* out1;              // UPDX: X^T (even iter)
-  void* out2;              // UPDX: X^T (odd iter)
+  A<void> out0;            // SYRK: A operand  POLY: B operand  UPDX: bf16 X
+  A<void> out1;            // UPDX: X^T (even iter)
+  A<void> out2;            // UPDX: X^T (odd iter)
   int32_t ld0, ld1;
-  const float* scale;      // per-matrix scalars (see EwTask::scale)
-  uint16_t* xlo;           // UPDX, bf16 operands: X - bf16 X (stride ld0)
-  const uint16_t* ahl;     // POLY with split A: A as [hi | lo | ...] rows
+  A<const float> scale;    // per-matrix scalars (see EwTask::scale)
+  A<uint16_t> xlo;         // UPDX, bf16 operands: X - bf16 X (stride ld0)
+  A<const uint16_t> ahl;   // POLY with split A: A as [hi | lo | ...] rows
   int32_t ld_ahl;          // its row stride
   int32_t pad0_;
-  void* sink;              // 16 writable, never-read bytes (see updx_final)
+  A<void> sink;            // 16 writable, never-read bytes (see updx_final)
   // UPDX, last iteration: the caller's param (step) or output (NS only).
   // Oriented element (r, c), r < pv, c < qv, sits at dst[r*qv + c], or at
   // dst[c*pv + r] when dst_trans (caller's matrix is the transpose).
-  void* dst;
+  A<void> dst;
   int32_t pv, qv;          // valid oriented extents p x q
   int32_t dst_trans;
   int32_t dst_dtype;
   int32_t add_diag;        // POLY (Gram-space P): add the iteration's a on the diagonal
   int32_t pad1_;
 };
+using GemmTask = GemmTaskT<Ptr>;
+using GemmTab = GemmTaskT<RefOf>;
 
 // What the UPDX epilogue does with the new X.
 enum Fin : int32_t {
@@ -108,27 +139,33 @@ struct IterArgs {
   float lr, decay;         // FIN_UPDATE only
 };
 
-struct NormTask {
+template <template <class> class A>
+struct NormTaskT {
   int32_t tile_begin, tile_count;
-  const float* partial;
-  float* scale;
+  A<const float> partial;
+  A<float> scale;
   // Gram NS on a shard: the shard's sum of squares goes here (to be summed
   // over the shard group) and the scales stay 1 until the group's norm is
   // known.
-  float* sumsq;
+  A<float> sumsq;
 };
+using NormTask = NormTaskT<Ptr>;
+using NormTab = NormTaskT<RefOf>;
 
 // Gram NS on a shard, once the group's sums are in: the normalization from
 // the summed squared norm, and the summed raw Gram matrix A (P x P rows of
 // stride ld) scaled by its square.  FIN_ROWS rows of A per block.
 constexpr int FIN_ROWS = 16;
-struct FinTask {
+template <template <class> class A>
+struct FinTaskT {
   int32_t tile_begin, tile_count;  // blocks
   int32_t P, ld;
-  float* a;
-  const float* sumsq;
-  float* scale;
+  A<float> a;
+  A<const float> sumsq;
+  A<float> scale;
 };
+using FinTask = FinTaskT<Ptr>;
+using FinTab = FinTaskT<RefOf>;
 
 // ---------------------------------------------------------------------------
 // Flat element-wise launches (gradient clipping, AdamW): every tensor is
@@ -192,19 +229,26 @@ hipError_t launch_adamw(const FlatTask* tasks, int ntasks, int total_blocks,
                         const AdamArgs& args, hipStream_t s);
 
 // Launch helpers implemented in dmuon_kernels.hip.
-hipError_t launch_momentum(const EwTask* tasks, int ntasks, int total_tiles,
-                           float momentum, int nesterov, int ns_only,
+// Copies `bytes` (a multiple of 8; dst 8-byte aligned) from host memory to
+// the device through kernel arguments, kUploadWords words per launch: a
+// stream-ordered upload that needs no host staging memory and allocates
+// nothing (the call's pointer slots; the launch tables of the
+// allocation-free entry point).
+constexpr int kUploadWords = 256;
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t launch_momentum(const EwTab* tasks, int ntasks, int total_tiles,
+                           float momentum, int nesterov, int ns_only, Bases b,
                            hipStream_t s);
-hipError_t launch_gram_finalize(const FinTask* tasks, int ntasks, int nblocks, float eps,
-                                hipStream_t s);
-hipError_t launch_norm(const NormTask* tasks, int ntasks, float eps,
+hipError_t launch_gram_finalize(const FinTab* tasks, int ntasks, int nblocks, float eps,
+                                Bases b, hipStream_t s);
+hipError_t launch_norm(const NormTab* tasks, int ntasks, float eps, Bases b,
                        hipStream_t s);
 // kind in {KIND_SYRK, KIND_POLY, KIND_UPDX}; tile in {64, 128, 256}
 // (bf16 operands) or {64, 128} (fp32 operands); bk, the K depth of a bf16
 // main-loop stage: 64, or 128 for the 64-wide SYRK and polynomial (every
 // task's K then a multiple of 128)
 hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk,
-                       const GemmTask* tasks, int ntasks, int total_tiles,
-                       const IterArgs& args, hipStream_t s);
+                       const GemmTab* tasks, int ntasks, int total_tiles,
+                       const IterArgs& args, Bases b, hipStream_t s);
 
 }  // namespace dmuon

@@ -11,6 +11,7 @@
 //   bop   B = bA + cA^2 as MFMA operand (fp32 / bf16 / [hi|lo] rows)
 // With every operand stored K-contiguous, all three products of one NS
 // iteration are "NT" products C = L R^T and share one MFMA main loop.
+#include <cstring>
 #include <type_traits>
 
 #include "dmuon_device.h"
@@ -18,6 +19,77 @@
 
 namespace dmuon {
 namespace {
+
+// --------------------------------------------------------------------------
+// Launch tables hold Refs (see Bases): resolved once per block.
+template <class T>
+__device__ __forceinline__ T* at(Ref r, const Bases& b) {
+  if (r >= 0) return reinterpret_cast<T*>(b.ws + r);
+  if (r == kRefNone) return nullptr;
+  typedef void* const GMEM* SlotPtr;
+  return static_cast<T*>(((SlotPtr)b.slots)[-2 - r]);
+}
+
+__device__ __forceinline__ EwTask resolve(const EwTab& t, const Bases& b) {
+  EwTask r = __builtin_bit_cast(EwTask, t);
+  r.src = at<const void>(t.src, b);
+  r.buf = at<float>(t.buf, b);
+  r.xm = at<float>(t.xm, b);
+  r.xb = at<uint16_t>(t.xb, b);
+  r.xlo = at<uint16_t>(t.xlo, b);
+  r.xt = at<void>(t.xt, b);
+  r.partial = at<float>(t.partial, b);
+  r.scale = at<float>(t.scale, b);
+  return r;
+}
+
+__device__ __forceinline__ GemmTask resolve(const GemmTab& t, const Bases& b) {
+  GemmTask r = __builtin_bit_cast(GemmTask, t);
+  r.L = at<const void>(t.L, b);
+  r.R0 = at<const void>(t.R0, b);
+  r.R1 = at<const void>(t.R1, b);
+  r.fbuf = at<float>(t.fbuf, b);
+  r.out0 = at<void>(t.out0, b);
+  r.out1 = at<void>(t.out1, b);
+  r.out2 = at<void>(t.out2, b);
+  r.scale = at<const float>(t.scale, b);
+  r.xlo = at<uint16_t>(t.xlo, b);
+  r.ahl = at<const uint16_t>(t.ahl, b);
+  r.sink = at<void>(t.sink, b);
+  r.dst = at<void>(t.dst, b);
+  return r;
+}
+
+__device__ __forceinline__ NormTask resolve(const NormTab& t, const Bases& b) {
+  NormTask r = __builtin_bit_cast(NormTask, t);
+  r.partial = at<const float>(t.partial, b);
+  r.scale = at<float>(t.scale, b);
+  r.sumsq = at<float>(t.sumsq, b);
+  return r;
+}
+
+__device__ __forceinline__ FinTask resolve(const FinTab& t, const Bases& b) {
+  FinTask r = __builtin_bit_cast(FinTask, t);
+  r.a = at<float>(t.a, b);
+  r.sumsq = at<const float>(t.sumsq, b);
+  r.scale = at<float>(t.scale, b);
+  return r;
+}
+
+// Host-to-device upload through kernel arguments: n <= kUploadWords
+// 8-byte words of one chunk go to dst.  Stream-ordered like any launch,
+// with no host staging buffer and no device allocation.
+struct UploadChunk {
+  uint64_t* dst;
+  int32_t n;
+  int32_t pad_;
+  uint64_t w[kUploadWords];
+};
+
+__global__ __launch_bounds__(kUploadWords) void upload_kernel(UploadChunk c) {
+  const int i = threadIdx.x;
+  if (i < c.n) *(uint64_t GMEM*)(c.dst + i) = c.w[i];
+}
 
 // The master copy of X, four consecutive elements at offset o (of the
 // fp32 row stride ldx or the bf16 row stride ldxb): fp32 only (fp32
@@ -47,15 +119,20 @@ __device__ __forceinline__ void store_master4(const EwTask& T, size_t row, int c
 // transposed one through LDS), pads are written as zeros, and the tile's
 // sum of u^2 goes to partial[tile].
 __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
-    const EwTask* __restrict__ tasks, int ntasks, int total_tiles, float mu,
-    int nesterov, int ns_only) {
+    const EwTab* __restrict__ tasks, int ntasks, int total_tiles, float mu,
+    int nesterov, int ns_only, Bases bases) {
   __shared__ float tile[EW_TILE][EW_TILE + 1];
   __shared__ float wsum[EW_THREADS / 64];
   const int gt = blockIdx.x;
   if (gt >= total_tiles) return;
   // A copy, not a reference: stores through the task's pointers could
   // otherwise alias it and force a reload of every field after each store.
-  const EwTask T = tasks[find_task(tasks, ntasks, gt)];
+  const EwTask T = resolve(tasks[find_task(tasks, ntasks, gt)], bases);
+  // 16-byte (fp32) / 8-byte (bf16) accesses of 4 elements when the caller's
+  // buffers allow them
+  const bool vec = T.n % 4 == 0 &&
+                   reinterpret_cast<uintptr_t>(T.src) % (T.in_dtype == 0 ? 16 : 8) == 0 &&
+                   reinterpret_cast<uintptr_t>(T.buf) % 16 == 0;
   const int lt = gt - T.tile_begin;
   const int r0 = (lt / T.tiles_c) * EW_TILE;
   const int c0 = (lt % T.tiles_c) * EW_TILE;
@@ -69,7 +146,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
   // before the first store: the stores to buf could alias later loads for
   // all the compiler knows, which would serialize the rows' round trips.
   constexpr int RK = EW_TILE / 16;  // rows per thread
-  const bool interior = T.vec && r0 + EW_TILE <= T.m && c0 + EW_TILE <= T.n;
+  const bool interior = vec && r0 + EW_TILE <= T.m && c0 + EW_TILE <= T.n;
   f32x4 gpre[RK], bpre[RK];
   if (interior) {
 #pragma unroll
@@ -88,7 +165,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
     f32x4 u = {0.f, 0.f, 0.f, 0.f};
     if (gr < T.m && gc < T.n) {
       const size_t idx = (size_t)gr * T.n + gc;
-      if (T.vec && gc + 3 < T.n) {
+      if (vec && gc + 3 < T.n) {
         const f32x4 g = interior ? gpre[k] : load4(T.src, T.in_dtype, idx);
         if (ns_only) {
           u = g;
@@ -169,10 +246,10 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(
 // --------------------------------------------------------------------------
 // Norm finalize: one block per matrix sums its tiles' partials in fp64 in a
 // fixed order and stores 1/(||u||_F + eps) and its square.
-__global__ __launch_bounds__(256) void norm_kernel(const NormTask* __restrict__ tasks,
-                                                   float eps) {
+__global__ __launch_bounds__(256) void norm_kernel(const NormTab* __restrict__ tasks,
+                                                   float eps, Bases bases) {
   __shared__ double wpart[4];
-  const NormTask T = tasks[blockIdx.x];
+  const NormTask T = resolve(tasks[blockIdx.x], bases);
   double acc = 0.0;
   for (int i = threadIdx.x; i < T.tile_count; i += 256)
     acc += (double)ld_f32(T.partial + T.tile_begin + i);
@@ -200,10 +277,10 @@ __global__ __launch_bounds__(256) void norm_kernel(const NormTask* __restrict__ 
 // Gram NS on a shard, after the group sum: inv = 1/(sqrt(sumsq) + eps) as in
 // norm_kernel, A *= inv^2 (the same fp32 factor the SYRK epilogue applies
 // when the norm is known up front), and the scales for the X update.
-__global__ __launch_bounds__(256) void gram_finalize_kernel(const FinTask* __restrict__ tasks,
-                                                            int ntasks, float eps) {
+__global__ __launch_bounds__(256) void gram_finalize_kernel(const FinTab* __restrict__ tasks,
+                                                            int ntasks, float eps, Bases bases) {
   const int b = blockIdx.x;
-  const FinTask T = tasks[find_task(tasks, ntasks, b)];
+  const FinTask T = resolve(tasks[find_task(tasks, ntasks, b)], bases);
   const double tot = (double)ld_f32(T.sumsq);
   const double s = sqrt(tot);
   const double inv = 1.0 / (s + (double)eps);
@@ -856,8 +933,9 @@ __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT
 }
 
 template <int KIND, int T, bool F32>
-__global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restrict__ tasks,
-                                                   int ntasks, int total_tiles, IterArgs A) {
+__global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTab* __restrict__ tasks,
+                                                   int ntasks, int total_tiles, IterArgs A,
+                                                   Bases bases) {
   using E = typename std::conditional<F32, float, uint16_t>::type;
   constexpr int ESZ = sizeof(E);
   constexpr int BK = 128 / ESZ;           // K elements per stage
@@ -872,7 +950,7 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTask* __restric
   if (vb >= total_tiles) return;
   // By value (see momentum_kernel): the epilogue's stores must not force
   // reloads of the descriptor.
-  const GemmTask G = tasks[find_task(tasks, ntasks, vb)];
+  const GemmTask G = resolve(tasks[find_task(tasks, ntasks, vb)], bases);
   const int lt = vb - G.tile_begin;
   int tm, tn;
   if (G.tri)
@@ -1048,8 +1126,9 @@ template <int T, int BK>
 constexpr int kStages = (T == 64 && BK == 64) ? 3 : 2;
 
 template <int KIND, int T, int BK>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restrict__ tasks,
-                                                        int ntasks, int total_tiles, IterArgs A) {
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTab* __restrict__ tasks,
+                                                        int ntasks, int total_tiles, IterArgs A,
+                                                        Bases bases) {
   constexpr int STAGES = kStages<T, BK>;
   constexpr int CPR = BK / 8;             // 16-byte chunks per row
   constexpr int WT = T / 2;               // wave tile (2 x 2 waves)
@@ -1063,7 +1142,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
   if (vb >= total_tiles) return;
   // By value (see momentum_kernel): the epilogue's stores must not force
   // reloads of the descriptor.
-  const GemmTask G = tasks[find_task(tasks, ntasks, vb)];
+  const GemmTask G = resolve(tasks[find_task(tasks, ntasks, vb)], bases);
   const int lt = vb - G.tile_begin;
   int tm, tn;
   if (G.tri)
@@ -1217,75 +1296,92 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTask* __restri
 }
 
 template <int KIND, int T>
-hipError_t launch_gemm_f32(const GemmTask* tasks, int ntasks, int total_tiles, const IterArgs& A,
-                           hipStream_t s) {
+hipError_t launch_gemm_f32(const GemmTab* tasks, int ntasks, int total_tiles, const IterArgs& A,
+                           Bases b, hipStream_t s) {
   const int grid = (total_tiles + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_reg_kernel<KIND, T, true>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
-                     total_tiles, A);
+                     total_tiles, A, b);
   return hipGetLastError();
 }
 
 template <int KIND, int T, int BK>
-hipError_t launch_gemm_bf16(const GemmTask* tasks, int ntasks, int total_tiles, const IterArgs& A,
-                            hipStream_t s) {
+hipError_t launch_gemm_bf16(const GemmTab* tasks, int ntasks, int total_tiles, const IterArgs& A,
+                            Bases b, hipStream_t s) {
   const int grid = (total_tiles + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_bf16_kernel<KIND, T, BK>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
-                     total_tiles, A);
+                     total_tiles, A, b);
   return hipGetLastError();
 }
 
 template <int KIND>
-hipError_t launch_gemm_k(int tile, int f32_ops, int bk, const GemmTask* tasks, int ntasks,
-                         int total_tiles, const IterArgs& A, hipStream_t s) {
+hipError_t launch_gemm_k(int tile, int f32_ops, int bk, const GemmTab* tasks, int ntasks,
+                         int total_tiles, const IterArgs& A, Bases b, hipStream_t s) {
   if (f32_ops) {
-    if (tile == 64) return launch_gemm_f32<KIND, 64>(tasks, ntasks, total_tiles, A, s);
-    if (tile == 128) return launch_gemm_f32<KIND, 128>(tasks, ntasks, total_tiles, A, s);
+    if (tile == 64) return launch_gemm_f32<KIND, 64>(tasks, ntasks, total_tiles, A, b, s);
+    if (tile == 128) return launch_gemm_f32<KIND, 128>(tasks, ntasks, total_tiles, A, b, s);
     return hipErrorInvalidValue;
   }
   if constexpr (KIND != KIND_UPDX) {
     if (tile == 64 && bk == 128)
-      return launch_gemm_bf16<KIND, 64, 128>(tasks, ntasks, total_tiles, A, s);
+      return launch_gemm_bf16<KIND, 64, 128>(tasks, ntasks, total_tiles, A, b, s);
   }
   if (bk != 64) return hipErrorInvalidValue;
-  if (tile == 64) return launch_gemm_bf16<KIND, 64, 64>(tasks, ntasks, total_tiles, A, s);
-  if (tile == 128) return launch_gemm_bf16<KIND, 128, 64>(tasks, ntasks, total_tiles, A, s);
-  if (tile == 256) return launch_gemm_bf16<KIND, 256, 64>(tasks, ntasks, total_tiles, A, s);
+  if (tile == 64) return launch_gemm_bf16<KIND, 64, 64>(tasks, ntasks, total_tiles, A, b, s);
+  if (tile == 128) return launch_gemm_bf16<KIND, 128, 64>(tasks, ntasks, total_tiles, A, b, s);
+  if (tile == 256) return launch_gemm_bf16<KIND, 256, 64>(tasks, ntasks, total_tiles, A, b, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_momentum(const EwTask* tasks, int ntasks, int total_tiles, float momentum,
-                           int nesterov, int ns_only, hipStream_t s) {
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (bytes % 8 || reinterpret_cast<uintptr_t>(dst) % 8) return hipErrorInvalidValue;
+  const size_t words = bytes / 8;
+  for (size_t off = 0; off < words; off += kUploadWords) {
+    UploadChunk c{};
+    c.dst = static_cast<uint64_t*>(dst) + off;
+    c.n = (int32_t)(words - off < (size_t)kUploadWords ? words - off : (size_t)kUploadWords);
+    std::memcpy(c.w, static_cast<const char*>(src) + 8 * off, 8 * (size_t)c.n);
+    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(kUploadWords), 0, s, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_momentum(const EwTab* tasks, int ntasks, int total_tiles, float momentum,
+                           int nesterov, int ns_only, Bases b, hipStream_t s) {
   hipLaunchKernelGGL(momentum_kernel, dim3(total_tiles), dim3(EW_THREADS), 0, s, tasks, ntasks,
-                     total_tiles, momentum, nesterov, ns_only);
+                     total_tiles, momentum, nesterov, ns_only, b);
   return hipGetLastError();
 }
 
-hipError_t launch_gram_finalize(const FinTask* tasks, int ntasks, int nblocks, float eps,
-                                hipStream_t s) {
-  hipLaunchKernelGGL(gram_finalize_kernel, dim3(nblocks), dim3(256), 0, s, tasks, ntasks, eps);
+hipError_t launch_gram_finalize(const FinTab* tasks, int ntasks, int nblocks, float eps,
+                                Bases b, hipStream_t s) {
+  hipLaunchKernelGGL(gram_finalize_kernel, dim3(nblocks), dim3(256), 0, s, tasks, ntasks, eps, b);
   return hipGetLastError();
 }
 
-hipError_t launch_norm(const NormTask* tasks, int ntasks, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(norm_kernel, dim3(ntasks), dim3(256), 0, s, tasks, eps);
+hipError_t launch_norm(const NormTab* tasks, int ntasks, float eps, Bases b, hipStream_t s) {
+  hipLaunchKernelGGL(norm_kernel, dim3(ntasks), dim3(256), 0, s, tasks, eps, b);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk, const GemmTask* tasks, int ntasks,
-                       int total_tiles, const IterArgs& A, hipStream_t s) {
+hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk, const GemmTab* tasks, int ntasks,
+                       int total_tiles, const IterArgs& A, Bases b, hipStream_t s) {
   switch (kind) {
     case KIND_SYRK:
-      return launch_gemm_k<KIND_SYRK>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, s);
+      return launch_gemm_k<KIND_SYRK>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, b, s);
     case KIND_POLY:
-      return launch_gemm_k<KIND_POLY>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, s);
+      return launch_gemm_k<KIND_POLY>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, b, s);
     case KIND_UPDX:
-      return launch_gemm_k<KIND_UPDX>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, s);
+      return launch_gemm_k<KIND_UPDX>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, b, s);
     case KIND_GRAMMUL:  // fp32 operands only
       if (!f32_ops) return hipErrorInvalidValue;
-      if (tile == 64) return launch_gemm_f32<KIND_GRAMMUL, 64>(tasks, ntasks, total_tiles, A, s);
-      if (tile == 128) return launch_gemm_f32<KIND_GRAMMUL, 128>(tasks, ntasks, total_tiles, A, s);
+      if (tile == 64)
+        return launch_gemm_f32<KIND_GRAMMUL, 64>(tasks, ntasks, total_tiles, A, b, s);
+      if (tile == 128)
+        return launch_gemm_f32<KIND_GRAMMUL, 128>(tasks, ntasks, total_tiles, A, b, s);
       return hipErrorInvalidValue;
     default:
       return hipErrorInvalidValue;

@@ -73,7 +73,8 @@ def _tile(p, prec):
 
 
 def _expected_ws(shapes, prec):
-    """Workspace rule: partials, scales and a 16-byte sink, then per matrix
+    """Workspace rule: partials, scales, a 16-byte sink and the call's
+    pointer slots (three per matrix), then per matrix
     the master X (fp32 X, plus bf16 X for bf16 operands; or, below 256-tiles,
     bf16 X plus its bf16 remainder), two X^T
     buffers, fp32 A (unless A is split), the operand forms of A ([hi|lo|hi|hi]
@@ -101,11 +102,12 @@ def _expected_ws(shapes, prec):
             base += a(2 * P * _ld(4 * P if split_a else P, 2))
             base += a(2 * P * _ld(2 * P if split_b else P, 2))
             per.append(base)
-    return a(4 * tiles) + a(16 * len(shapes)) + a(16) + sum(per)
+    return a(4 * tiles) + a(16 * len(shapes)) + a(16) + a(24 * len(shapes)) + sum(per)
 
 
 def test_workspace_size_gram():
-    """Gram-space layout (fp32 operands): partials, scales, sink, then per
+    """Gram-space layout (fp32 operands): partials, scales, sink, pointer
+    slots, then per
     matrix fp32 X, two fp32 X^T, and five fp32 P x P buffers (A, P, P A and
     the Q pair)."""
     a = lambda x: _pad(x, 256)  # noqa: E731
@@ -117,7 +119,7 @@ def test_workspace_size_gram():
         P, Q = _pad(p, t), _pad(q, t)
         tiles += (P // 64) * (Q // 64)
         per += a(4 * P * _ld(Q, 4)) + 2 * a(4 * Q * _ld(P, 4)) + 5 * a(4 * P * _ld(P, 4))
-    want = a(4 * tiles) + a(16 * len(shapes)) + a(16) + per
+    want = a(4 * tiles) + a(16 * len(shapes)) + a(16) + a(24 * len(shapes)) + per
     for prec in ("f32", "auto"):
         assert dm.workspace_size(shapes, prec, backend="gram") == want
 
@@ -430,7 +432,7 @@ def _expected_local(shapes, transposed):
         tiles += (P // 64) * (Q // 64)
         bucket += a(4 * P * _ld(P, 4))
         per += a(4 * P * _ld(Q, 4)) + 2 * a(4 * Q * _ld(P, 4)) + 4 * a(4 * P * _ld(P, 4))
-    head = a(4 * tiles) + a(16 * len(shapes)) + a(16)
+    head = a(4 * tiles) + a(16 * len(shapes)) + a(16) + a(24 * len(shapes))
     return head + bucket + per, head, bucket
 
 
