@@ -14,7 +14,8 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import bf16_param_excess, exact64, rel_frobenius, sigma_dev, to_dev
+from tests.gpu_util import (bf16_frac_cap, bf16_param_check, bf16_param_excess, exact64,
+                            rel_frobenius, sigma_dev, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,13 +79,17 @@ def _run(cfg, steps, check_ns_steps, shapes=None, cfg_id=None, nesterov=None):
                 # value) may separate p_after from p_before - lr*O_oracle;
                 # whatever exceeds it is NS error and must stay within the
                 # NS tolerance, relative to lr*O.
-                e, frac = bf16_param_excess(p_before[i], p_after, O, cfg.lr)
+                e, _ = bf16_param_excess(p_before[i], p_after, O, cfg.lr)
                 assert e <= ns_tol, ("param excess", step, i, shapes[i], e)
-                # Sanity bound on rounding: the share of elements whose bf16
-                # value differs from RNE(oracle) follows the NS error (a few
-                # percent here); truncating instead of rounding would move
-                # about half of them.
-                assert frac <= 0.25, ("param frac", step, i, frac)
+                # Against the exact update rounded once: every element within
+                # one bf16 spacing, and at most 5% of them different at all --
+                # or, where lr*O spans several spacings (these reduced sizes),
+                # the share an NS error at the tolerance would move.
+                # Truncating instead of rounding would move about half.
+                dist, frac = bf16_param_check(p_before[i], p_after, O, cfg.lr)
+                cap = bf16_frac_cap(p_before[i], O, cfg.lr, ns_tol)
+                assert dist <= 1.0 + 1e-9, ("param distance", step, i, dist)
+                assert frac <= cap, ("param frac", step, i, frac, cap)
                 report.append(frac)
     return report
 
