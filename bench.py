@@ -5,17 +5,21 @@ One step = one pass of the whole hot path over one batch of synthetic
 gradients already resident in HBM: momentum (+ Nesterov), Newton-Schulz of
 every matrix (5 iterations of A = X X^T, B = bA + cA^2, X = aX + BX) and the
 lr-scaled update, all in libdmuon's HIP kernels.  The default workload is
-the 4-layer TinyMLP of DMuon's Quick Start (d=512, ff=2048: 12 matrices);
-``--config 3`` / ``--config 5`` run the Llama-8B projection and 70B-MLP
-batches, ``--config 4`` the 512-matrix NS-only batch.  ``--ns-backend gram``
+the largest single-GPU batch, the 70B-class MLP matrices (4 of 28672 x 8192,
+2 of 8192 x 28672, bf16, Nesterov); ``--config 2`` runs the 4-layer TinyMLP
+of DMuon's Quick Start (d=512, ff=2048), ``--config 3`` the Llama-8B
+projections, ``--config 4`` the 512-matrix NS-only batch and ``--config 1``
+the fp32 TinyMLP.  ``--ns-backend gram``
 runs the Gram-space iteration with restarts instead (fp32 operands); the
 value stays the direct method's algorithmic flops per second, so the two
 backends compare on the same work.
 
 Prints ONE JSON line: NS TFLOP/s (algorithmic, symmetry-aware flops) as the
-value, ms per step, the dominant kernel's roofline (timed with HIP events
-on its stream inside the timed region) and the fp64 oracle's throughput on
-a bounded sample of the same workload on the host cores.
+value and ms per step, both from a timed region with nothing but the steps
+in it; the dominant kernel's roofline from a second timed region of the
+same K steps in which HIP events on the kernel's stream bracket each of its
+launches; and the fp64 oracle's throughput on a bounded sample of the same
+workload on the host cores, per phase.
 """
 import argparse
 import hashlib
@@ -72,7 +76,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--op", default="muon", choices=["muon", "clip", "adamw", "gram_local"],
                     help="muon: the Muon step (default); clip / adamw: the element-wise "
                          "companions (gradient clipping, AdamW) on their own workloads; "
@@ -83,31 +87,37 @@ def parse():
     ap.add_argument("--restarts", default=None, metavar="K,K,...",
                     help="Gram backend: iterations that start a new window (default: 2; "
                          "'' for none)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the oracle's host timing (0 disables it)")
+    ap.add_argument("--grads", default="workload", choices=["workload", "gauss"],
+                    help="workload: the configuration's gradient recipe (default); gauss: "
+                         "iid N(0,1) gradients of the same shapes and dtype, which calls no "
+                         "solver (QR) while building inputs -- for profiled runs, where "
+                         "kernel work does not depend on the values")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of this many MiB first (a "
                          "known-size reference for rocprofv3 byte counters)")
     return ap.parse_args()
 
 
-def make_inputs(cfg, n_sets, device):
+def make_inputs(cfg, n_sets, device, grad_kind=None):
     import torch
     import workloads
     from workloads.synth import powerlaw_basis_torch
     dt = {"f32": torch.float32, "bf16": torch.bfloat16}
     shapes = cfg.shapes
+    grad_kind = grad_kind or cfg.grad_kind
     params = [workloads.param_torch(m, n, cfg.cfg_id, i, device, dt[cfg.param_dtype])
               for i, (m, n) in enumerate(shapes)]
     bufs = [torch.zeros(m, n, dtype=torch.float32, device=device) for m, n in shapes]
     bases = [None] * len(shapes)
-    if cfg.grad_kind == "powerlaw_t3":
+    if grad_kind == "powerlaw_t3":
         for i, (m, n) in enumerate(shapes):
             bases[i] = powerlaw_basis_torch(m, n, cfg.cfg_id, i, device)
             log(f"basis {i + 1}/{len(shapes)} ready")
     sets = []
     for s in range(n_sets):
-        sets.append([workloads.grad_torch(cfg.grad_kind, m, n, cfg.cfg_id, s, i, device,
+        sets.append([workloads.grad_torch(grad_kind, m, n, cfg.cfg_id, s, i, device,
                                           dt[cfg.grad_dtype], basis=bases[i])
                      for i, (m, n) in enumerate(shapes)])
         log(f"gradient set {s + 1}/{n_sets} ready")
@@ -139,62 +149,114 @@ def traffic_for(kind, workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, budget_s, backend="direct", restarts=None):
-    """The fp64 oracle as it stands, on the host, over the same recipe:
-    whole matrices of the workload in order until the budget is used.  With
-    the Gram backend the oracle's Gram iteration replaces its direct one."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()
+                    if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, budget_s, backend="direct", restarts=None, grad_sets=None):
+    """The fp64 oracle as it stands, on the host, over the same inputs, timed
+    per phase: momentum (oracle.momentum_update), Newton-Schulz
+    (oracle.direct_newton_schulz, or oracle.gram_newton_schulz for the Gram
+    backend) and the update (oracle.update_param).  Matrices are taken in
+    the workload's order, step after step (the gradient sets the GPU ran,
+    copied to the host, or else the seeded numpy recipe; the momentum
+    carried over), until the budget is spent.  A matrix whose whole NS would
+    not fit in the remaining budget (the 70B MLP's) runs one of its NS
+    iterations instead, which is one fifth of the NS flops with the same
+    products; the sample says which."""
     import numpy as np
     import oracle
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()
-                       if d.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = None
-    flops = 0.0
-    done = 0
-    t_total = 0.0
+    quintic = [tuple(oracle.QUINTIC)]
+    t_phase = {"momentum": 0.0, "ns": 0.0, "update": 0.0}
+    elems = {"momentum": 0, "update": 0}
+    ns_flops_done = 0.0
+    rate = 0.4e12  # assumed until measured: algorithmic NS flop/s of the oracle
     bufs, params = {}, {}
-    step = 0
-    # Whole steps of the workload (fresh seeded gradients each step, the
-    # momentum carried over) until the budget is spent.
+    parts = []
+    step, t_total = 0, 0.0
     while t_total < budget_s:
         for i, (m, n) in enumerate(cfg.shapes):
-            g = workloads.grad_np(cfg.grad_kind, m, n, cfg.cfg_id, step, i)
+            if grad_sets is not None:
+                g = grad_sets[step % len(grad_sets)][i].double().cpu().numpy()
+            else:
+                g = workloads.grad_np(cfg.grad_kind, m, n, cfg.cfg_id, step, i)
             if i not in params:
                 params[i] = workloads.param_np(m, n, cfg.cfg_id, i)
                 bufs[i] = np.zeros((m, n))
+            full = ns_flops([(m, n)], cfg.ns_steps)
+            iters = cfg.ns_steps
+            if backend == "direct" and t_total + full / rate > budget_s:
+                iters = 1
+            u = g
+            if not cfg.ns_only:
+                t0 = time.perf_counter()
+                bufs[i], u = oracle.momentum_update(bufs[i], g, cfg.momentum, cfg.nesterov)
+                t_phase["momentum"] += time.perf_counter() - t0
+                elems["momentum"] += m * n
             t0 = time.perf_counter()
             if backend == "gram":
-                u = g
-                if not cfg.ns_only:
-                    bufs[i], u = oracle.momentum_update(bufs[i], g, cfg.momentum, cfg.nesterov)
                 O = oracle.gram_newton_schulz(u, steps=cfg.ns_steps, restart_iterations=restarts)
-                if not cfg.ns_only:
-                    params[i] = params[i] - cfg.lr * cfg.weight_decay * params[i] - cfg.lr * O
-            elif cfg.ns_only:
-                oracle.direct_newton_schulz(g, steps=cfg.ns_steps)
+            elif iters == cfg.ns_steps:
+                O = oracle.direct_newton_schulz(u, steps=cfg.ns_steps)
             else:
-                params[i], bufs[i], _ = oracle.muon_step(
-                    params[i], g, bufs[i], lr=cfg.lr, momentum=cfg.momentum,
-                    weight_decay=cfg.weight_decay, nesterov=cfg.nesterov, ns_steps=cfg.ns_steps)
-            t_total += time.perf_counter() - t0
-            flops += ns_flops([(m, n)], cfg.ns_steps)
-            done += 1
+                O = oracle.direct_newton_schulz(u, coefficients=quintic)
+            dt = time.perf_counter() - t0
+            t_phase["ns"] += dt
+            if dt > 5:
+                log(f"oracle: {m}x{n}, {iters} NS iteration(s) in {dt:.1f} s")
+            done = full * iters / cfg.ns_steps
+            ns_flops_done += done
+            rate = ns_flops_done / t_phase["ns"]
+            if not cfg.ns_only:
+                t0 = time.perf_counter()
+                params[i] = oracle.update_param(params[i], O, cfg.lr, cfg.weight_decay)
+                t_phase["update"] += time.perf_counter() - t0
+                elems["update"] += m * n
+            parts.append(f"{m}x{n}" + ("" if iters == cfg.ns_steps else f" ({iters} of "
+                                                                        f"{cfg.ns_steps} NS iterations)"))
+            t_total = sum(t_phase.values())
             if t_total >= budget_s:
                 break
         step += 1
-    nmat = len(cfg.shapes)
+    numel = sum(m * n for m, n in cfg.shapes)
+    ns_step = ns_flops(cfg.shapes, cfg.ns_steps)
+    est = {"ns": ns_step / rate}
+    if not cfg.ns_only:
+        est["momentum"] = t_phase["momentum"] / elems["momentum"] * numel
+        est["update"] = t_phase["update"] / elems["update"] * numel
+    counts = {}
+    for p_ in parts:
+        counts[p_] = counts.get(p_, 0) + 1
+    desc = ", ".join(f"{c} x {k}" for k, c in counts.items())
     return {
-        "value": flops / t_total / 1e12,
+        "value": rate / 1e12,
         "unit": "NS TFLOP/s",
-        "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
+        "cores": blas_threads(),
         "kind": "oracle",
-        "sample": (f"{done} matrices = {done // nmat} whole steps + {done % nmat} of the "
-                   f"{nmat} matrices of a step, {t_total:.1f} s; numpy fp64 BLAS"
+        "cpu_model": cpu_model(),
+        "sample": (f"{len(parts)} matrices of the workload in order, {step} whole steps "
+                   f"and part of the next ({desc}); {t_total:.1f} s; numpy fp64 BLAS"
                    + ("; Gram-space NS" if backend == "gram" else "")),
-        "ms_per_step_estimate": t_total / (done / nmat) * 1e3,
+        "phase_s": {k: round(v, 3) for k, v in t_phase.items()},
+        "step_s_estimate": {k: round(v, 2) for k, v in est.items()},
+        "ms_per_step_estimate": round(sum(est.values()) * 1e3, 1),
     }
 
 
@@ -499,8 +561,10 @@ def main():
     torch.cuda.set_device(device)
     calib_copy(args.calib_copy, device)
     n_sets = 1 if cfg.ns_only else max(1, min(cfg.steps, steps + warmup))
-    log(f"config {cfg.cfg_id} ({cfg.name}): {len(cfg.shapes)} matrices, {n_sets} gradient sets")
-    params, bufs, sets = make_inputs(cfg, n_sets, device)
+    grad_kind = "gauss" if args.grads == "gauss" else cfg.grad_kind
+    log(f"config {cfg.cfg_id} ({cfg.name}): {len(cfg.shapes)} matrices, {n_sets} gradient sets"
+        f" ({grad_kind})")
+    params, bufs, sets = make_inputs(cfg, n_sets, device, grad_kind)
     shapes = list(cfg.shapes)
     flops_step = ns_flops(shapes, cfg.ns_steps)
     backend = args.ns_backend
@@ -522,9 +586,10 @@ def main():
                                    **ns_kw)
         run = call
 
-    # Warm-up; the last warm-up step times every kernel kind once to find
-    # the dominant one.
-    for w in range(max(warmup - 1, 0)):
+    # Warm-up (every gradient set at least once); the last warm-up step
+    # times every kernel kind once to find the dominant one.
+    builds0 = dm.plan_builds()
+    for w in range(max(warmup - 1, n_sets - 1, 0)):
         run(w % n_sets)
     with dm.profile() as prof_all:
         run((warmup - 1) % n_sets if warmup else 0)
@@ -533,24 +598,39 @@ def main():
     log(f"warm-up done; per-kind ms of one step: "
         + ", ".join(f"{k}={v['ms']:.3f}" for k, v in prof_all.rows.items())
         + f"; dominant: {dominant}")
+    builds_warm = dm.plan_builds()
 
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+
+    # Timed region 1: the K steps alone (value, ms_per_step).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
+    for s in range(steps):
+        run((warmup + s) % n_sets)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / steps
+    ns_tflops = flops_step / (ms_step * 1e-3) / 1e12
+    log(f"timed {steps} steps: {ms_step:.4f} ms/step (wall {wall * 1e3 / steps:.4f} ms/step), "
+        f"NS {ns_tflops:.1f} TFLOP/s")
+
+    # Timed region 2: the same K steps with HIP events on the launch stream
+    # around every launch of the dominant kernel (its roofline).
+    torch.cuda.synchronize()
     with dm.profile(kinds=[dominant]) as prof:
         e0.record(stream)
         for s in range(steps):
             run((warmup + s) % n_sets)
         e1.record(stream)
         torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / steps
-    ns_tflops = flops_step / (ms_step * 1e-3) / 1e12
-    log(f"timed {steps} steps: {ms_step:.4f} ms/step (wall {wall * 1e3 / steps:.4f} ms/step), "
-        f"NS {ns_tflops:.1f} TFLOP/s")
+    ms_step_ev = e0.elapsed_time(e1) / steps
+    builds_timed = dm.plan_builds() - builds_warm
+    log(f"evented region: {ms_step_ev:.4f} ms/step; launch tables built: "
+        f"{builds_warm - builds0} in warm-up, {builds_timed} in the timed regions")
 
     row = prof.rows[dominant]
     roof = roofline(row, arith)
@@ -559,12 +639,13 @@ def main():
                  "bytes_per_launch": row["bytes"] / row["launches"],
                  "avg_launch_ms": round(row["ms"] / row["launches"], 5),
                  "launches": row["launches"],
+                 "ms_per_step_evented": round(ms_step_ev, 5),
                  "traffic": traffic_for(dominant, cfg.name)})
 
     cpu = None
     if args.cpu_seconds > 0:
         log("timing the fp64 oracle on the host")
-        cpu = cpu_baseline(cfg, args.cpu_seconds, backend, restarts)
+        cpu = cpu_baseline(cfg, args.cpu_seconds, backend, restarts, grad_sets=sets)
 
     out = {
         "metric": METRIC,
@@ -590,7 +671,7 @@ def main():
             "grad_dtype": cfg.grad_dtype,
             "nesterov": cfg.nesterov,
             "ns_only": cfg.ns_only,
-            "gradients": cfg.grad_kind,
+            "gradients": grad_kind,
             "parallelism": "1 GPU (owner-local batch)",
         },
         "ns_tflop_per_step": round(flops_step / 1e12, 6),
@@ -607,6 +688,7 @@ def main():
                 **{f: roofline(v, arith)[f] for f in ("bound", "mfma_frac", "hbm_frac")}}
             for k, v in prof_all.rows.items() if v["ms"] > 0},
         "matrices_per_s": round(len(shapes) / (ms_step * 1e-3), 1),
+        "launch_tables_built_in_timed_regions": builds_timed,
         "kernel_ms_one_step": {k: round(v["ms"], 4) for k, v in prof_all.rows.items()},
         "roofline": roof,
         "cpu_baseline": cpu,

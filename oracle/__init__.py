@@ -23,6 +23,7 @@ from .muon_ref import (  # noqa: F401
     gram_newton_schulz,
     gram_newton_schulz_distributed_local,
     muon_step,
+    update_param,
     round_to_bf16,
 )
 from .optim_ref import (  # noqa: F401

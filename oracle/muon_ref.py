@@ -277,9 +277,16 @@ def muon_step(param, grad, buf, *, lr: float = 0.02, momentum: float = 0.95,
     new_buf, u = momentum_update(buf, grad, momentum, nesterov)
     O = direct_newton_schulz(u, steps=ns_steps, eps=eps,
                              coefficients=coefficients)
+    return update_param(param, O, lr, weight_decay), new_buf, O
+
+
+def update_param(param, O, lr: float, weight_decay: float = 0.0):
+    """The weight update of a Muon step: ``p - lr*wd*p - lr*O`` in float64
+    (READING: decoupled weight decay on the pre-update p, no shape-dependent
+    factor on the lr; DMuon "HSDP Training (Multi-Node)", What Happens Under
+    the Hood: the owner applies weight decay and the update)."""
     p = np.asarray(param, dtype=np.float64)
-    new_param = p - lr * weight_decay * p - lr * O
-    return new_param, new_buf, O
+    return p - lr * weight_decay * p - lr * O
 
 
 _BF16_DROP = 45  # fp64 keeps 52 explicit mantissa bits, bf16 keeps 7
