@@ -181,6 +181,31 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params,
                                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dmuon_muon_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the workspace, the call's
+ * pointer slots and its launch tables live in a static device array of
+ * 64 MiB per GPU, which the library holds from its first use on that GPU
+ * until the process ends.  The call allocates nothing, on the device or
+ * through any library, and its result is bitwise the one dmuon_muon_step
+ * gives for the same arguments.
+ *   - Batches whose workspace plus launch tables exceed 64 MiB are rejected
+ *     with DMUON_E_UNSUPPORTED (e.g. the fp32 TinyMLP d=256 step fits; one
+ *     TinyMLP d=512 layer fits; the whole 4-layer d=512 step does not).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind: two calls that overlap in time on one GPU (other streams,
+ *     other threads) race and give wrong results.  Calls on one stream are
+ *     ordered and safe.  Nothing in the array needs clearing between calls.
+ * Arguments and errors as dmuon_muon_step.
+ */
+dmuon_status_t dmuon_muon_step_noalloc(const dmuon_batch_t* params,
+                                       const dmuon_batch_t* grads,
+                                       const dmuon_batch_t* bufs,
+                                       const dmuon_ns_cfg_t* cfg,
+                                       float momentum, float lr, float weight_decay,
+                                       int32_t nesterov, void* stream);
+
+/*
  * Gram-space NS of matrices held as column shards of their oriented view
  * (DMuon "API Reference", gram_newton_schulz_distributed_local and its
  * batched variant: the shard group rebuilds only the small Gram matrix by

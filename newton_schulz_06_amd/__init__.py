@@ -65,7 +65,8 @@ EXPORTS = ("dmuon_ns_workspace_size", "dmuon_ns_orthogonalize", "dmuon_muon_step
            "dmuon_gram_local_begin", "dmuon_gram_local_advance",
            "dmuon_clip_workspace_size", "dmuon_clip_grad_norm", "dmuon_adamw_step",
            "dmuon_status_str", "dmuon_last_error", "dmuon_backend_info",
-           "dmuon_profile_begin", "dmuon_profile_end", "dmuon_plan_builds")
+           "dmuon_profile_begin", "dmuon_profile_end", "dmuon_plan_builds",
+           "dmuon_muon_step_noalloc")
 
 _lib = None
 
@@ -93,6 +94,11 @@ def lib():
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p]
     L.dmuon_muon_step.restype = st
+    L.dmuon_muon_step_noalloc.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(Batch),
+                                          ctypes.POINTER(Batch), ctypes.POINTER(NsCfg),
+                                          ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                          ctypes.c_int32, ctypes.c_void_p]
+    L.dmuon_muon_step_noalloc.restype = st
     L.dmuon_gram_local_workspace_size.argtypes = [ctypes.POINTER(Batch), ctypes.c_int32,
                                                   ctypes.POINTER(NsCfg),
                                                   ctypes.POINTER(ctypes.c_size_t)]
@@ -322,6 +328,22 @@ def muon_step(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_decay=0.0, 
                                  ctypes.byref(cfg), float(momentum), float(lr),
                                  float(weight_decay), int(bool(nesterov)), wptr, wbytes,
                                  _stream_handle(stream)))
+
+
+def muon_step_noalloc(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_decay=0.0,
+                      nesterov=True, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
+                      stream=None):
+    """dmuon_muon_step_noalloc: as :func:`muon_step`, with the library's
+    static device scratch instead of a workspace (nothing is allocated)."""
+    params, grads, bufs = list(params), list(grads), list(bufs)
+    bp, kp = make_batch(params)
+    bg, kg = make_batch(grads)
+    bb, kb = make_batch(bufs)
+    cfg, kc = make_cfg(coefficients, ns_steps, eps, prec, "direct", None)
+    _check(lib().dmuon_muon_step_noalloc(ctypes.byref(bp), ctypes.byref(bg), ctypes.byref(bb),
+                                         ctypes.byref(cfg), float(momentum), float(lr),
+                                         float(weight_decay), int(bool(nesterov)),
+                                         _stream_handle(stream)))
 
 
 KINDS = ("momentum", "input", "norm", "syrk", "poly", "update_x", "clip_norm", "clip_scale",

@@ -1250,6 +1250,48 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t*
   return run(*plan, cfg, false, momentum, nesterov ? 1 : 0, lr, decay, b, s);
 }
 
+dmuon_status_t dmuon_muon_step_noalloc(const dmuon_batch_t* params, const dmuon_batch_t* grads,
+                                       const dmuon_batch_t* bufs, const dmuon_ns_cfg_t* cfg,
+                                       float momentum, float lr, float weight_decay,
+                                       int32_t nesterov, void* stream) {
+  g_last_error.clear();
+  Layout L;
+  dmuon_status_t st = check_step(params, grads, bufs, cfg, momentum, lr, weight_decay, &L);
+  if (st || params->count == 0) return st;
+  std::vector<Span> spans;
+  add_spans(spans, params, 0);
+  add_spans(spans, grads, 1);
+  add_spans(spans, bufs, 2);
+  static const char* const names[] = {"params", "grads", "bufs"};
+  if ((st = check_disjoint(spans, names))) return st;
+  // The launch tables, built on the host and not cached: every byte this
+  // call needs on the device lives in the static scratch.
+  Plan* raw = nullptr;
+  if ((st = build_plan(L, grads, params, bufs, false, -1, {}, 0, false, &raw))) return st;
+  std::unique_ptr<Plan> plan(raw);
+  const size_t tab_off = align_up(L.total, kWsAlign);
+  const size_t need = tab_off + plan->image.size();
+  if (need > kScratchBytes)
+    return fail(DMUON_E_UNSUPPORTED, "this batch needs " + std::to_string(need) +
+                                         " bytes of device scratch; the allocation-free step "
+                                         "holds " + std::to_string(kScratchBytes) +
+                                         " (use dmuon_muon_step with a workspace)");
+  void* base = nullptr;
+  hipError_t e = scratch_address(&base);
+  if (e != hipSuccess)
+    return fail(DMUON_E_HIP, std::string("scratch address: ") + hipGetErrorString(e));
+  char* ws = static_cast<char*>(base);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  plan->dtab = ws + tab_off;  // not owned: the plan never frees it
+  e = launch_upload(plan->dtab, plan->image.data(), plan->image.size(), s);
+  if (e != hipSuccess)
+    return fail(DMUON_E_HIP, std::string("launch table upload: ") + hipGetErrorString(e));
+  const float decay = (float)(1.0 - (double)lr * (double)weight_decay);
+  Bases b;
+  if ((st = upload_slots(L, grads, params, bufs, ws, s, &b))) return st;
+  return run(*plan, cfg, false, momentum, nesterov ? 1 : 0, lr, decay, b, s);
+}
+
 dmuon_status_t dmuon_gram_local_workspace_size(const dmuon_batch_t* g, int32_t transposed,
                                                const dmuon_ns_cfg_t* cfg, size_t* bytes) {
   g_last_error.clear();

@@ -236,6 +236,13 @@ hipError_t launch_adamw(const FlatTask* tasks, int ntasks, int total_blocks,
 // allocation-free entry point).
 constexpr int kUploadWords = 256;
 hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+// Device memory of the allocation-free step (dmuon_muon_step_noalloc): a
+// static array of kScratchBytes per device, holding that call's workspace,
+// pointer slots and launch tables.  scratch_address gives this device's
+// address of it (looked up once per device).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_address(void** out);
 hipError_t launch_momentum(const EwTab* tasks, int ntasks, int total_tiles,
                            float momentum, int nesterov, int ns_only, Bases b,
                            hipStream_t s);

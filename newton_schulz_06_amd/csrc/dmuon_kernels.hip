@@ -12,6 +12,7 @@
 // With every operand stored K-contiguous, all three products of one NS
 // iteration are "NT" products C = L R^T and share one MFMA main loop.
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "dmuon_device.h"
@@ -1333,6 +1334,31 @@ hipError_t launch_gemm_k(int tile, int f32_ops, int bk, const GemmTab* tasks, in
 }
 
 }  // namespace
+
+// Scratch of dmuon_muon_step_noalloc (see kScratchBytes): every GPU the
+// library runs on holds one copy until the process ends.  In host code the
+// name is only a handle; the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
   if (bytes % 8 || reinterpret_cast<uintptr_t>(dst) % 8) return hipErrorInvalidValue;
