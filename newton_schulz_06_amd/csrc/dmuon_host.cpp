@@ -670,6 +670,10 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           }
         }
         t.tile_begin = acc;
+        // column windows (win_decode): whole windows of 256 tiles starting on
+        // a window boundary, 8, 16, 32 or 64 tile rows
+        t.win = !t.tri && !L.f32_ops && t.tiles_m % 8 == 0 && 256 % t.tiles_m == 0 &&
+                t.tile_count % 256 == 0 && t.tile_begin % 256 == 0;
         acc += t.tile_count;
         gtasks.push_back(t);
       }

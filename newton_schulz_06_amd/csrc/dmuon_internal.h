@@ -119,7 +119,7 @@ struct GemmTaskT {
   int32_t dst_trans;
   int32_t dst_dtype;
   int32_t add_diag;        // POLY (Gram-space P): add the iteration's a on the diagonal
-  int32_t pad1_;
+  int32_t win;             // full product: tiles in column windows (see win_decode)
 };
 using GemmTask = GemmTaskT<Ptr>;
 using GemmTab = GemmTaskT<RefOf>;

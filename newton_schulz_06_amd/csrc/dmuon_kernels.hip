@@ -359,6 +359,25 @@ __device__ __forceinline__ void tri_decode(int t, int nt, int& tm, int& tn) {
   tm = tn = 0;  // not reached for t < nt(nt+1)/2
 }
 
+// Full-product order in column windows, for a matrix whose tiles start at
+// a multiple of 8 * kXcdChunk in the launch and fill whole windows (the host
+// checks; tiles_m 8, 16, 32 or 64): window W holds all tile rows
+// of 8 * kXcdChunk / tiles_m tile columns, and XCD x (chunk x of the window
+// in xcd_remap's order) takes an 8-row by 4-column block of it.  Each XCD's
+// L2 sees the same 12 operand panels per wave of tiles as in full_decode's
+// order, but a panel of the short operand (rows) is fetched again in every
+// window while it is still in the Infinity Cache, and a panel of the long
+// one (columns) is fetched once per launch instead of once per group of 8
+// tile rows.  Measured on the operand stream of a 8192 x 28672 X update:
+// 5% more bytes per clock.
+__device__ __forceinline__ void win_decode(int t, int tiles_m, int& tm, int& tn) {
+  constexpr int W = 8 * kXcdChunk;
+  const int r = t % W, x = r / kXcdChunk, i = r % kXcdChunk;
+  const int rb = tiles_m / 8;  // 8-row blocks of a window
+  tm = (x % rb) * 8 + (i & 7);
+  tn = (t / W) * (W / tiles_m) + (x / rb) * 4 + (i >> 3);
+}
+
 __device__ __forceinline__ void full_decode(int t, int tiles_m, int tiles_n, int& tm,
                                             int& tn) {
   const int group = t / (GROUP * tiles_n);
@@ -1148,6 +1167,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTab* __restric
   int tm, tn;
   if (G.tri)
     tri_decode(lt, G.tiles_m, tm, tn);
+  else if (G.win)
+    win_decode(lt, G.tiles_m, tm, tn);
   else
     full_decode(lt, G.tiles_m, G.tiles_n, tm, tn);
 
