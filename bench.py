@@ -251,8 +251,9 @@ def cpu_baseline(cfg, budget_s, backend="direct", restarts=None, grad_sets=None)
         "cores": blas_threads(),
         "kind": "oracle",
         "cpu_model": cpu_model(),
-        "sample": (f"{len(parts)} matrices of the workload in order, {step} whole steps "
-                   f"and part of the next ({desc}); {t_total:.1f} s; numpy fp64 BLAS"
+        "sample": (f"{len(parts)} matrices of the workload in order ({len(parts) // len(cfg.shapes)} "
+                   f"whole steps and {len(parts) % len(cfg.shapes)} of the next: {desc}); "
+                   f"{t_total:.1f} s; numpy fp64 BLAS"
                    + ("; Gram-space NS" if backend == "gram" else "")),
         "phase_s": {k: round(v, 3) for k, v in t_phase.items()},
         "step_s_estimate": {k: round(v, 2) for k, v in est.items()},
