@@ -89,18 +89,49 @@ def parse():
                          "'' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the oracle's host timing (0 disables it)")
-    ap.add_argument("--grads", default="workload", choices=["workload", "gauss"],
-                    help="workload: the configuration's gradient recipe (default); gauss: "
-                         "iid N(0,1) gradients of the same shapes and dtype, which calls no "
-                         "solver (QR) while building inputs -- for profiled runs, where "
-                         "kernel work does not depend on the values")
+    ap.add_argument("--grads", default="workload", choices=["workload", "host", "gauss"],
+                    help="workload: the configuration's gradient recipe drawn on the device "
+                         "(default; its Haar factors call the device QR solver); host: the "
+                         "same recipe drawn by the numpy generator on the host and copied "
+                         "in, so the process runs no solver on the device -- for profiled "
+                         "runs; gauss: iid N(0,1) gradients of the same shapes and dtype, "
+                         "drawn on the device without a solver (kernel work does not depend "
+                         "on the values)")
+    ap.add_argument("--launch", default="graph", choices=["graph", "stream"],
+                    help="graph: each gradient set's step is recorded once "
+                         "(dmuon_muon_step_graph / dmuon_ns_orthogonalize_graph) and "
+                         "replayed (default); stream: every step calls the entry point, "
+                         "which launches its kernels one by one. The evented region "
+                         "always launches one by one (its events sit between launches)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of this many MiB first (a "
                          "known-size reference for rocprofv3 byte counters)")
     return ap.parse_args()
 
 
+def _host_sets(cfg, n_sets, device, dtype):
+    """The configuration's gradient recipe drawn by the numpy generator on
+    the host (no device solver), copied to ``device``."""
+    import torch
+    import workloads
+    bases = [None] * len(cfg.shapes)
+    if cfg.grad_kind == "powerlaw_t3" and n_sets > 1:
+        for i, (m, n) in enumerate(cfg.shapes):
+            bases[i] = workloads.powerlaw_basis_np(m, n, cfg.cfg_id, i)
+            log(f"host basis {i + 1}/{len(cfg.shapes)} ready")
+    sets = []
+    for s in range(n_sets):
+        sets.append([torch.from_numpy(workloads.grad_np(cfg.grad_kind, m, n, cfg.cfg_id, s, i,
+                                                        basis=bases[i])).to(device, dtype)
+                     for i, (m, n) in enumerate(cfg.shapes)])
+        log(f"host gradient set {s + 1}/{n_sets} ready")
+    return sets
+
+
 def make_inputs(cfg, n_sets, device, grad_kind=None):
+    """params, zero momentum buffers and ``n_sets`` gradient sets of ``cfg``
+    on ``device``. ``grad_kind``: a gradient recipe drawn on the device, or
+    "host" for the configuration's recipe drawn by numpy on the host."""
     import torch
     import workloads
     from workloads.synth import powerlaw_basis_torch
@@ -110,6 +141,10 @@ def make_inputs(cfg, n_sets, device, grad_kind=None):
     params = [workloads.param_torch(m, n, cfg.cfg_id, i, device, dt[cfg.param_dtype])
               for i, (m, n) in enumerate(shapes)]
     bufs = [torch.zeros(m, n, dtype=torch.float32, device=device) for m, n in shapes]
+    if grad_kind == "host":
+        sets = _host_sets(cfg, n_sets, device, dt[cfg.grad_dtype])
+        torch.cuda.synchronize()
+        return params, bufs, sets
     bases = [None] * len(shapes)
     if grad_kind == "powerlaw_t3":
         for i, (m, n) in enumerate(shapes):
@@ -562,7 +597,7 @@ def main():
     torch.cuda.set_device(device)
     calib_copy(args.calib_copy, device)
     n_sets = 1 if cfg.ns_only else max(1, min(cfg.steps, steps + warmup))
-    grad_kind = "gauss" if args.grads == "gauss" else cfg.grad_kind
+    grad_kind = {"gauss": "gauss", "host": "host"}.get(args.grads, cfg.grad_kind)
     log(f"config {cfg.cfg_id} ({cfg.name}): {len(cfg.shapes)} matrices, {n_sets} gradient sets"
         f" ({grad_kind})")
     params, bufs, sets = make_inputs(cfg, n_sets, device, grad_kind)
@@ -577,23 +612,33 @@ def main():
     arith = "f32" if prec == "f32" else "bf16"
     ns_kw = dict(ns_steps=cfg.ns_steps, prec=prec, backend=backend, restart_iterations=restarts)
 
+    graph = args.launch == "graph"
     if cfg.ns_only:
         outs = [torch.empty_like(g) for g in sets[0]]
         call = dm.PreparedNs(sets[0], outs, **ns_kw)
-        run = lambda i: call()  # noqa: E731
+        run_stream = lambda i: call()  # noqa: E731
+        gcall = dm.PreparedNs(sets[0], outs, workspace=call.ws, graph=True, **ns_kw) if graph \
+            else None
+        run = (lambda i: gcall()) if graph else run_stream  # noqa: E731
     else:
-        call = dm.PreparedMuonStep(params, bufs, sets, lr=cfg.lr, momentum=cfg.momentum,
-                                   weight_decay=cfg.weight_decay, nesterov=cfg.nesterov,
-                                   **ns_kw)
-        run = call
+        step_kw = dict(lr=cfg.lr, momentum=cfg.momentum, weight_decay=cfg.weight_decay,
+                       nesterov=cfg.nesterov, **ns_kw)
+        call = dm.PreparedMuonStep(params, bufs, sets, **step_kw)
+        run_stream = call
+        run = dm.PreparedMuonStep(params, bufs, sets, workspace=call.ws, graph=True,
+                                  **step_kw) if graph else run_stream
 
     # Warm-up (every gradient set at least once); the last warm-up step
     # times every kernel kind once to find the dominant one.
     builds0 = dm.plan_builds()
     for w in range(max(warmup - 1, n_sets - 1, 0)):
         run(w % n_sets)
+    if graph:
+        if not cfg.ns_only:
+            run.record()  # every gradient set's graph, before any timed region
+        run_stream(0)  # the stream path's own warm-up (the evented region uses it)
     with dm.profile() as prof_all:
-        run((warmup - 1) % n_sets if warmup else 0)
+        run_stream((warmup - 1) % n_sets if warmup else 0)
     torch.cuda.synchronize()
     dominant = max(prof_all.rows, key=lambda k: prof_all.rows[k]["ms"])
     log(f"warm-up done; per-kind ms of one step: "
@@ -625,7 +670,7 @@ def main():
     with dm.profile(kinds=[dominant]) as prof:
         e0.record(stream)
         for s in range(steps):
-            run((warmup + s) % n_sets)
+            run_stream((warmup + s) % n_sets)
         e1.record(stream)
         torch.cuda.synchronize()
     ms_step_ev = e0.elapsed_time(e1) / steps
@@ -672,7 +717,8 @@ def main():
             "grad_dtype": cfg.grad_dtype,
             "nesterov": cfg.nesterov,
             "ns_only": cfg.ns_only,
-            "gradients": grad_kind,
+            "gradients": f"{cfg.grad_kind} (numpy, host)" if grad_kind == "host" else grad_kind,
+            "launch": "hip_graph" if graph else "stream",
             "parallelism": "1 GPU (owner-local batch)",
         },
         "ns_tflop_per_step": round(flops_step / 1e12, 6),

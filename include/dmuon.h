@@ -206,6 +206,54 @@ dmuon_status_t dmuon_muon_step_noalloc(const dmuon_batch_t* params,
                                        int32_t nesterov, void* stream);
 
 /*
+ * Recorded calls (HIP graphs), for batches whose step is short enough that
+ * launching its kernels one by one costs a visible share of it (the
+ * TinyMLP shapes of DMuon "Quick Start"; many small owned matrices).
+ *
+ * dmuon_muon_step_graph / dmuon_ns_orthogonalize_graph validate exactly as
+ * dmuon_muon_step / dmuon_ns_orthogonalize, then record the kernels that
+ * call would enqueue -- with these buffer pointers, this workspace and these
+ * hyperparameters -- into an executable graph (nothing runs yet).
+ * dmuon_graph_launch enqueues one replay on `stream`: the same operation,
+ * bitwise the same result as the direct call would give on the buffers'
+ * contents at that point of the stream.
+ *   - The graph keeps the pointers: params, grads, bufs (or g, out) and ws
+ *     must stay allocated, unmoved, until dmuon_graph_destroy; refill the
+ *     gradient buffers between replays.  A new lr, momentum or gradient
+ *     buffer needs a new graph (recording costs a few host milliseconds and
+ *     no device synchronization).
+ *   - Replays of one graph share its workspace: replays that overlap in time
+ *     (different streams without ordering) race.
+ *   - Launch with the recording device current, on any stream of it.
+ *   - The graph holds a reference to its launch tables; they outlive the
+ *     table cache's eviction until the graph is destroyed.
+ *   - Recording must not happen inside another stream capture; an empty
+ *     batch is DMUON_E_INVALID (there is nothing to record).
+ * dmuon_graph_destroy waits for the device to finish outstanding work, then
+ * frees the graph; NULL is a no-op.
+ */
+typedef struct dmuon_graph_s* dmuon_graph_t;
+
+dmuon_status_t dmuon_muon_step_graph(const dmuon_batch_t* params,
+                                     const dmuon_batch_t* grads,
+                                     const dmuon_batch_t* bufs,
+                                     const dmuon_ns_cfg_t* cfg,
+                                     float momentum, float lr, float weight_decay,
+                                     int32_t nesterov,
+                                     void* ws, size_t ws_bytes,
+                                     dmuon_graph_t* graph);
+
+dmuon_status_t dmuon_ns_orthogonalize_graph(const dmuon_batch_t* g,
+                                            const dmuon_batch_t* out,
+                                            const dmuon_ns_cfg_t* cfg,
+                                            void* ws, size_t ws_bytes,
+                                            dmuon_graph_t* graph);
+
+dmuon_status_t dmuon_graph_launch(dmuon_graph_t graph, void* stream);
+
+void dmuon_graph_destroy(dmuon_graph_t graph);
+
+/*
  * Gram-space NS of matrices held as column shards of their oriented view
  * (DMuon "API Reference", gram_newton_schulz_distributed_local and its
  * batched variant: the shard group rebuilds only the small Gram matrix by

@@ -66,7 +66,8 @@ EXPORTS = ("dmuon_ns_workspace_size", "dmuon_ns_orthogonalize", "dmuon_muon_step
            "dmuon_clip_workspace_size", "dmuon_clip_grad_norm", "dmuon_adamw_step",
            "dmuon_status_str", "dmuon_last_error", "dmuon_backend_info",
            "dmuon_profile_begin", "dmuon_profile_end", "dmuon_plan_builds",
-           "dmuon_muon_step_noalloc")
+           "dmuon_muon_step_noalloc", "dmuon_muon_step_graph",
+           "dmuon_ns_orthogonalize_graph", "dmuon_graph_launch", "dmuon_graph_destroy")
 
 _lib = None
 
@@ -99,6 +100,20 @@ def lib():
                                           ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                           ctypes.c_int32, ctypes.c_void_p]
     L.dmuon_muon_step_noalloc.restype = st
+    gp = ctypes.POINTER(ctypes.c_void_p)
+    L.dmuon_muon_step_graph.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(Batch),
+                                        ctypes.POINTER(Batch), ctypes.POINTER(NsCfg),
+                                        ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, gp]
+    L.dmuon_muon_step_graph.restype = st
+    L.dmuon_ns_orthogonalize_graph.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(Batch),
+                                               ctypes.POINTER(NsCfg), ctypes.c_void_p,
+                                               ctypes.c_size_t, gp]
+    L.dmuon_ns_orthogonalize_graph.restype = st
+    L.dmuon_graph_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    L.dmuon_graph_launch.restype = st
+    L.dmuon_graph_destroy.argtypes = [ctypes.c_void_p]
+    L.dmuon_graph_destroy.restype = None
     L.dmuon_gram_local_workspace_size.argtypes = [ctypes.POINTER(Batch), ctypes.c_int32,
                                                   ctypes.POINTER(NsCfg),
                                                   ctypes.POINTER(ctypes.c_size_t)]
@@ -376,13 +391,75 @@ class profile:
         return False
 
 
+class Graph:
+    """A recorded call (dmuon_muon_step_graph / dmuon_ns_orthogonalize_graph):
+    ``g(stream=None)`` enqueues one replay (dmuon_graph_launch); the graph is
+    destroyed with this object.  ``keep`` holds the recorded buffers."""
+
+    def __init__(self, handle, keep):
+        self.handle = handle
+        self._keep = keep
+        self._destroy = lib().dmuon_graph_destroy
+
+    def __call__(self, stream=None):
+        st = lib().dmuon_graph_launch(self.handle, _stream_handle(stream))
+        if st:
+            _check(st)
+
+    def close(self):
+        if self.handle:
+            self._destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+
+def muon_step_graph(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_decay=0.0,
+                    nesterov=True, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
+                    backend="direct", restart_iterations=None, workspace=None):
+    """dmuon_muon_step_graph: records one Muon step on these buffers; call
+    the returned :class:`Graph` to run it."""
+    params, grads, bufs = list(params), list(grads), list(bufs)
+    bp, kp = make_batch(params)
+    bg, kg = make_batch(grads)
+    bb, kb = make_batch(bufs)
+    cfg, kc = make_cfg(coefficients, ns_steps, eps, prec, backend, restart_iterations)
+    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in grads], prec, grads[0].device,
+                           backend)
+    h = ctypes.c_void_p()
+    _check(lib().dmuon_muon_step_graph(ctypes.byref(bp), ctypes.byref(bg), ctypes.byref(bb),
+                                       ctypes.byref(cfg), float(momentum), float(lr),
+                                       float(weight_decay), int(bool(nesterov)), wptr, wbytes,
+                                       ctypes.byref(h)))
+    return Graph(h, (params, grads, bufs, ws))
+
+
+def ns_orthogonalize_graph(gs, outs, *, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
+                           backend="direct", restart_iterations=None, workspace=None):
+    """dmuon_ns_orthogonalize_graph: records outs[i] = NS(gs[i]); call the
+    returned :class:`Graph` to run it."""
+    gs, outs = list(gs), list(outs)
+    bg, kg = make_batch(gs)
+    bo, ko = make_batch(outs)
+    cfg, kc = make_cfg(coefficients, ns_steps, eps, prec, backend, restart_iterations)
+    ws, wptr, wbytes = _ws(workspace, [tuple(g.shape) for g in gs], prec, gs[0].device, backend)
+    h = ctypes.c_void_p()
+    _check(lib().dmuon_ns_orthogonalize_graph(ctypes.byref(bg), ctypes.byref(bo),
+                                              ctypes.byref(cfg), wptr, wbytes, ctypes.byref(h)))
+    return Graph(h, (gs, outs, ws))
+
+
 class PreparedMuonStep:
     """dmuon_muon_step with the descriptors marshalled once, for repeated
-    calls on fixed buffers (one gradient batch per call, chosen by index)."""
+    calls on fixed buffers (one gradient batch per call, chosen by index).
+    ``graph=True`` records each gradient batch's step once
+    (dmuon_muon_step_graph) and replays it on later calls."""
 
     def __init__(self, params, bufs, grad_sets, *, lr=0.02, momentum=0.95, weight_decay=0.0,
                  nesterov=True, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
-                 backend="direct", restart_iterations=None, workspace=None, stream=None):
+                 backend="direct", restart_iterations=None, workspace=None, stream=None,
+                 graph=False):
         self._keep = []
         self.bp, k = make_batch(params); self._keep.append(k)
         self.bb, k = make_batch(bufs); self._keep.append(k)
@@ -400,10 +477,33 @@ class PreparedMuonStep:
         self.scalars = (ctypes.c_float(momentum), ctypes.c_float(lr),
                         ctypes.c_float(weight_decay), ctypes.c_int32(int(bool(nesterov))))
         self.fn = lib().dmuon_muon_step
+        self.graphs = [None] * len(self.bgs) if graph else None
+        self._launch = lib().dmuon_graph_launch
+
+    def record(self):
+        """Records every gradient batch's graph now (graph=True), so that
+        later calls only replay."""
+        for i in range(len(self.bgs)):
+            if self.graphs[i] is None:
+                self._graph(i)
+
+    def _graph(self, i):
+        h = ctypes.c_void_p()
+        _check(lib().dmuon_muon_step_graph(ctypes.byref(self.bp), ctypes.byref(self.bgs[i]),
+                                           ctypes.byref(self.bb), ctypes.byref(self.cfg),
+                                           *self.scalars, self.wptr, self.wbytes,
+                                           ctypes.byref(h)))
+        self.graphs[i] = Graph(h, None)
+        return self.graphs[i]
 
     def __call__(self, i=0):
-        st = self.fn(ctypes.byref(self.bp), ctypes.byref(self.bgs[i]), ctypes.byref(self.bb),
-                     ctypes.byref(self.cfg), *self.scalars, self.wptr, self.wbytes, self.stream)
+        if self.graphs is not None:
+            g = self.graphs[i] or self._graph(i)
+            st = self._launch(g.handle, self.stream)
+        else:
+            st = self.fn(ctypes.byref(self.bp), ctypes.byref(self.bgs[i]), ctypes.byref(self.bb),
+                         ctypes.byref(self.cfg), *self.scalars, self.wptr, self.wbytes,
+                         self.stream)
         if st:
             _check(st)
 
@@ -412,7 +512,8 @@ class PreparedNs:
     """dmuon_ns_orthogonalize with the descriptors marshalled once."""
 
     def __init__(self, gs, outs, *, coefficients=None, ns_steps=5, eps=1e-7, prec="bf16",
-                 backend="direct", restart_iterations=None, workspace=None, stream=None):
+                 backend="direct", restart_iterations=None, workspace=None, stream=None,
+                 graph=False):
         self.bg, self._kg = make_batch(gs)
         self.bo, self._ko = make_batch(outs)
         self.cfg, self._kc = make_cfg(coefficients, ns_steps, eps, prec, backend,
@@ -422,10 +523,21 @@ class PreparedNs:
                                               stream)
         self.stream = _stream_handle(stream)
         self.fn = lib().dmuon_ns_orthogonalize
+        self.graph = None
+        if graph:
+            h = ctypes.c_void_p()
+            _check(lib().dmuon_ns_orthogonalize_graph(ctypes.byref(self.bg), ctypes.byref(self.bo),
+                                                      ctypes.byref(self.cfg), self.wptr,
+                                                      self.wbytes, ctypes.byref(h)))
+            self.graph = Graph(h, None)
+        self._launch = lib().dmuon_graph_launch
 
     def __call__(self):
-        st = self.fn(ctypes.byref(self.bg), ctypes.byref(self.bo), ctypes.byref(self.cfg),
-                     self.wptr, self.wbytes, self.stream)
+        if self.graph is not None:
+            st = self._launch(self.graph.handle, self.stream)
+        else:
+            st = self.fn(ctypes.byref(self.bg), ctypes.byref(self.bo), ctypes.byref(self.cfg),
+                         self.wptr, self.wbytes, self.stream)
         if st:
             _check(st)
 

@@ -354,8 +354,10 @@ std::mutex g_plan_mu;
 // static destructor could run after the HIP runtime has shut down.  Plans
 // are keyed by shapes and options only, so a training loop uses one per
 // batch layout; the eviction (a device synchronization and a free) happens
-// only past kMaxPlans distinct layouts.
-std::vector<std::unique_ptr<Plan>>& g_plans = *new std::vector<std::unique_ptr<Plan>>();
+// only past kMaxPlans distinct layouts.  A recorded graph shares its plan,
+// so an evicted plan lives on until the last graph that launches its
+// tables is destroyed.
+std::vector<std::shared_ptr<Plan>>& g_plans = *new std::vector<std::shared_ptr<Plan>>();
 constexpr size_t kMaxPlans = 256;
 // Plans built so far (dmuon_plan_builds).
 int64_t g_plan_builds = 0;
@@ -729,7 +731,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
 // later call with other buffers (or another workspace) of the same shapes
 // reuses the plan without touching device memory.
 dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_batch_t* dst,
-                        const dmuon_batch_t* bufs, bool ns_only, Plan** out) {
+                        const dmuon_batch_t* bufs, bool ns_only, std::shared_ptr<Plan>* out) {
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
@@ -757,11 +759,11 @@ dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_b
   for (size_t k = g_plans.size(); k-- > 0;) {
     if (g_plans[k]->hash == hash && g_plans[k]->key == key) {
       if (k + 1 != g_plans.size()) {
-        std::unique_ptr<Plan> hit = std::move(g_plans[k]);
+        std::shared_ptr<Plan> hit = std::move(g_plans[k]);
         g_plans.erase(g_plans.begin() + (long)k);
         g_plans.push_back(std::move(hit));
       }
-      *out = g_plans.back().get();
+      *out = g_plans.back();
       return DMUON_OK;
     }
   }
@@ -772,7 +774,7 @@ dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_b
   ++g_plan_builds;
   if (g_plans.size() >= kMaxPlans) g_plans.erase(g_plans.begin());
   g_plans.emplace_back(p);
-  *out = p;
+  *out = g_plans.back();
   return DMUON_OK;
 }
 
@@ -1161,6 +1163,128 @@ dmuon_status_t check_step(const dmuon_batch_t* params, const dmuon_batch_t* grad
   return make_layout(grads, cfg->prec, cfg->backend, L);
 }
 
+// Validation of one dmuon_ns_orthogonalize call (also its graph form).
+dmuon_status_t check_ns_call(const dmuon_batch_t* g, const dmuon_batch_t* out,
+                             const dmuon_ns_cfg_t* cfg, void* ws, size_t ws_bytes, Layout* L) {
+  dmuon_status_t st = check_batch(g, "g", true);
+  if (st) return st;
+  if ((st = check_batch(out, "out", true))) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = same_shapes(g, out, "g", "out"))) return st;
+  if (g->dtype != out->dtype) return fail(DMUON_E_INVALID, "out dtype must equal g dtype");
+  if (g->count == 0) return DMUON_OK;
+  if ((st = make_layout(g, cfg->prec, cfg->backend, L))) return st;
+  if ((st = check_ws(*L, ws, ws_bytes))) return st;
+  // out[i] may be exactly g[i]; nothing else may overlap.
+  std::vector<Span> spans;
+  add_spans(spans, g, 0);
+  for (int i = 0; i < out->count; ++i)
+    if (out->mats[i].ptr != g->mats[i].ptr) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(out->mats[i].ptr);
+      spans.push_back({lo, lo + (uintptr_t)(out->mats[i].m * out->mats[i].n * esize(out->dtype)),
+                       1, i});
+    }
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(ws);
+  spans.push_back({wlo, wlo + L->total, 2, 0});
+  static const char* const names[] = {"g", "out", "ws"};
+  return check_disjoint(spans, names);
+}
+
+// Validation of one dmuon_muon_step call (also its graph form).
+dmuon_status_t check_step_call(const dmuon_batch_t* params, const dmuon_batch_t* grads,
+                               const dmuon_batch_t* bufs, const dmuon_ns_cfg_t* cfg,
+                               float momentum, float lr, float weight_decay, void* ws,
+                               size_t ws_bytes, Layout* L) {
+  dmuon_status_t st = check_step(params, grads, bufs, cfg, momentum, lr, weight_decay, L);
+  if (st || params->count == 0) return st;
+  if ((st = check_ws(*L, ws, ws_bytes))) return st;
+  std::vector<Span> spans;
+  add_spans(spans, params, 0);
+  add_spans(spans, grads, 1);
+  add_spans(spans, bufs, 2);
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(ws);
+  spans.push_back({wlo, wlo + L->total, 3, 0});
+  static const char* const names[] = {"params", "grads", "bufs", "ws"};
+  return check_disjoint(spans, names);
+}
+
+// The kernels of one NS call on stream s: the pointer upload, then run().
+dmuon_status_t enqueue_ns(const Plan& plan, const Layout& L, const dmuon_batch_t* g,
+                          const dmuon_batch_t* out, const dmuon_ns_cfg_t* cfg, void* ws,
+                          hipStream_t s) {
+  Bases b;
+  dmuon_status_t st = upload_slots(L, g, out, nullptr, static_cast<char*>(ws), s, &b);
+  if (st) return st;
+  return run(plan, cfg, true, 0.f, 0, 0.f, 1.f, b, s);
+}
+
+// The kernels of one Muon step on stream s.
+dmuon_status_t enqueue_step(const Plan& plan, const Layout& L, const dmuon_batch_t* params,
+                            const dmuon_batch_t* grads, const dmuon_batch_t* bufs,
+                            const dmuon_ns_cfg_t* cfg, float momentum, float lr,
+                            float weight_decay, int32_t nesterov, void* ws, hipStream_t s) {
+  // decoupled weight decay on the pre-update parameter
+  const float decay = (float)(1.0 - (double)lr * (double)weight_decay);
+  Bases b;
+  dmuon_status_t st = upload_slots(L, grads, params, bufs, static_cast<char*>(ws), s, &b);
+  if (st) return st;
+  return run(plan, cfg, false, momentum, nesterov ? 1 : 0, lr, decay, b, s);
+}
+
+}  // namespace
+
+// A recorded call: its executable graph and the plan whose launch tables the
+// graph's kernels read.
+struct dmuon_graph_s {
+  std::shared_ptr<Plan> plan;
+  hipGraphExec_t exec = nullptr;
+  int device = -1;
+};
+
+namespace {
+
+// Records what `enqueue` launches on a private stream into an executable
+// graph.  Capture is thread-local: other threads' HIP calls are unaffected.
+// Event timing is off while recording (an event would become a graph node).
+template <class F>
+dmuon_status_t record_graph(std::shared_ptr<Plan> plan, dmuon_graph_t* out, F&& enqueue) {
+  int device = -1;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  hipStream_t cs = nullptr;
+  e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess)
+    return fail(DMUON_E_HIP, std::string("capture stream: ") + hipGetErrorString(e));
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return fail(DMUON_E_HIP, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
+  }
+  const bool prof = g_prof.on;
+  g_prof.on = false;
+  const dmuon_status_t st = enqueue(cs);
+  g_prof.on = prof;
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(cs, &graph);
+  (void)hipStreamDestroy(cs);
+  if (st != DMUON_OK || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    if (st != DMUON_OK) return st;
+    return fail(DMUON_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+  }
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess)
+    return fail(DMUON_E_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+  dmuon_graph_s* g = new dmuon_graph_s;
+  g->plan = std::move(plan);
+  g->exec = exec;
+  g->device = device;
+  *out = g;
+  return DMUON_OK;
+}
+
 }  // namespace
 
 static_assert(sizeof(dmuon_clip_stats_t) == sizeof(dmuon::ClipStats), "clip stats layout");
@@ -1192,37 +1316,13 @@ dmuon_status_t dmuon_ns_orthogonalize(const dmuon_batch_t* g, const dmuon_batch_
                                       const dmuon_ns_cfg_t* cfg, void* ws, size_t ws_bytes,
                                       void* stream) {
   g_last_error.clear();
-  dmuon_status_t st = check_batch(g, "g", true);
-  if (st) return st;
-  if ((st = check_batch(out, "out", true))) return st;
-  if ((st = check_cfg(cfg))) return st;
-  if ((st = same_shapes(g, out, "g", "out"))) return st;
-  if (g->dtype != out->dtype) return fail(DMUON_E_INVALID, "out dtype must equal g dtype");
-  if (g->count == 0) return DMUON_OK;
   Layout L;
-  if ((st = make_layout(g, cfg->prec, cfg->backend, &L))) return st;
-  if ((st = check_ws(L, ws, ws_bytes))) return st;
-  // out[i] may be exactly g[i]; nothing else may overlap.
-  std::vector<Span> spans;
-  add_spans(spans, g, 0);
-  for (int i = 0; i < out->count; ++i)
-    if (out->mats[i].ptr != g->mats[i].ptr) {
-      const uintptr_t lo = reinterpret_cast<uintptr_t>(out->mats[i].ptr);
-      spans.push_back({lo, lo + (uintptr_t)(out->mats[i].m * out->mats[i].n * esize(out->dtype)),
-                       1, i});
-    }
-  const uintptr_t wlo = reinterpret_cast<uintptr_t>(ws);
-  spans.push_back({wlo, wlo + L.total, 2, 0});
-  static const char* const names[] = {"g", "out", "ws"};
-  if ((st = check_disjoint(spans, names))) return st;
-
+  dmuon_status_t st = check_ns_call(g, out, cfg, ws, ws_bytes, &L);
+  if (st || g->count == 0) return st;
   std::lock_guard<std::mutex> lock(g_plan_mu);
-  Plan* plan = nullptr;
+  std::shared_ptr<Plan> plan;
   if ((st = get_plan(L, g, out, nullptr, true, &plan))) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  Bases b;
-  if ((st = upload_slots(L, g, out, nullptr, static_cast<char*>(ws), s, &b))) return st;
-  return run(*plan, cfg, true, 0.f, 0, 0.f, 1.f, b, s);
+  return enqueue_ns(*plan, L, g, out, cfg, ws, static_cast<hipStream_t>(stream));
 }
 
 dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t* grads,
@@ -1231,27 +1331,83 @@ dmuon_status_t dmuon_muon_step(const dmuon_batch_t* params, const dmuon_batch_t*
                                void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
   Layout L;
-  dmuon_status_t st = check_step(params, grads, bufs, cfg, momentum, lr, weight_decay, &L);
+  dmuon_status_t st =
+      check_step_call(params, grads, bufs, cfg, momentum, lr, weight_decay, ws, ws_bytes, &L);
   if (st || params->count == 0) return st;
-  if ((st = check_ws(L, ws, ws_bytes))) return st;
-  std::vector<Span> spans;
-  add_spans(spans, params, 0);
-  add_spans(spans, grads, 1);
-  add_spans(spans, bufs, 2);
-  const uintptr_t wlo = reinterpret_cast<uintptr_t>(ws);
-  spans.push_back({wlo, wlo + L.total, 3, 0});
-  static const char* const names[] = {"params", "grads", "bufs", "ws"};
-  if ((st = check_disjoint(spans, names))) return st;
-
-  // decoupled weight decay on the pre-update parameter
-  const float decay = (float)(1.0 - (double)lr * (double)weight_decay);
   std::lock_guard<std::mutex> lock(g_plan_mu);
-  Plan* plan = nullptr;
+  std::shared_ptr<Plan> plan;
   if ((st = get_plan(L, grads, params, bufs, false, &plan))) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  Bases b;
-  if ((st = upload_slots(L, grads, params, bufs, static_cast<char*>(ws), s, &b))) return st;
-  return run(*plan, cfg, false, momentum, nesterov ? 1 : 0, lr, decay, b, s);
+  return enqueue_step(*plan, L, params, grads, bufs, cfg, momentum, lr, weight_decay, nesterov,
+                      ws, static_cast<hipStream_t>(stream));
+}
+
+dmuon_status_t dmuon_muon_step_graph(const dmuon_batch_t* params, const dmuon_batch_t* grads,
+                                     const dmuon_batch_t* bufs, const dmuon_ns_cfg_t* cfg,
+                                     float momentum, float lr, float weight_decay,
+                                     int32_t nesterov, void* ws, size_t ws_bytes,
+                                     dmuon_graph_t* graph) {
+  g_last_error.clear();
+  if (!graph) return fail(DMUON_E_INVALID, "graph: null");
+  *graph = nullptr;
+  Layout L;
+  dmuon_status_t st =
+      check_step_call(params, grads, bufs, cfg, momentum, lr, weight_decay, ws, ws_bytes, &L);
+  if (st) return st;
+  if (params->count == 0) return fail(DMUON_E_INVALID, "params: an empty batch has no graph");
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  std::shared_ptr<Plan> plan;
+  if ((st = get_plan(L, grads, params, bufs, false, &plan))) return st;
+  const Plan& pl = *plan;
+  return record_graph(std::move(plan), graph, [&](hipStream_t s) {
+    return enqueue_step(pl, L, params, grads, bufs, cfg, momentum, lr, weight_decay, nesterov, ws,
+                        s);
+  });
+}
+
+dmuon_status_t dmuon_ns_orthogonalize_graph(const dmuon_batch_t* g, const dmuon_batch_t* out,
+                                            const dmuon_ns_cfg_t* cfg, void* ws,
+                                            size_t ws_bytes, dmuon_graph_t* graph) {
+  g_last_error.clear();
+  if (!graph) return fail(DMUON_E_INVALID, "graph: null");
+  *graph = nullptr;
+  Layout L;
+  dmuon_status_t st = check_ns_call(g, out, cfg, ws, ws_bytes, &L);
+  if (st) return st;
+  if (g->count == 0) return fail(DMUON_E_INVALID, "g: an empty batch has no graph");
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  std::shared_ptr<Plan> plan;
+  if ((st = get_plan(L, g, out, nullptr, true, &plan))) return st;
+  const Plan& pl = *plan;
+  return record_graph(std::move(plan), graph,
+                      [&](hipStream_t s) { return enqueue_ns(pl, L, g, out, cfg, ws, s); });
+}
+
+dmuon_status_t dmuon_graph_launch(dmuon_graph_t graph, void* stream) {
+  g_last_error.clear();
+  if (!graph) return fail(DMUON_E_INVALID, "graph: null");
+  int device = -1;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (device != graph->device)
+    return fail(DMUON_E_INVALID, "graph: recorded on device " + std::to_string(graph->device) +
+                                     ", launched with device " + std::to_string(device) +
+                                     " current");
+  e = hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DMUON_E_HIP, std::string("hipGraphLaunch: ") + hipGetErrorString(e));
+  return DMUON_OK;
+}
+
+void dmuon_graph_destroy(dmuon_graph_t graph) {
+  if (!graph) return;
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  (void)hipSetDevice(graph->device);
+  // launches still in flight finish before the executable graph goes
+  (void)hipDeviceSynchronize();
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipSetDevice(cur);
+  std::lock_guard<std::mutex> lock(g_plan_mu);  // the plan's last owner may be this graph
+  delete graph;
 }
 
 dmuon_status_t dmuon_muon_step_noalloc(const dmuon_batch_t* params, const dmuon_batch_t* grads,
@@ -1337,7 +1493,7 @@ dmuon_status_t dmuon_gram_local_begin(const dmuon_batch_t* g, const dmuon_batch_
   dmuon_status_t st = local_setup(g, out, transposed, cfg, ws, ws_bytes, &L);
   if (st || g->count == 0) return st;
   std::lock_guard<std::mutex> lock(g_plan_mu);
-  Plan* plan = nullptr;
+  std::shared_ptr<Plan> plan;
   if ((st = get_plan(L, g, out, nullptr, true, &plan))) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   Bases b;
@@ -1358,7 +1514,7 @@ dmuon_status_t dmuon_gram_local_advance(const dmuon_batch_t* g, const dmuon_batc
     return fail(DMUON_E_INVALID, "window must be in [0, " + std::to_string(windows) + ")");
   if (g->count == 0) return DMUON_OK;
   std::lock_guard<std::mutex> lock(g_plan_mu);
-  Plan* plan = nullptr;
+  std::shared_ptr<Plan> plan;
   if ((st = get_plan(L, g, out, nullptr, true, &plan))) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   Bases b;

@@ -318,6 +318,59 @@ def test_step_rejects(case):
     assert st == dm.DMUON_E_INVALID, (case, st, _err())
 
 
+# ------------------------------------------------- recorded calls (graphs) --
+
+def _step_graph(p, g, b, cfg, mu=0.95, lr=0.02, ws=FAKE_WS, ws_bytes=1 << 40, out=True):
+    h = ctypes.c_void_p(0x1234)
+    st = dm.lib().dmuon_muon_step_graph(ctypes.byref(p), ctypes.byref(g), ctypes.byref(b),
+                                        ctypes.byref(cfg), mu, lr, 0.0, 1, ctypes.c_void_p(ws),
+                                        ws_bytes, ctypes.byref(h) if out else None)
+    return st, h
+
+
+@pytest.mark.parametrize("case", sorted(STEP_BAD))
+def test_step_graph_rejects_what_the_step_rejects(case):
+    """The graph form validates as the direct call, before anything is
+    recorded, and leaves no handle behind."""
+    c = STEP_BAD[case]
+    p, k1 = _mats([(*c.get("pshape", (8, 8)), c.get("pptr", FAKE_O))])
+    g, k2 = _mats([(8, 8, c.get("gptr", FAKE_G))])
+    b, k3 = _mats([(8, 8, FAKE_B)], c.get("bdt", dm.DMUON_F32))
+    cfg, kc = dm.make_cfg()
+    st, h = _step_graph(p, g, b, cfg, mu=c.get("mu", 0.95), lr=c.get("lr", 0.02))
+    assert st == dm.DMUON_E_INVALID, (case, st, _err())
+    assert not h.value
+
+
+@pytest.mark.parametrize("case", ["null batch", "shape differs", "partial overlap",
+                                  "workspace overlaps", "ns_steps 0"])
+def test_ns_graph_rejects_what_ns_rejects(case):
+    g, o, cfg, kw = NS_BAD[case]()
+    h = ctypes.c_void_p(0x1234)
+    st = dm.lib().dmuon_ns_orthogonalize_graph(ctypes.byref(g) if g is not None else None,
+                                               ctypes.byref(o), ctypes.byref(cfg),
+                                               ctypes.c_void_p(FAKE_WS), 1 << 40,
+                                               ctypes.byref(h))
+    assert st == dm.DMUON_E_INVALID, (case, st, _err())
+    assert not h.value
+
+
+def test_graph_arguments():
+    p, k1 = _mats([(8, 8, FAKE_O)])
+    g, k2 = _mats([(8, 8, FAKE_G)])
+    b, k3 = _mats([(8, 8, FAKE_B)])
+    cfg, kc = dm.make_cfg()
+    st, _ = _step_graph(p, g, b, cfg, out=False)
+    assert st == dm.DMUON_E_INVALID and "graph" in _err()
+    st, _ = _step_graph(p, g, b, cfg, ws_bytes=16)
+    assert st == dm.DMUON_E_WORKSPACE, _err()
+    e1, e2, e3 = _mats([])[0], _mats([])[0], _mats([])[0]
+    st, h = _step_graph(e1, e2, e3, cfg, ws=0, ws_bytes=0)
+    assert st == dm.DMUON_E_INVALID and "empty" in _err()
+    assert dm.lib().dmuon_graph_launch(None, None) == dm.DMUON_E_INVALID
+    dm.lib().dmuon_graph_destroy(None)  # a no-op
+
+
 def test_python_binding_maps_errors():
     with pytest.raises(ValueError):
         dm.workspace_size([(0, 3)])

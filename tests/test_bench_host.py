@@ -45,3 +45,16 @@ def test_gram_flops_hand_count():
     assert bench.gram_flops(2, 3) == two + three
     # restarts outside 1..steps-1 have no effect
     assert bench.gram_flops(2, 3, restarts=[0, 5, 9]) == bench.gram_flops(2, 3, restarts=[])
+
+
+def test_host_gradients_reuse_the_power_law_basis():
+    """bench.py --grads host keeps each matrix's power-law basis across
+    steps; a gradient built from the kept basis equals the one that
+    recomputes it."""
+    import numpy as np
+    import workloads
+    for step in (0, 3):
+        basis = workloads.powerlaw_basis_np(80, 48, 5, 1)
+        kept = workloads.grad_np("powerlaw_t3", 80, 48, 5, step, 1, basis=basis)
+        fresh = workloads.grad_np("powerlaw_t3", 80, 48, 5, step, 1)
+        assert np.array_equal(kept, fresh)

@@ -13,6 +13,7 @@ from .synth import (  # noqa: F401
     c4_shapes,
     grad_np,
     param_np,
+    powerlaw_basis_np,
     grad_torch,
     param_torch,
     seed_words,

@@ -118,8 +118,21 @@ def _unit_rms(L):
     return L * (math.sqrt(L.size) / np.linalg.norm(L))
 
 
-def grad_np(kind: str, m: int, n: int, cfg_id: int, step: int, idx: int):
-    """float32 gradient for matrix ``idx`` of config ``cfg_id`` at ``step``."""
+def powerlaw_basis_np(m: int, n: int, cfg_id: int, idx: int):
+    """Unit-rms full-rank L with a k^-1.5 spectrum for matrix ``idx``: the
+    part of every step's power-law gradient that does not change."""
+    brng = np.random.default_rng(seed_words(cfg_id, 0, idx, STREAM_BASIS))
+    k = min(m, n)
+    U = _haar_np(brng, m, k)
+    V = _haar_np(brng, n, k)
+    s = np.arange(1, k + 1, dtype=np.float64) ** -1.5
+    return _unit_rms((U * s) @ V.T)
+
+
+def grad_np(kind: str, m: int, n: int, cfg_id: int, step: int, idx: int, basis=None):
+    """float32 gradient for matrix ``idx`` of config ``cfg_id`` at ``step``.
+    ``basis``: :func:`powerlaw_basis_np` of the same matrix, if the caller
+    keeps it across steps (power-law kind only; recomputed when omitted)."""
     rng = np.random.default_rng(seed_words(cfg_id, step, idx, STREAM_GRAD))
     if kind == "gauss":
         g = rng.standard_normal((m, n))
@@ -134,12 +147,7 @@ def grad_np(kind: str, m: int, n: int, cfg_id: int, step: int, idx: int):
         L = _unit_rms((U * s) @ V.T)
         g = L + 1e-2 * rng.standard_normal((m, n))
     elif kind == "powerlaw_t3":
-        brng = np.random.default_rng(seed_words(cfg_id, 0, idx, STREAM_BASIS))
-        k = min(m, n)
-        U = _haar_np(brng, m, k)
-        V = _haar_np(brng, n, k)
-        s = np.arange(1, k + 1, dtype=np.float64) ** -1.5
-        L = _unit_rms((U * s) @ V.T)
+        L = powerlaw_basis_np(m, n, cfg_id, idx) if basis is None else basis
         g = L + (1e-2 / math.sqrt(3.0)) * rng.standard_t(3, size=(m, n))
     else:
         raise ValueError(f"unknown gradient kind {kind!r}")
