@@ -1174,7 +1174,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTab* __restric
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: wr, wc in SGPRs
   const int wr = (wave >> 1) * WT;
   const int wc = (wave & 1) * WT;
   const int nk = G.K / BK;

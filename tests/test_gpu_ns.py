@@ -253,3 +253,36 @@ def test_deep_stage_full_table():
         want = oracle.direct_newton_schulz(g)
         assert rel_frobenius(o, want) <= 2e-2, s
         assert sigma_dev(o, want) <= 2e-2, s
+
+
+@pytest.mark.parametrize("shapes,prec,dtype,tol", [
+    # fp32 TinyMLP d=256: 30 SYRK and polynomial tiles per launch
+    ([(1024, 256), (1024, 256), (256, 1024)], "f32", "f32", 1e-4),
+    # one TinyMLP d=512 matrix, automatic precision (split-A polynomial)
+    ([(2048, 512)], "auto", "bf16", 2e-2),
+    # two ragged 64-tile matrices in one launch, both orientations,
+    # automatic precision (plain bf16 operands put such Gaussian matrices
+    # just past 2e-2)
+    ([(500, 2000), (2000, 480)], "auto", "bf16", 2e-2),
+])
+def test_few_tile_launches(shapes, prec, dtype, tol):
+    """Launches of fewer tiles than CUs, with long K (up to 2048): the
+    result matches the oracle and repeats bit for bit, also through the
+    single-term tables that isolate the SYRK and the polynomial."""
+    gs_np = [_gen(s, 60 + i) for i, s in enumerate(shapes)]
+    gin, outs = _run_ns(gs_np, dtype, prec)
+    _, again = _run_ns(gs_np, dtype, prec)
+    for i, (g, o) in enumerate(zip(gin, outs)):
+        assert np.array_equal(o, again[i]), ("repeat", i)
+        want = oracle.direct_newton_schulz(g)
+        e = rel_frobenius(o, want)
+        assert e <= tol, (shapes[i], prec, e)
+        if prec != "f32":
+            assert sigma_dev(o, want) <= 2e-2
+    for name in ("syrk", "poly"):
+        gin, outs = _run_ns(gs_np, dtype, prec, coefficients=UNIT_TABLES[name], ns_steps=1)
+        for i, (g, o) in enumerate(zip(gin, outs)):
+            want = oracle.direct_newton_schulz(g, steps=1, coefficients=UNIT_TABLES[name])
+            e = rel_frobenius(o, want)
+            # as test_single_term_tables: 2e-6 with fp32 operands, 1.5e-2 bf16
+            assert e <= (2e-6 if prec == "f32" else 1.5e-2), (name, shapes[i], e)

@@ -170,3 +170,54 @@ def test_step_is_deterministic_and_resumable():
     c = run(2, restored)
     for x, y in zip(a[0] + a[1], c[0] + c[1]):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("nesterov,grad_dtype,ns_steps",
+                         [(True, "bf16", 5), (False, "bf16", 5), (True, "f32", 1),
+                          (False, "f32", 5), (True, "bf16", 1)])
+def test_ragged_256_tiles_nesterov_and_iteration_counts(nesterov, grad_dtype, ns_steps):
+    """256-wide tiles with bf16 operands (fp32 master X) on a ragged shape
+    in both orientations (p = 1200: a 176-row last tile row and column),
+    Nesterov on and off, fp32 and bf16 gradients, one and five NS
+    iterations (with one, the first X update is also the one that writes
+    the param).  Checked against the oracle on the second step, where the
+    momentum buffer is not a multiple of the gradient."""
+    shapes = [(1200, 1500), (1500, 1200)]  # p = 1200: 256-wide tiles, 176-row tail
+    mu, lr = 0.95, 0.02
+    params = [to_dev(workloads.param_np(m, n, 96, i), "f32") for i, (m, n) in enumerate(shapes)]
+    bufs = [torch.zeros(m, n, dtype=torch.float32, device="cuda") for m, n in shapes]
+    ref = [np.zeros(s) for s in shapes]
+    for step in range(2):
+        gs = [to_dev(workloads.grad_np("gauss", m, n, 96, step, i), grad_dtype)
+              for i, (m, n) in enumerate(shapes)]
+        p_before = [exact64(p) for p in params]
+        dm.muon_step(params, gs, bufs, lr=lr, momentum=mu, nesterov=nesterov,
+                     ns_steps=ns_steps, prec="bf16")
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            ref[i], u = oracle.momentum_update(ref[i], exact64(gs[i]), mu, nesterov)
+            assert rel_frobenius(exact64(bufs[i]), ref[i]) <= 1e-6
+            if step == 0:
+                continue
+            O = oracle.direct_newton_schulz(u, steps=ns_steps)
+            O_gpu = (p_before[i] - exact64(params[i])) / lr
+            e = rel_frobenius(O_gpu, O)
+            d = sigma_dev(O_gpu, O)
+            assert e <= 2e-2 and d <= 2e-2, (shapes[i], e, d)
+
+
+@pytest.mark.parametrize("ns_steps", [1, 5])
+def test_in_place_ns_256_tiles(ns_steps):
+    """NS only on 256-wide tiles, in place (out is g) and out of place give
+    the same bits; one iteration (the first X update writes the output) and
+    five."""
+    shapes = [(1200, 1500), (1500, 1200)]
+    gs = [to_dev(workloads.grad_np("gauss", m, n, 97, 0, i), "bf16") for i, (m, n) in enumerate(shapes)]
+    out = dm.ns_orthogonalize(gs, prec="bf16", ns_steps=ns_steps)
+    inp = [g.clone() for g in gs]
+    dm.ns_orthogonalize(inp, outs=inp, prec="bf16", ns_steps=ns_steps)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(out[i], inp[i]), i
+        want = oracle.direct_newton_schulz(exact64(gs[i]), steps=ns_steps)
+        assert rel_frobenius(exact64(out[i]), want) <= 2e-2
