@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Muon step ms & NS TFLOP/s (MFMA util %) per owned matrix batch, 1 GPU"
 # MI355X published dense MFMA peaks (TFLOP/s) and HBM3E bandwidth (GB/s).
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+# Dense MFMA peaks of MI355X: bf16 and fp16 2.5 PFLOP/s, fp32 157.3 TFLOP/s.
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "bf16+f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -609,7 +610,17 @@ def main():
         restarts = [int(v) for v in args.restarts.split(",") if v.strip()]
     # The Gram backend runs on fp32 operands only.
     prec = "f32" if backend == "gram" else cfg.ns_prec
-    arith = "f32" if prec == "f32" else "bf16"
+    # the products' operand type ("bf16+f16": bf16 on the first iteration,
+    # fp16 after; fp32 accumulation everywhere).  The automatic mode takes
+    # fp16 only for matrices below 256-wide tiles (min side < 1024, or
+    # more than 1/8 padding at 256).
+    def tile256(m, n):
+        p = min(m, n)
+        return p >= 1024 and -(-p // 256) * 256 * 8 <= 9 * p
+    if prec == "auto":
+        arith = "bf16" if all(tile256(m, n) for m, n in shapes) else "bf16+f16"
+    else:
+        arith = {"f32": "f32", "f16": "bf16+f16"}.get(prec, "bf16")
     ns_kw = dict(ns_steps=cfg.ns_steps, prec=prec, backend=backend, restart_iterations=restarts)
 
     graph = args.launch == "graph"

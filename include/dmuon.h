@@ -69,15 +69,27 @@ typedef enum { DMUON_F32 = 0, DMUON_BF16 = 1 } dmuon_dtype_t;
  *                         two).
  *   DMUON_NS_BF16_SPLIT_A as DMUON_NS_BF16 with only A split (A^2 from three
  *                         products, B X from one).
- *   DMUON_NS_AUTO         per matrix by p = min(m, n): BF16_SPLIT for
- *                         p <= 128, BF16_SPLIT_A for p <= 1024, else BF16.
+ *   DMUON_NS_F16          as DMUON_NS_BF16 for the first iteration (its
+ *                         input is not normalized yet, and bf16 has fp32's
+ *                         exponent range), then fp16 copies of X, A and B
+ *                         (3 more fraction bits than bf16; the normalized
+ *                         iterates stay inside fp16's range) on the
+ *                         same-rate fp16 MFMA.  No operand is split.
+ *   DMUON_NS_AUTO         per matrix by its tile class: DMUON_NS_F16 on
+ *                         64- and 128-wide tiles (min side below 1024, or
+ *                         where 256-wide tiles would pad more than 1/8),
+ *                         DMUON_NS_BF16 on 256-wide tiles (fp16 products run
+ *                         a few percent slower there and plain bf16 is well
+ *                         within tolerance at those sizes).  Nothing is
+ *                         split.
  */
 typedef enum {
   DMUON_NS_F32 = 0,
   DMUON_NS_BF16 = 1,
   DMUON_NS_BF16_SPLIT = 2,
   DMUON_NS_AUTO = 3,
-  DMUON_NS_BF16_SPLIT_A = 4
+  DMUON_NS_BF16_SPLIT_A = 4,
+  DMUON_NS_F16 = 5
 } dmuon_prec_t;
 
 /* One matrix: m rows, n columns, row-major, device pointer. */

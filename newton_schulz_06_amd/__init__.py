@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdmuon.so
 
 DMUON_OK, DMUON_E_INVALID, DMUON_E_UNSUPPORTED, DMUON_E_WORKSPACE, DMUON_E_HIP = range(5)
 DMUON_F32, DMUON_BF16 = 0, 1
-PREC = {"f32": 0, "bf16": 1, "bf16_split": 2, "auto": 3, "bf16_split_a": 4}
+PREC = {"f32": 0, "bf16": 1, "bf16_split": 2, "auto": 3, "bf16_split_a": 4, "f16": 5}
 
 # Quintic used when no coefficient list is given.
 QUINTIC = (3.4445, -4.7750, 2.0315)

@@ -120,6 +120,86 @@ __device__ __forceinline__ f32x4 unpack_bf16x4(u32x2 w) {
   return r;
 }
 
+// 16-bit operand formats of the bf16-path NS products: Op16<0> bf16,
+// Op16<1> fp16 (IEEE half: 5 exponent bits, 10 fraction bits).  Both
+// convert fp32 with round to nearest even and feed the same-rate gfx950
+// MFMA (v_mfma_f32_32x32x16_bf16 / _f16).  A hi/lo master X keeps its
+// remainder scaled by kLoScale: x - hi is at most half an fp16 spacing of
+// x, which falls in fp16's subnormal range for |x| below 2^-3; scaled by
+// 2^11 it stays normal down to |x| = 2^-14 (bf16's exponent range needs no
+// scale).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int H>
+struct Op16;
+
+// kAScale / kBScale: the A and B operands are stored times these powers of
+// two and their products divided by them in the consumers' epilogues (exact
+// either way).  With ||X|| near 1, the off-diagonal entries of A = X X^T
+// and A^2 fall below fp16's normal range (2^-14) as p grows; scaled they stay
+// normal, with room up to |A| = 16 and |B| = 64 (the NS iterates keep
+// |A| <= ~1.5 and |B| <= ~12 with the quintic).
+template <>
+struct Op16<0> {
+  using vec8 = bf16x8;
+  static constexpr float kLoScale = 1.f;
+  static constexpr float kAScale = 1.f;
+  static constexpr float kBScale = 1.f;
+  static __device__ __forceinline__ uint16_t to(float f) { return to_bf16(f); }
+  static __device__ __forceinline__ uint32_t to2(float a, float b) { return to_bf16x2(a, b); }
+  static __device__ __forceinline__ float from(uint16_t h) { return from_bf16(h); }
+  // element 0 (low half) and element 1 (high half) of a packed pair
+  static __device__ __forceinline__ float e0(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float e1(uint32_t w) {
+    return __uint_as_float(w & 0xffff0000u);
+  }
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Op16<1> {
+  using vec8 = f16x8;
+  static constexpr float kLoScale = 2048.f;
+  static constexpr float kAScale = 4096.f;
+  static constexpr float kBScale = 1024.f;
+  static __device__ __forceinline__ uint16_t to(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+  }
+  static __device__ __forceinline__ uint32_t to2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  static __device__ __forceinline__ float from(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+  }
+  static __device__ __forceinline__ float e0(uint32_t w) { return from((uint16_t)(w & 0xffffu)); }
+  static __device__ __forceinline__ float e1(uint32_t w) { return from((uint16_t)(w >> 16)); }
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int H>
+__device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
+  u32x2 w;
+  w.x = Op16<H>::to2(a, b);
+  w.y = Op16<H>::to2(c, d);
+  return w;
+}
+
+template <int H>
+__device__ __forceinline__ f32x4 unpack4(u32x2 w) {
+  f32x4 r;
+  r[0] = Op16<H>::e0(w.x);
+  r[1] = Op16<H>::e1(w.x);
+  r[2] = Op16<H>::e0(w.y);
+  r[3] = Op16<H>::e1(w.y);
+  return r;
+}
+
 // Last task whose tile_begin <= tile (tasks are sorted by tile_begin).
 template <class Task>
 __device__ __forceinline__ int find_task(const Task* tasks, int ntasks, int tile) {

@@ -38,6 +38,7 @@ size_t esize(int dtype) { return dtype == DMUON_F32 ? 4 : 2; }
 // min side stays within 1/8, else 64 -- small matrices are latency-bound and
 // want many small tiles.  fp32 operands: 64 up to 512, 128 above.
 constexpr int kTiles[3] = {64, 128, 256};
+int tile_index(int tile) { return tile == 64 ? 0 : tile == 128 ? 1 : 2; }
 
 int tile_class(int64_t p, bool f32_ops) {
   if (f32_ops) return p <= 512 ? 64 : 128;
@@ -46,13 +47,6 @@ int tile_class(int64_t p, bool f32_ops) {
   if (p >= 768 && fits(128)) return 128;
   return 64;
 }
-// DMUON_NS_AUTO: hi/lo A and B up to this min side, hi/lo A only up to the
-// next.  With plain bf16 operands iid-noise-like spectra of narrow matrices
-// (e.g. 2048 x 512) land just past a 2e-2 relative error; splitting A (the
-// A^2 product) brings them to ~1.3e-2, and the smallest sides (<= 128)
-// need B split as well.
-constexpr int kAutoSplitMaxP = 128;
-constexpr int kAutoSplitAMaxP = 1024;
 constexpr float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
 // Shortest K for 128-deep main-loop stages (see build_plan).  Measured: the
 // TinyMLP SYRK (K 2048) and polynomial (1536) run 10% faster with them, the
@@ -87,6 +81,14 @@ struct Layout {
   size_t partial_off = 0, scale_off = 0, sink_off = 0, slot_off = 0, total = 0;
   int64_t in_tiles = 0;
   int f32_ops = 0;
+  // Tile classes whose products take fp16 operands after the first
+  // iteration (bit i: kTiles[i]): all with DMUON_NS_F16; with DMUON_NS_AUTO
+  // those below 256.  Measured: fp16 makes the 64- and 128-wide launches
+  // faster than the hi/lo bf16 splits it replaces (TinyMLP x4 0.475 -> 0.427
+  // ms, 512 small matrices 1.93 -> 1.52 ms), but the 256-wide ones 2-4%
+  // slower than plain bf16 (same MFMA peak; Llama-8B 71.4 -> 73.0 ms, 70B
+  // MLP 195.8 -> 202.7 ms), where plain bf16 already has a wide margin.
+  int f16 = 0;
   int gram = 0;  // Gram-space NS layout (fp32 operands)
   // Gram NS on column shards: every matrix's sum of squares (one float
   // each, padded to kWsAlign), then every fp32 Gram matrix back to back, so
@@ -104,6 +106,7 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
   L.gram = backend == DMUON_NS_GRAM;
   L.local = local;
   L.f32_ops = (prec == DMUON_NS_F32) || L.gram;
+  L.f16 = L.f32_ops ? 0 : prec == DMUON_NS_F16 ? 7 : prec == DMUON_NS_AUTO ? 3 : 0;
   const int n = b->count;
   L.g.resize(n);
   int64_t tiles = 0;
@@ -121,11 +124,8 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
         G.P * ld_for(3 * G.P, 2) > INT32_MAX)
       return fail(DMUON_E_UNSUPPORTED, "matrix " + std::to_string(i) +
                                            ": padded size exceeds 2^31 elements");
-    const bool auto_ab = prec == DMUON_NS_AUTO && G.p <= kAutoSplitMaxP;
-    const bool auto_a = prec == DMUON_NS_AUTO && G.p <= kAutoSplitAMaxP;
-    G.split_b = !L.f32_ops && (prec == DMUON_NS_BF16_SPLIT || auto_ab);
-    G.split_a = !L.f32_ops && (prec == DMUON_NS_BF16_SPLIT || prec == DMUON_NS_BF16_SPLIT_A ||
-                               auto_a);
+    G.split_b = !L.f32_ops && prec == DMUON_NS_BF16_SPLIT;
+    G.split_a = !L.f32_ops && (prec == DMUON_NS_BF16_SPLIT || prec == DMUON_NS_BF16_SPLIT_A);
     tiles += (G.P / EW_TILE) * (G.Q / EW_TILE);
   }
   if (tiles > INT32_MAX) return fail(DMUON_E_UNSUPPORTED, "batch too large (tile count)");
@@ -243,7 +243,7 @@ dmuon_status_t check_cfg(const dmuon_ns_cfg_t* cfg) {
     return fail(DMUON_E_INVALID, "cfg: ns_steps must be in [1, 16]");
   if (!std::isfinite(cfg->eps) || cfg->eps < 0.f)
     return fail(DMUON_E_INVALID, "cfg: eps must be finite and >= 0");
-  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_BF16_SPLIT_A)
+  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_F16)
     return fail(DMUON_E_INVALID, "cfg: unknown precision mode");
   if (cfg->coeffs)
     for (int i = 0; i < 3 * cfg->ns_steps; ++i)
@@ -331,6 +331,7 @@ struct Plan {
   bool owns_dtab = true;           // dtab is this plan's own allocation
   std::vector<char> image;         // the launch tables (host copy)
   int f32_ops = 0;
+  int f16 = 0;
   int gram = 0;
   int local = 0;
   size_t in_off = 0, norm_off = 0, fin_off = 0;
@@ -499,6 +500,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   plan->hash = hash;
   plan->device = device;
   plan->f32_ops = L.f32_ops;
+  plan->f16 = L.f16;
   plan->gram = L.gram;
   plan->local = L.local;
   const int n = src->count;
@@ -739,7 +741,7 @@ dmuon_status_t get_plan(const Layout& L, const dmuon_batch_t* src, const dmuon_b
   key.reserve(10 + 3 * (size_t)src->count);
   key.push_back(device);
   key.push_back(ns_only);
-  key.push_back(L.f32_ops);
+  key.push_back(L.f32_ops + 2 * L.f16);  // f16: a tile-class mask
   key.push_back(L.gram);
   key.push_back(L.local);
   key.push_back(src->dtype);
@@ -862,7 +864,7 @@ dmuon_status_t gram_group(const Plan& plan, int gid, const IterArgs& args, Bases
     const GemmTab* tasks = reinterpret_cast<const GemmTab*>(tab + gl.off);
     const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
     const hipError_t e = timed(gl.kind, gl.flops, bytes, s, [&] {
-      return launch_gemm(gl.kind, gl.tile, 1, gl.bk, tasks, gl.ntasks, gl.total, args, b, s);
+      return launch_gemm(gl.kind, gl.tile, 1, gl.bk, 0, 0, tasks, gl.ntasks, gl.total, args, b, s);
     });
     if (e != hipSuccess)
       return fail(DMUON_E_HIP, std::string("Gram NS product launch: ") + hipGetErrorString(e));
@@ -964,10 +966,15 @@ dmuon_status_t run(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_only, fl
     for (const GemmLaunch& gl : plan.gemms) {
       const GemmTab* tasks = reinterpret_cast<const GemmTab*>(tab + gl.off);
       const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
+      // fp16 mode: bf16 products on iteration 0 (its input is not yet
+      // normalized), fp16 after; iteration 0's X update writes fp16 copies
+      const bool f16 = (plan.f16 >> tile_index(gl.tile)) & 1;
+      const int h = f16 && it > 0;
+      const int hn = f16 && it + 1 < cfg->ns_steps ? 1 : h;
       st = check(timed(gl.kind, gl.flops, bytes, s,
                        [&] {
-                         return launch_gemm(gl.kind, gl.tile, plan.f32_ops, gl.bk, tasks, gl.ntasks,
-                                            gl.total, args, b, s);
+                         return launch_gemm(gl.kind, gl.tile, plan.f32_ops, gl.bk, h, hn, tasks,
+                                            gl.ntasks, gl.total, args, b, s);
                        }),
                  "NS product launch");
       if (st) return st;
@@ -1302,7 +1309,7 @@ dmuon_status_t dmuon_ns_workspace_size(const dmuon_batch_t* g, const dmuon_ns_cf
   dmuon_status_t st = check_batch(g, "g", false);
   if (st) return st;
   if (!cfg) return fail(DMUON_E_INVALID, "cfg: null");
-  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_BF16_SPLIT_A)
+  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_F16)
     return fail(DMUON_E_INVALID, "cfg: unknown precision mode");
   if ((st = check_backend(cfg))) return st;
   Layout L;
@@ -1459,7 +1466,7 @@ dmuon_status_t dmuon_gram_local_workspace_size(const dmuon_batch_t* g, int32_t t
   dmuon_status_t st = check_local(cfg, transposed);
   if (st) return st;
   if ((st = check_batch(g, "g", false))) return st;
-  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_BF16_SPLIT_A)
+  if (cfg->prec < DMUON_NS_F32 || cfg->prec > DMUON_NS_F16)
     return fail(DMUON_E_INVALID, "cfg: unknown precision mode");
   if ((st = check_backend(cfg))) return st;
   Layout L;

@@ -251,10 +251,12 @@ hipError_t launch_gram_finalize(const FinTab* tasks, int ntasks, int nblocks, fl
 hipError_t launch_norm(const NormTab* tasks, int ntasks, float eps, Bases b,
                        hipStream_t s);
 // kind in {KIND_SYRK, KIND_POLY, KIND_UPDX}; tile in {64, 128, 256}
-// (bf16 operands) or {64, 128} (fp32 operands); bk, the K depth of a bf16
-// main-loop stage: 64, or 128 for the 64-wide SYRK and polynomial (every
-// task's K then a multiple of 128)
-hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk,
+// (16-bit operands) or {64, 128} (fp32 operands); bk, the K depth of a
+// 16-bit main-loop stage: 64, or 128 for the 64-wide SYRK and polynomial
+// (every task's K then a multiple of 128).  h: operand format of the
+// products (0 bf16, 1 fp16); hn: format of the X copies an X update writes
+// for the next iteration (h, or 1 after a bf16 first iteration).
+hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk, int h, int hn,
                        const GemmTab* tasks, int ntasks, int total_tiles,
                        const IterArgs& args, Bases b, hipStream_t s);
 

@@ -398,7 +398,7 @@ __device__ __forceinline__ void full_decode(int t, int tiles_m, int tiles_n, int
 // and GRAMMUL (C = L R^T) tiles of the upper triangle; off-diagonal tiles
 // are also written mirrored.  AHL: POLY reads
 // A as hi + lo from the split operand rows instead of the fp32 A.
-template <int KIND, int T, bool F32, int NT, bool AHL>
+template <int KIND, int T, bool F32, int NT, bool AHL, int H>
 __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
                                              int tn, int wr, int wc, int lane,
                                              const IterArgs& A) {
@@ -406,7 +406,11 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
   const int col_base = tn * T + wc + (lane & 31);
   const bool mirror = G.tri && (tm != tn);
   const float s = (KIND == KIND_SYRK && A.iter == 0) ? G.scale[1] : 1.f;
-  const float cb = A.b, cc = A.c;
+  // 16-bit operands: A is stored times kA, so the POLY product A A^T comes
+  // times kA^2 (undone by folding 1/kA^2 into c, exactly); B is stored
+  // times kB
+  constexpr float kA = Op16<H>::kAScale, kB = Op16<H>::kBScale;
+  const float cb = A.b, cc = (F32 || KIND != KIND_POLY) ? A.c : A.c * (1.f / (kA * kA));
   const int P = G.P;
   float* F = G.fbuf;
   const int ldf = G.ld_f;
@@ -457,12 +461,12 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
           if constexpr (!F32) {
             uint16_t* o0 = static_cast<uint16_t*>(G.out0);
             const int ld0 = G.ld0;
-            if (!G.split) {
+            if (H == 1 || !G.split) {
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) st_u16(o0 + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
+              for (int rr = 0; rr < 4; ++rr) st_u16(o0 + (size_t)(gi + rr) * ld0 + gj, Op16<H>::to(v[rr] * kA));
               if (mirror)
-                st_u32x2(o0 + (size_t)gj * ld0 + gi, pack_bf16x4(v[0], v[1], v[2], v[3]));
-            } else {
+                st_u32x2(o0 + (size_t)gj * ld0 + gi, pack4<H>(v[0] * kA, v[1] * kA, v[2] * kA, v[3] * kA));
+            } else if constexpr (H == 0) {  // the split modes are bf16 only
               // Rows [hi | lo | hi | hi] along K (4P).  The polynomial
               // product pairs columns 0..3P (hi, lo, hi) with columns
               // P..4P (lo, hi, hi): hi lo^T + lo hi^T + hi hi^T.
@@ -511,12 +515,12 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
           } else {
             uint16_t* o0 = static_cast<uint16_t*>(G.out0);
             const int ld0 = G.ld0;
-            if (!G.split) {
+            if (H == 1 || !G.split) {
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) st_u16(o0 + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
+              for (int rr = 0; rr < 4; ++rr) st_u16(o0 + (size_t)(gi + rr) * ld0 + gj, Op16<H>::to(v[rr] * kB));
               if (mirror)
-                st_u32x2(o0 + (size_t)gj * ld0 + gi, pack_bf16x4(v[0], v[1], v[2], v[3]));
-            } else {
+                st_u32x2(o0 + (size_t)gj * ld0 + gi, pack4<H>(v[0] * kB, v[1] * kB, v[2] * kB, v[3] * kB));
+            } else if constexpr (H == 0) {  // the split modes are bf16 only
               // [hi | lo] along K (2P); the B X product pairs both halves
               // with the same X^T.
               f32x4 hi, lo;
@@ -551,8 +555,8 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
 template <int T>
 constexpr bool kHiLoMaster = T < 256;
 
-// The master X at (r, c): fp32, or xb + xlo (both bf16).
-template <bool F32, bool HL>
+// The master X at (r, c): fp32, or xb + xlo / kLoScale in format H.
+template <bool F32, bool HL, int H>
 __device__ __forceinline__ float load_master(const GemmTask& G, int r, int c) {
   if constexpr (!F32 && !HL) {  // 256-wide tiles: streamed (see ld_f32_nt)
     return ld_f32_nt(G.fbuf + (size_t)r * G.ld_f + c);
@@ -560,8 +564,8 @@ __device__ __forceinline__ float load_master(const GemmTask& G, int r, int c) {
     return ld_f32(G.fbuf + (size_t)r * G.ld_f + c);
   } else {
     const size_t o = (size_t)r * G.ld0 + c;
-    return from_bf16(ld_u16(static_cast<const uint16_t*>(G.out0) + o)) +
-           from_bf16(ld_u16(G.xlo + o));
+    return Op16<H>::from(ld_u16(static_cast<const uint16_t*>(G.out0) + o)) +
+           Op16<H>::from(ld_u16(G.xlo + o)) * (1.f / Op16<H>::kLoScale);
   }
 }
 
@@ -570,7 +574,7 @@ __device__ __forceinline__ float load_master(const GemmTask& G, int r, int c) {
 // remainder), and X^T: in fp32 with fp32 operands, else in bf16 transposed
 // through LDS (8-byte groups XOR-swizzled) so that it leaves the tile as
 // full rows.
-template <int T, bool F32, int NT>
+template <int T, bool F32, int NT, int H, int HN>
 __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
                                               int tn, int wr, int wc, int lane,
                                               const IterArgs& A, uint16_t* stage) {
@@ -594,8 +598,8 @@ __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[N
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          xv[j][g][rr] = load_master<F32, HL>(G, row_base + i * 32 + 8 * g + rr,
-                                              col_base + j * 32);
+          xv[j][g][rr] = load_master<F32, HL, H>(G, row_base + i * 32 + 8 * g + rr,
+                                                 col_base + j * 32);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads together (see sym_epilogue)
 #pragma unroll
     for (int j = 0; j < NT; ++j)
@@ -605,7 +609,8 @@ __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[N
         const int gj = col_base + j * 32;
         f32x4 v;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) v[rr] = s * fmaf(ca, xv[j][g][rr], acc[i][j][4 * g + rr]);
+        for (int rr = 0; rr < 4; ++rr)
+          v[rr] = s * fmaf(ca, xv[j][g][rr], acc[i][j][4 * g + rr] * (1.f / Op16<H>::kBScale));
         if constexpr (F32) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) st_f32(X + (size_t)(gi + rr) * ldf + gj, v[rr]);
@@ -616,16 +621,18 @@ __device__ __forceinline__ void updx_epilogue(const GemmTask& G, f32x16 (&acc)[N
           uint16_t* xb = static_cast<uint16_t*>(G.out0);
           const int ld0 = G.ld0;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) st_u16_nt(xb + (size_t)(gi + rr) * ld0 + gj, to_bf16(v[rr]));
+          for (int rr = 0; rr < 4; ++rr) st_u16_nt(xb + (size_t)(gi + rr) * ld0 + gj, Op16<HN>::to(v[rr]));
           const int il = gi - tm * T, jl = gj - tn * T;
           const int x = 4 * (jl & (T / 4 - 1));
-          *reinterpret_cast<u32x2*>(stage + jl * T + (il ^ x)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<u32x2*>(stage + jl * T + (il ^ x)) = pack4<HN>(v[0], v[1], v[2], v[3]);
         } else {
           uint16_t* xb = static_cast<uint16_t*>(G.out0);
           const int ld0 = G.ld0;
-          const u32x2 h4 = pack_bf16x4(v[0], v[1], v[2], v[3]);
-          const f32x4 hf = unpack_bf16x4(h4);
-          const u32x2 l4 = pack_bf16x4(v[0] - hf[0], v[1] - hf[1], v[2] - hf[2], v[3] - hf[3]);
+          const u32x2 h4 = pack4<HN>(v[0], v[1], v[2], v[3]);
+          const f32x4 hf = unpack4<HN>(h4);
+          constexpr float ls = Op16<HN>::kLoScale;
+          const u32x2 l4 = pack4<HN>((v[0] - hf[0]) * ls, (v[1] - hf[1]) * ls,
+                                     (v[2] - hf[2]) * ls, (v[3] - hf[3]) * ls);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const size_t o = (size_t)(gi + rr) * ld0 + gj;
@@ -675,7 +682,7 @@ __device__ __forceinline__ void dst_store(void* p, float v) {
   else st_u16(static_cast<uint16_t*>(p), to_bf16(v));
 }
 
-template <int T, bool F32, int NT, int DT>
+template <int T, bool F32, int NT, int DT, int H>
 __device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm,
                                            int tn, int wr, int wc, int lane,
                                            const IterArgs& A) {
@@ -700,8 +707,8 @@ __device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          xv[j][g][rr] = load_master<F32, kHiLoMaster<T>>(G, row_base + i * 32 + 8 * g + rr,
-                                                          col_base + j * 32);
+          xv[j][g][rr] = load_master<F32, kHiLoMaster<T>, H>(G, row_base + i * 32 + 8 * g + rr,
+                                                             col_base + j * 32);
     if (upd) {
 #pragma unroll
       for (int j = 0; j < NT; ++j)
@@ -722,7 +729,7 @@ __device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int r = row_base + i * 32 + 8 * g + rr, c = col_base + j * 32;
-          float o = s * fmaf(ca, xv[j][g][rr], acc[i][j][4 * g + rr]);
+          float o = s * fmaf(ca, xv[j][g][rr], acc[i][j][4 * g + rr] * (1.f / Op16<H>::kBScale));
           if (upd) o = fmaf(-A.lr, o, pv4[j][g][rr] * A.decay);
           char* to = (r < pv && c < qv) ? static_cast<char*>(dst) + (r * rs + c * cs) * ESZ
                                         : static_cast<char*>(G.sink);
@@ -742,11 +749,10 @@ __device__ __forceinline__ void updx_final(const GemmTask& G, f32x16 (&acc)[NT][
 // stage the X^T rows are written from (same swizzle as updx_epilogue).
 // LDS: T*T bf16 stage, then R x (T+8) fp32 rows (row stride T+8 puts the
 // two half-waves' rows on disjoint banks): 26 KB (T=64), 49 KB (T=128).
-template <int T, int NT>
+template <int T, int NT, int H, int HN>
 __device__ __forceinline__ void updx_epilogue_hl(const GemmTask& G, f32x16 (&acc)[NT][NT],
                                                  int tm, int tn, int wr, int wc, int lane,
                                                  const IterArgs& A, uint16_t* lds) {
-  constexpr int WT = T / 2;
   constexpr int RB = T == 64 ? 2 : 1;  // 32-row blocks per slab
   constexpr int R = 32 * RB;
   constexpr int LDR = T + 8;
@@ -803,14 +809,15 @@ __device__ __forceinline__ void updx_epilogue_hl(const GemmTask& G, f32x16 (&acc
       uint32_t ho[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x0 = __uint_as_float(hw[e] << 16) + __uint_as_float(lw[e] << 16);
-        const float x1 = __uint_as_float(hw[e] & 0xffff0000u) + __uint_as_float(lw[e] & 0xffff0000u);
+        constexpr float rin = 1.f / Op16<H>::kLoScale, lout = Op16<HN>::kLoScale;
+        const float x0 = Op16<H>::e0(hw[e]) + Op16<H>::e0(lw[e]) * rin;
+        const float x1 = Op16<H>::e1(hw[e]) + Op16<H>::e1(lw[e]) * rin;
         const float acc0 = e < 2 ? a0[2 * e] : a1[2 * e - 4];
         const float acc1 = e < 2 ? a0[2 * e + 1] : a1[2 * e - 3];
-        const float v0 = s * fmaf(ca, x0, acc0), v1 = s * fmaf(ca, x1, acc1);
-        ho[e] = to_bf16x2(v0, v1);
-        lo[e] = to_bf16x2(v0 - __uint_as_float(ho[e] << 16),
-                          v1 - __uint_as_float(ho[e] & 0xffff0000u));
+        constexpr float rb = 1.f / Op16<H>::kBScale;  // B was stored times kB
+        const float v0 = s * fmaf(ca, x0, acc0 * rb), v1 = s * fmaf(ca, x1, acc1 * rb);
+        ho[e] = Op16<HN>::to2(v0, v1);
+        lo[e] = Op16<HN>::to2((v0 - Op16<HN>::e0(ho[e])) * lout, (v1 - Op16<HN>::e1(ho[e])) * lout);
       }
       *(GMEM u32x4*)(xb + go[k]) = u32x4{ho[0], ho[1], ho[2], ho[3]};
       *(GMEM u32x4*)(xlo + go[k]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
@@ -922,33 +929,36 @@ __device__ __forceinline__ void syrk_split_epilogue(const GemmTask& G, f32x16 (&
   }
 }
 
-template <int KIND, int T, bool F32, int NT>
+// H: the operand format of this launch's products (and of the A or B it
+// writes); HN: the format of the X copies an X update writes for the next
+// iteration.  The split modes are bf16 only.
+template <int KIND, int T, bool F32, int NT, int H = 0, int HN = H>
 __device__ __forceinline__ void epilogue(const GemmTask& G, f32x16 (&acc)[NT][NT], int tm, int tn,
                                          int wr, int wc, int lane, const IterArgs& A,
                                          uint16_t* stage) {
   if constexpr (KIND == KIND_UPDX) {
     if (A.fin == FIN_NONE) {
       if constexpr (!F32 && kHiLoMaster<T>)
-        updx_epilogue_hl<T, NT>(G, acc, tm, tn, wr, wc, lane, A, stage);
+        updx_epilogue_hl<T, NT, H, HN>(G, acc, tm, tn, wr, wc, lane, A, stage);
       else
-        updx_epilogue<T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A, stage);
+        updx_epilogue<T, F32, NT, H, HN>(G, acc, tm, tn, wr, wc, lane, A, stage);
     }
     else if (G.dst_dtype == 0)
-      updx_final<T, F32, NT, 0>(G, acc, tm, tn, wr, wc, lane, A);
+      updx_final<T, F32, NT, 0, H>(G, acc, tm, tn, wr, wc, lane, A);
     else
-      updx_final<T, F32, NT, 1>(G, acc, tm, tn, wr, wc, lane, A);
-  } else if constexpr (KIND == KIND_SYRK && !F32 && T < 256) {
+      updx_final<T, F32, NT, 1, H>(G, acc, tm, tn, wr, wc, lane, A);
+  } else if constexpr (KIND == KIND_SYRK && !F32 && T < 256 && H == 0) {
     if (G.split)
       syrk_split_epilogue<T, NT>(G, acc, tm, tn, wr, wc, lane, A, stage);
     else
-      sym_epilogue<KIND, T, F32, NT, false>(G, acc, tm, tn, wr, wc, lane, A);
-  } else if constexpr (KIND == KIND_POLY && !F32) {
+      sym_epilogue<KIND, T, F32, NT, false, H>(G, acc, tm, tn, wr, wc, lane, A);
+  } else if constexpr (KIND == KIND_POLY && !F32 && H == 0) {
     if (G.ahl)
-      sym_epilogue<KIND, T, F32, NT, true>(G, acc, tm, tn, wr, wc, lane, A);
+      sym_epilogue<KIND, T, F32, NT, true, H>(G, acc, tm, tn, wr, wc, lane, A);
     else
-      sym_epilogue<KIND, T, F32, NT, false>(G, acc, tm, tn, wr, wc, lane, A);
+      sym_epilogue<KIND, T, F32, NT, false, H>(G, acc, tm, tn, wr, wc, lane, A);
   } else {
-    sym_epilogue<KIND, T, F32, NT, false>(G, acc, tm, tn, wr, wc, lane, A);
+    sym_epilogue<KIND, T, F32, NT, false, H>(G, acc, tm, tn, wr, wc, lane, A);
   }
 }
 
@@ -1145,7 +1155,7 @@ __device__ __forceinline__ void wait_stages(int younger) {
 template <int T, int BK>
 constexpr int kStages = (T == 64 && BK == 64) ? 3 : 2;
 
-template <int KIND, int T, int BK>
+template <int KIND, int T, int BK, int H, int HN>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTab* __restrict__ tasks,
                                                         int ntasks, int total_tiles, IterArgs A,
                                                         Bases bases) {
@@ -1234,20 +1244,21 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTab* __restric
   // Two operand register sets: the LDS reads of substep ks+1 (or of the
   // next stage's first substep) are in flight while substep ks's MFMAs run,
   // so the LDS latency is not paid once per MFMA row.
-  bf16x8 ra[2][NT], rb[2][NT];
+  using V8 = typename Op16<H>::vec8;
+  V8 ra[2][NT], rb[2][NT];
   auto read_ops = [&](int set, const uint16_t* sa, const uint16_t* sb, int ks) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      ra[set][t] = *reinterpret_cast<const bf16x8*>(sa + offA[ks][t]);
-      rb[set][t] = *reinterpret_cast<const bf16x8*>(sb + offB[ks][t]);
+      ra[set][t] = *reinterpret_cast<const V8*>(sa + offA[ks][t]);
+      rb[set][t] = *reinterpret_cast<const V8*>(sb + offB[ks][t]);
     }
   };
   // MFMAs [first, last) of one substep, row-major over the NT x NT blocks.
   auto mfmas = [&](int set, int first, int last) {
 #pragma unroll
     for (int x = first; x < last; ++x)
-      acc[x / NT][x % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          ra[set][x / NT], rb[set][x % NT], acc[x / NT][x % NT], 0, 0, 0);
+      acc[x / NT][x % NT] =
+          Op16<H>::mfma(ra[set][x / NT], rb[set][x % NT], acc[x / NT][x % NT]);
   };
   // Interleave a substep's MFMAs with the next substep's 2*NT LDS reads.
   auto interleave = [&]() {
@@ -1279,7 +1290,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTab* __restric
         mfmas(0, 0, 1);
       }
     }
-    epilogue<KIND, T, false, NT>(G, acc, tm, tn, wr, wc, lane, A, &lds[0][0][0]);
+    epilogue<KIND, T, false, NT, H, HN>(G, acc, tm, tn, wr, wc, lane, A, &lds[0][0][0]);
     return;
   }
   wait_stages<LOADS, STAGES - 2>(min(nk - 1, STAGES - 2));
@@ -1314,7 +1325,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmTab* __restric
     mfmas(1, HALF, NT * NT);
   }
 
-  epilogue<KIND, T, false, NT>(G, acc, tm, tn, wr, wc, lane, A, &lds[0][0][0]);
+  epilogue<KIND, T, false, NT, H, HN>(G, acc, tm, tn, wr, wc, lane, A, &lds[0][0][0]);
 }
 
 template <int KIND, int T>
@@ -1326,31 +1337,49 @@ hipError_t launch_gemm_f32(const GemmTab* tasks, int ntasks, int total_tiles, co
   return hipGetLastError();
 }
 
-template <int KIND, int T, int BK>
+template <int KIND, int T, int BK, int H, int HN>
 hipError_t launch_gemm_bf16(const GemmTab* tasks, int ntasks, int total_tiles, const IterArgs& A,
                             Bases b, hipStream_t s) {
   const int grid = (total_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_bf16_kernel<KIND, T, BK>), dim3(grid), dim3(256), 0, s, tasks, ntasks,
-                     total_tiles, A, b);
+  hipLaunchKernelGGL((gemm_bf16_kernel<KIND, T, BK, H, HN>), dim3(grid), dim3(256), 0, s, tasks,
+                     ntasks, total_tiles, A, b);
   return hipGetLastError();
 }
 
+// 16-bit operand kernels by tile class and stage depth; H/HN as in epilogue
+// (SYRK and polynomial launches write their output in their own format).
+template <int KIND, int H, int HN>
+hipError_t launch_gemm_h(int tile, int bk, const GemmTab* tasks, int ntasks, int total_tiles,
+                         const IterArgs& A, Bases b, hipStream_t s) {
+  if constexpr (KIND != KIND_UPDX) {
+    if (tile == 64 && bk == 128)
+      return launch_gemm_bf16<KIND, 64, 128, H, HN>(tasks, ntasks, total_tiles, A, b, s);
+  }
+  if (bk != 64) return hipErrorInvalidValue;
+  if (tile == 64) return launch_gemm_bf16<KIND, 64, 64, H, HN>(tasks, ntasks, total_tiles, A, b, s);
+  if (tile == 128)
+    return launch_gemm_bf16<KIND, 128, 64, H, HN>(tasks, ntasks, total_tiles, A, b, s);
+  if (tile == 256)
+    return launch_gemm_bf16<KIND, 256, 64, H, HN>(tasks, ntasks, total_tiles, A, b, s);
+  return hipErrorInvalidValue;
+}
+
 template <int KIND>
-hipError_t launch_gemm_k(int tile, int f32_ops, int bk, const GemmTab* tasks, int ntasks,
-                         int total_tiles, const IterArgs& A, Bases b, hipStream_t s) {
+hipError_t launch_gemm_k(int tile, int f32_ops, int bk, int h, int hn, const GemmTab* tasks,
+                         int ntasks, int total_tiles, const IterArgs& A, Bases b, hipStream_t s) {
   if (f32_ops) {
     if (tile == 64) return launch_gemm_f32<KIND, 64>(tasks, ntasks, total_tiles, A, b, s);
     if (tile == 128) return launch_gemm_f32<KIND, 128>(tasks, ntasks, total_tiles, A, b, s);
     return hipErrorInvalidValue;
   }
-  if constexpr (KIND != KIND_UPDX) {
-    if (tile == 64 && bk == 128)
-      return launch_gemm_bf16<KIND, 64, 128>(tasks, ntasks, total_tiles, A, b, s);
+  if (h == 0 && hn == 0)
+    return launch_gemm_h<KIND, 0, 0>(tile, bk, tasks, ntasks, total_tiles, A, b, s);
+  if (h == 1 && hn == 1)
+    return launch_gemm_h<KIND, 1, 1>(tile, bk, tasks, ntasks, total_tiles, A, b, s);
+  if constexpr (KIND == KIND_UPDX) {  // the first X update of the fp16 mode
+    if (h == 0 && hn == 1)
+      return launch_gemm_h<KIND, 0, 1>(tile, bk, tasks, ntasks, total_tiles, A, b, s);
   }
-  if (bk != 64) return hipErrorInvalidValue;
-  if (tile == 64) return launch_gemm_bf16<KIND, 64, 64>(tasks, ntasks, total_tiles, A, b, s);
-  if (tile == 128) return launch_gemm_bf16<KIND, 128, 64>(tasks, ntasks, total_tiles, A, b, s);
-  if (tile == 256) return launch_gemm_bf16<KIND, 256, 64>(tasks, ntasks, total_tiles, A, b, s);
   return hipErrorInvalidValue;
 }
 
@@ -1414,15 +1443,19 @@ hipError_t launch_norm(const NormTab* tasks, int ntasks, float eps, Bases b, hip
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk, const GemmTab* tasks, int ntasks,
-                       int total_tiles, const IterArgs& A, Bases b, hipStream_t s) {
+hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk, int h, int hn,
+                       const GemmTab* tasks, int ntasks, int total_tiles, const IterArgs& A,
+                       Bases b, hipStream_t s) {
   switch (kind) {
     case KIND_SYRK:
-      return launch_gemm_k<KIND_SYRK>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, b, s);
+      return launch_gemm_k<KIND_SYRK>(tile, f32_ops, bk, h, h, tasks, ntasks, total_tiles, A, b,
+                                      s);
     case KIND_POLY:
-      return launch_gemm_k<KIND_POLY>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, b, s);
+      return launch_gemm_k<KIND_POLY>(tile, f32_ops, bk, h, h, tasks, ntasks, total_tiles, A, b,
+                                      s);
     case KIND_UPDX:
-      return launch_gemm_k<KIND_UPDX>(tile, f32_ops, bk, tasks, ntasks, total_tiles, A, b, s);
+      return launch_gemm_k<KIND_UPDX>(tile, f32_ops, bk, h, hn, tasks, ntasks, total_tiles, A, b,
+                                      s);
     case KIND_GRAMMUL:  // fp32 operands only
       if (!f32_ops) return hipErrorInvalidValue;
       if (tile == 64)

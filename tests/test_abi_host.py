@@ -88,8 +88,8 @@ def _expected_ws(shapes, prec):
         t = _tile(p, prec)
         P, Q = _pad(p, t), _pad(q, t)
         tiles += (P // 64) * (Q // 64)
-        split_b = prec == "bf16_split" or (prec == "auto" and p <= 128)
-        split_a = prec in ("bf16_split", "bf16_split_a") or (prec == "auto" and p <= 1024)
+        split_b = prec == "bf16_split"
+        split_a = prec in ("bf16_split", "bf16_split_a")  # auto (= f16) splits nothing
         if prec == "f32":
             per.append(a(4 * P * _ld(Q, 4)) + 2 * a(4 * Q * _ld(P, 4)) + a(4 * P * _ld(P, 4))
                        + a(4 * P * _ld(P, 4)))
@@ -124,7 +124,7 @@ def test_workspace_size_gram():
         assert dm.workspace_size(shapes, prec, backend="gram") == want
 
 
-@pytest.mark.parametrize("prec", ["f32", "bf16", "bf16_split", "auto", "bf16_split_a"])
+@pytest.mark.parametrize("prec", ["f32", "bf16", "bf16_split", "auto", "bf16_split_a", "f16"])
 def test_workspace_size(prec):
     shapes = [(1024, 256), (256, 1024), (100, 37), (4096, 14336), (32, 480), (544, 800),
               (900, 960), (8192, 28672)]
@@ -175,7 +175,7 @@ def _cfg_with(**fields):
 def test_gram_needs_fp32_operands():
     g, k1 = _mats([(64, 96, FAKE_G)])
     o, k2 = _mats([(64, 96, FAKE_O)])
-    for prec in ("bf16", "bf16_split", "bf16_split_a"):
+    for prec in ("bf16", "bf16_split", "bf16_split_a", "f16"):
         cfg = _keep_cfg(prec=prec, backend="gram")
         assert _call_ns(g, o, cfg) == dm.DMUON_E_UNSUPPORTED, _err()
         assert "fp32" in _err()
