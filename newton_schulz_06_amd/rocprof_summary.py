@@ -31,10 +31,12 @@ def short_name(name: str) -> str:
     m = re.search(r"dmuon::\(anonymous namespace\)::(\w+)(<[^>]*>)?", name)
     if m:
         kern, targs = m.group(1), m.group(2) or ""
-        t = re.match(r"<(\d+), (\d+)(?:, (\d+))?", targs)
+        t = re.match(r"<(\d+), (\d+)(?:, (\d+))?(?:, (\d+), (\d+))?", targs)
         if t and kern.startswith("gemm"):
             bk = f",BK={t.group(3)}" if kern == "gemm_bf16_kernel" and t.group(3) not in (None, "64") else ""
-            return f"{KINDS.get(t.group(1), t.group(1))}[{kern}<T={t.group(2)}{bk}>]"
+            # 16-bit operand formats: inputs and the X copies written next
+            fmt = {("1", "1"): ",f16", ("0", "1"): ",bf16>f16"}.get((t.group(4), t.group(5)), "")
+            return f"{KINDS.get(t.group(1), t.group(1))}[{kern}<T={t.group(2)}{bk}{fmt}>]"
         return kern
     if "elementwise" in name and ("copy" in name.lower() or "direct_copy" in name):
         return "torch_copy"
