@@ -33,15 +33,18 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 size_t esize(int dtype) { return dtype == DMUON_F32 ? 4 : 2; }
 
-// GEMM tile classes (square T x T output tiles).  bf16 operands: the
+// GEMM tile classes (square T x T output tiles).  16-bit operands: the
 // largest of 256 (min side >= 1024) / 128 (>= 768) whose padding of the
 // min side stays within 1/8, else 64 -- small matrices are latency-bound and
-// want many small tiles.  fp32 operands: 64 up to 512, 128 above.
-constexpr int kTiles[3] = {64, 128, 256};
-int tile_index(int tile) { return tile == 64 ? 0 : tile == 128 ? 1 : 2; }
+// want many small tiles.  fp32 operands: 32 up to 256 (direct NS only: the
+// 32-wide kernel splits K over its waves), 64 up to 512, 128 above.
+// Matrices are padded to multiples of max(T, 64) (the element-wise passes
+// work on 64 x 64 tiles).
+constexpr int kTiles[4] = {32, 64, 128, 256};
+int tile_index(int tile) { return tile == 32 ? 0 : tile == 64 ? 1 : tile == 128 ? 2 : 3; }
 
-int tile_class(int64_t p, bool f32_ops) {
-  if (f32_ops) return p <= 512 ? 64 : 128;
+int tile_class(int64_t p, bool f32_ops, bool gram = false) {
+  if (f32_ops) return p <= 256 && !gram ? 32 : p <= 512 ? 64 : 128;
   auto fits = [p](int64_t t) { return round_up(p, t) * 8 <= p * 9; };
   if (p >= 1024 && fits(256)) return 256;
   if (p >= 768 && fits(128)) return 128;
@@ -82,8 +85,8 @@ struct Layout {
   int64_t in_tiles = 0;
   int f32_ops = 0;
   // Tile classes whose products take fp16 operands after the first
-  // iteration (bit i: kTiles[i]): all with DMUON_NS_F16; with DMUON_NS_AUTO
-  // those below 256.  Measured: fp16 makes the 64- and 128-wide launches
+  // iteration (bit tile_index(T)): all with DMUON_NS_F16; with
+  // DMUON_NS_AUTO those below 256.  Measured: fp16 makes the 64- and 128-wide launches
   // faster than the hi/lo bf16 splits it replaces (TinyMLP x4 0.475 -> 0.427
   // ms, 512 small matrices 1.93 -> 1.52 ms), but the 256-wide ones 2-4%
   // slower than plain bf16 (same MFMA peak; Llama-8B 71.4 -> 73.0 ms, 70B
@@ -106,7 +109,8 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
   L.gram = backend == DMUON_NS_GRAM;
   L.local = local;
   L.f32_ops = (prec == DMUON_NS_F32) || L.gram;
-  L.f16 = L.f32_ops ? 0 : prec == DMUON_NS_F16 ? 7 : prec == DMUON_NS_AUTO ? 3 : 0;
+  // bits: tile_index (the 32-wide class has fp32 operands only)
+  L.f16 = L.f32_ops ? 0 : prec == DMUON_NS_F16 ? 0xe : prec == DMUON_NS_AUTO ? 0x6 : 0;
   const int n = b->count;
   L.g.resize(n);
   int64_t tiles = 0;
@@ -117,9 +121,9 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
     G.transposed = orient < 0 ? G.m > G.n : orient;
     G.p = G.transposed ? G.n : G.m;
     G.q = G.transposed ? G.m : G.n;
-    G.tile = tile_class(G.p, L.f32_ops != 0);
-    G.P = round_up(G.p, G.tile);
-    G.Q = round_up(G.q, G.tile);
+    G.tile = tile_class(G.p, L.f32_ops != 0, L.gram || L.local);
+    G.P = round_up(G.p, std::max(G.tile, EW_TILE));
+    G.Q = round_up(G.q, std::max(G.tile, EW_TILE));
     if (G.P * ld_for(G.Q, 4) > INT32_MAX || G.Q * ld_for(G.P, 4) > INT32_MAX ||
         G.P * ld_for(3 * G.P, 2) > INT32_MAX)
       return fail(DMUON_E_UNSUPPORTED, "matrix " + std::to_string(i) +
@@ -580,6 +584,10 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
         }
         if (deep) bk = 128;
       }
+      // The 32-wide class speeds the SYRK and polynomial (K split over the
+      // block's waves); its X updates run on 64-wide tiles (P and Q are
+      // multiples of 64 for every class).
+      const int ltile = (kind == KIND_UPDX && tile == 32) ? 64 : tile;
       const size_t begin = gtasks.size();
       int acc = 0;
       double flops = 0, bytes = 0, bytes_fin = 0;
@@ -590,7 +598,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
         t.L = t.R0 = t.R1 = t.fbuf = t.out0 = t.out1 = t.out2 = t.scale = t.xlo = t.ahl =
             t.sink = t.dst = kRefNone;
         const int P = (int)G.P, Q = (int)G.Q;
-        const int nt = P / tile;
+        const int nt = P / ltile;
         const double p = (double)G.p, q = (double)G.q;
         t.P = P;
         t.scale = scale(i);
@@ -643,7 +651,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
           t.K = G.split_b ? 2 * P : P;
           t.kper = P;
           t.tiles_m = nt;
-          t.tiles_n = Q / tile;
+          t.tiles_n = Q / ltile;
           t.tri = 0;
           t.tile_count = t.tiles_m * t.tiles_n;
           t.fbuf = G.hilo ? kRefNone : wsr(G.xm);
@@ -682,7 +690,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
         gtasks.push_back(t);
       }
       if (gtasks.size() > begin) {
-        GemmLaunch gl{kind, tile, 0, (int)(gtasks.size() - begin), acc, flops, bytes,
+        GemmLaunch gl{kind, ltile, 0, (int)(gtasks.size() - begin), acc, flops, bytes,
                       kind == KIND_UPDX ? bytes_fin : bytes, kind, bk};
         plan->gemms.push_back(gl);
         ranges.push_back({begin, gtasks.size()});

@@ -1092,6 +1092,61 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTab* __restrict
   epilogue<KIND, T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A, nullptr);
 }
 
+// fp32 products of small matrices (direct NS, min side <= 256): 32 x 32
+// output tiles, so a launch has four times the blocks of 64-wide tiles (the
+// TinyMLP d=256 SYRK: 108 instead of 30 on 256 CUs; each 64-wide block is
+// bound by one CU's fp32 MFMA rate).  The block's 4 waves each take a
+// quarter of K, straight from global memory (the operands are L2-resident
+// at these sizes), and add their 32 x 32 partials through LDS in wave
+// order -- a fixed order, inside the block, so no device-scope
+// synchronization -- before wave 0 runs the tile's epilogue.  fp32 MFMA
+// 32x32x2: lane half h supplies k = k0 + 4h + t to instruction t of a
+// group of 4 (both operands, so the sum over k is complete).  K (the
+// task's padded extent, a multiple of 64) splits into 4 x 16-aligned
+// quarters.
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_f32_small_kernel(const GemmTab* __restrict__ tasks,
+                                                         int ntasks, int total_tiles, IterArgs A,
+                                                         Bases bases) {
+  constexpr int T = 32;
+  __shared__ f32x16 part[3][64];
+  const int vb = xcd_remap(blockIdx.x, gridDim.x, total_tiles);
+  if (vb >= total_tiles) return;
+  const GemmTask G = resolve(tasks[find_task(tasks, ntasks, vb)], bases);
+  const int lt = vb - G.tile_begin;
+  int tm, tn;
+  if (G.tri)
+    tri_decode(lt, G.tiles_m, tm, tn);
+  else
+    full_decode(lt, G.tiles_m, G.tiles_n, tm, tn);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  const float* lrow =
+      static_cast<const float*>(G.L) + ((size_t)tm * T + r) * G.ldl + 4 * h;
+  const float* rrow = static_cast<const float*>((A.iter & 1) ? G.R1 : G.R0) +
+                      ((size_t)tn * T + r) * G.ldr + 4 * h;
+  const int kq = G.K / 4;
+  const int kper = G.kper;
+  f32x16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int k0 = wave * kq; k0 < (wave + 1) * kq; k0 += 8) {
+    const f32x4 a = ld_f32x4(lrow + k0);
+    const f32x4 b = ld_f32x4(rrow + k0 % kper);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc, 0, 0, 0);
+  }
+  if (wave > 0) part[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x16 tot[1][1];
+  tot[0][0] = ((acc + part[0][lane]) + part[1][lane]) + part[2][lane];
+  epilogue<KIND, T, true, 1>(G, tot, tm, tn, 0, 0, lane, A, nullptr);
+}
+
 // bf16 main loop fed by direct global->LDS loads (global_load_lds_dwordx4):
 // STAGES buffers of BK k-values per row are kept in flight, so each K-step's
 // loads were issued STAGES-1 steps before they are consumed.  Rows are
@@ -1368,6 +1423,12 @@ template <int KIND>
 hipError_t launch_gemm_k(int tile, int f32_ops, int bk, int h, int hn, const GemmTab* tasks,
                          int ntasks, int total_tiles, const IterArgs& A, Bases b, hipStream_t s) {
   if (f32_ops) {
+    if (tile == 32) {
+      const int grid = (total_tiles + 7) / 8 * 8;
+      hipLaunchKernelGGL((gemm_f32_small_kernel<KIND>), dim3(grid), dim3(256), 0, s, tasks,
+                         ntasks, total_tiles, A, b);
+      return hipGetLastError();
+    }
     if (tile == 64) return launch_gemm_f32<KIND, 64>(tasks, ntasks, total_tiles, A, b, s);
     if (tile == 128) return launch_gemm_f32<KIND, 128>(tasks, ntasks, total_tiles, A, b, s);
     return hipErrorInvalidValue;

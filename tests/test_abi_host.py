@@ -58,9 +58,9 @@ def _ld(n, esz):
     return u * 256 // esz
 
 
-def _tile(p, prec):
+def _tile(p, prec, gram=False):
     if prec == "f32":
-        return 64 if p <= 512 else 128
+        return 32 if p <= 256 and not gram else 64 if p <= 512 else 128
 
     def fits(t):
         return _pad(p, t) * 8 <= p * 9
@@ -86,7 +86,7 @@ def _expected_ws(shapes, prec):
     for m, n in shapes:
         p, q = min(m, n), max(m, n)
         t = _tile(p, prec)
-        P, Q = _pad(p, t), _pad(q, t)
+        P, Q = _pad(p, max(t, 64)), _pad(q, max(t, 64))  # 64 x 64 element-wise tiles
         tiles += (P // 64) * (Q // 64)
         split_b = prec == "bf16_split"
         split_a = prec in ("bf16_split", "bf16_split_a")  # auto (= f16) splits nothing
@@ -115,7 +115,7 @@ def test_workspace_size_gram():
     tiles, per = 0, 0
     for m, n in shapes:
         p, q = min(m, n), max(m, n)
-        t = _tile(p, "f32")
+        t = _tile(p, "f32", gram=True)
         P, Q = _pad(p, t), _pad(q, t)
         tiles += (P // 64) * (Q // 64)
         per += a(4 * P * _ld(Q, 4)) + 2 * a(4 * Q * _ld(P, 4)) + 5 * a(4 * P * _ld(P, 4))
@@ -480,7 +480,7 @@ def _expected_local(shapes, transposed):
     tiles, per, bucket = 0, 0, a(4 * len(shapes))
     for m, n in shapes:
         p, q = (n, m) if transposed else (m, n)
-        t = _tile(p, "f32")
+        t = _tile(p, "f32", gram=True)
         P, Q = _pad(p, t), _pad(q, t)
         tiles += (P // 64) * (Q // 64)
         bucket += a(4 * P * _ld(P, 4))
