@@ -1724,9 +1724,9 @@ int64_t dmuon_plan_builds(void) {
 }
 
 const char* dmuon_backend_info(void) {
-  return "direct NS (SYRK + symmetric poly + update-X) . gfx950 MFMA "
-         "bf16 32x32x16 (tiles 64/128/256) / fp32 32x32x2 (tiles 64/128) . fp32 master X . "
-         "update fused into the last X product";
+  return "direct NS (SYRK + symmetric poly + update-X) or Gram-space NS . gfx950 MFMA "
+         "bf16/fp16 32x32x16 (tiles 64/128/256) / fp32 32x32x2 (tiles 32/64/128) . "
+         "fp32-grade master X . update fused into the last X product";
 }
 
 int32_t dmuon_profile_begin(uint32_t kind_mask) {
