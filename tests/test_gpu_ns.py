@@ -334,3 +334,25 @@ def test_auto_resolution():
     torch.cuda.synchronize()
     assert torch.equal(auto[0], f16[0]) and torch.equal(auto[1], f16[1])
     assert torch.equal(auto[2], bf16[0])
+
+
+def test_f16_mode_you_table_and_special_inputs():
+    """The fp16 mode with the printed YOU coefficient table (larger early
+    coefficients than the quintic: the scaled A and B operands must stay in
+    fp16's range) against the oracle, and a zero and a NaN-holding input
+    (zero stays zero, NaN propagates)."""
+    table = oracle.YOU_COEFFICIENTS
+    shapes = [(300, 700), (2048, 512), (96, 96)]
+    gs_np = [_gen(s, 150 + i) for i, s in enumerate(shapes)]
+    gin, outs = _run_ns(gs_np, "bf16", "f16", coefficients=table, ns_steps=len(table))
+    for s, g, o in zip(shapes, gin, outs):
+        want = oracle.direct_newton_schulz(g, steps=len(table), coefficients=table)
+        assert np.all(np.isfinite(o)), s
+        assert rel_frobenius(o, want) <= 2e-2, (s, rel_frobenius(o, want))
+    z = torch.zeros(64, 200, device="cuda", dtype=torch.bfloat16)
+    n = torch.randn(200, 64, device="cuda").to(torch.bfloat16)
+    n[3, 5] = float("nan")
+    out = dm.ns_orthogonalize([z, n], prec="f16")
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[0]).item() == 0
+    assert torch.isnan(out[1].float()).any().item()
