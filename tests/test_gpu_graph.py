@@ -140,3 +140,26 @@ def test_graph_outlives_table_eviction():
     for i, (m, n) in enumerate(shapes):
         want = oracle.direct_newton_schulz(exact64(gs[i]))
         assert rel_frobenius(exact64(o_direct[i]), want) <= 1e-4
+
+
+def test_gram_backend_graph_replays_bitwise():
+    """A recorded Gram-space NS call (fp32 operands, restart windows) and a
+    recorded fp32 step on 32-wide tiles replay bit for bit what the direct
+    calls compute."""
+    shapes = [(300, 120), (120, 500)]
+    gs = [to_dev(workloads.grad_np("gauss", m, n, 74, 0, i), "f32") for i, (m, n) in enumerate(shapes)]
+    o_direct = [torch.empty_like(t) for t in gs]
+    o_graph = [torch.empty_like(t) for t in gs]
+    graph = dm.ns_orthogonalize_graph(gs, o_graph, prec="f32", backend="gram",
+                                      restart_iterations=[2])
+    for rep in range(2):
+        graph()
+        dm.ns_orthogonalize(gs, o_direct, prec="f32", backend="gram", restart_iterations=[2])
+        torch.cuda.synchronize()
+        _eager_noise()
+        for i in range(len(gs)):
+            assert torch.equal(o_graph[i], o_direct[i]), ("gram", rep, i)
+    for i in range(len(gs)):
+        want = oracle.direct_newton_schulz(exact64(gs[i]))
+        assert rel_frobenius(exact64(o_graph[i]), want) <= 1e-4
+    graph.close()
