@@ -84,7 +84,12 @@ def parse():
                          "gram_local: Gram-space NS of one tensor-parallel rank's blocks")
     ap.add_argument("--ns-backend", default="direct", choices=["direct", "gram"],
                     help="direct: X <- aX + BX every iteration (default); gram: the "
-                         "Gram-space iteration with restarts (fp32 operands)")
+                         "Gram-space iteration with restarts")
+    ap.add_argument("--ns-prec", default=None,
+                    choices=["f32", "bf16", "bf16_split", "bf16_split_a", "auto", "f16"],
+                    help="operand precision of the NS products (default: the "
+                         "configuration's own for the direct backend, f32 for gram; gram "
+                         "takes f32 or f16)")
     ap.add_argument("--restarts", default=None, metavar="K,K,...",
                     help="Gram backend: iterations that start a new window (default: 2; "
                          "'' for none)")
@@ -608,8 +613,8 @@ def main():
     restarts = None
     if args.restarts is not None:
         restarts = [int(v) for v in args.restarts.split(",") if v.strip()]
-    # The Gram backend runs on fp32 operands only.
-    prec = "f32" if backend == "gram" else cfg.ns_prec
+    # The Gram backend runs on fp32 operands unless fp16 is asked for.
+    prec = args.ns_prec or ("f32" if backend == "gram" else cfg.ns_prec)
     # the products' operand type ("bf16+f16": bf16 on the first iteration,
     # fp16 after; fp32 accumulation everywhere).  The automatic mode takes
     # fp16 only for matrices below 256-wide tiles (min side < 1024, or
@@ -619,6 +624,8 @@ def main():
         return p >= 1024 and -(-p // 256) * 256 * 8 <= 9 * p
     if prec == "auto":
         arith = "bf16" if all(tile256(m, n) for m, n in shapes) else "bf16+f16"
+    elif backend == "gram":
+        arith = prec  # f32, or f16 from the first product on
     else:
         arith = {"f32": "f32", "f16": "bf16+f16"}.get(prec, "bf16")
     ns_kw = dict(ns_steps=cfg.ns_steps, prec=prec, backend=backend, restart_iterations=restarts)

@@ -113,10 +113,22 @@ typedef struct {
  *   DMUON_NS_GRAM    Gram space (gram_newton_schulz): per restart window,
  *                    A = X X^T, then per step P = a I + b A + c A^2,
  *                    Q <- P Q, A <- P A P, and X <- Q X at the window's
- *                    end.  Equal to DIRECT in exact arithmetic.  Runs with
- *                    fp32 operands only (prec F32, or AUTO which resolves
- *                    to F32): with bf16 operands the Q factor amplifies the
- *                    rounding of X in the small singular directions.
+ *                    end.  Equal to DIRECT in exact arithmetic.  Operands:
+ *                    fp32 (prec F32, or AUTO, which resolves to F32), or
+ *                    fp16 (prec F16; DMuon "API Reference", the
+ *                    newton_schulz module note: the mixed-precision Gram
+ *                    pipeline in fp16), with X normalized before the first
+ *                    window, A and P A stored times 2^12, P and Q times
+ *                    2^10, fp32 accumulation, and the fp32 A kept for the
+ *                    b A term.  The Q factor amplifies the rounding of X in
+ *                    the small singular directions: relative Frobenius
+ *                    error about 3e-3 on Gaussian inputs, up to 2e-2 on
+ *                    low-rank ones with the default restart.  With F16 the
+ *                    coefficients must keep |Q| below 48 over each window
+ *                    (eigenvalues of A in [0, 1.25]): the quintic does
+ *                    (40.9 over three steps); other tables are rejected
+ *                    with DMUON_E_UNSUPPORTED.  Other precisions:
+ *                    DMUON_E_UNSUPPORTED.
  */
 typedef enum { DMUON_NS_DIRECT = 0, DMUON_NS_GRAM = 1 } dmuon_ns_backend_t;
 
@@ -419,7 +431,8 @@ const char* dmuon_backend_info(void);
  * kernels, the bytes the step must move at minimum).
  * Kinds: 0 momentum, 1 input, 2 norm, 3 syrk, 4 poly, 5 update_x,
  * 6 clip_norm, 7 clip_scale, 8 adamw, 9 gram_mul (a product of two commuting
- * symmetric p x p factors of Gram-space NS).  The last update_x launch of a
+ * symmetric p x p factors of Gram-space NS), 10 gram_x (Gram-space NS with
+ * fp16 operands: X normalized into its fp16 form).  The last update_x launch of a
  * call also applies the parameter update (or writes the NS output), so there
  * is no separate update kind.
  */

@@ -362,7 +362,7 @@ def muon_step_noalloc(params, grads, bufs, *, lr=0.02, momentum=0.95, weight_dec
 
 
 KINDS = ("momentum", "input", "norm", "syrk", "poly", "update_x", "clip_norm", "clip_scale",
-         "adamw", "gram_mul")
+         "adamw", "gram_mul", "gram_x")
 
 
 class profile:

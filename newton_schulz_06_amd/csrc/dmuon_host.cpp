@@ -108,7 +108,8 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
   Layout L;
   L.gram = backend == DMUON_NS_GRAM;
   L.local = local;
-  L.f32_ops = (prec == DMUON_NS_F32) || L.gram;
+  // Gram-space NS: fp32 operands, or fp16 with DMUON_NS_F16 (not on shards)
+  L.f32_ops = (prec == DMUON_NS_F32) || (L.gram && (prec != DMUON_NS_F16 || local));
   // bits: tile_index (the 32-wide class has fp32 operands only)
   L.f16 = L.f32_ops ? 0 : prec == DMUON_NS_F16 ? 0xe : prec == DMUON_NS_AUTO ? 0x6 : 0;
   const int n = b->count;
@@ -178,7 +179,17 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
     G.xt1 = take(e * Q * G.ld_xt);
     if (!L.local && (L.f32_ops || !G.split_a)) G.a32 = take(4 * P * G.ld_a32);
     G.pm = G.pa = G.qa = G.qb = 0;
-    if (L.gram) {
+    if (L.gram && !L.f32_ops) {
+      // fp16 operands: A, P, P A and the Q pair as fp16 (power-of-two
+      // scaled); the fp32 A above feeds the polynomial's linear term
+      G.ld_aop = G.ld_bop = ld_for(G.P, 2);
+      G.aop = take(2 * P * G.ld_aop);
+      G.bop = 0;
+      G.pm = take(2 * P * G.ld_aop);
+      G.pa = take(2 * P * G.ld_aop);
+      G.qa = take(2 * P * G.ld_aop);
+      G.qb = take(2 * P * G.ld_aop);
+    } else if (L.gram) {
       G.aop = G.a32;
       G.ld_aop = G.ld_a32;
       G.ld_bop = G.ld_a32;
@@ -227,6 +238,37 @@ dmuon_status_t check_batch(const dmuon_batch_t* b, const char* name, bool need_p
   return DMUON_OK;
 }
 
+std::vector<int> gram_cuts(const dmuon_ns_cfg_t* cfg);
+
+// Gram-space NS with fp16 operands stores P times 2^10 and Q (a product of
+// a window's P's) times 2^10, so both must stay below 64 in magnitude.  The
+// eigenvalues of A stay within [0, 1.25] for NS coefficient schedules
+// (each step maps an eigenvalue l to l p(l)^2 of the contracting
+// polynomial), so max over that interval of |p_k(l)| bounds ||P_k|| and
+// the product over a window's steps bounds ||Q||.  Reject tables whose
+// bound exceeds 48 (the quintic: 3.44 per step, 41 over three steps).
+dmuon_status_t check_gram16_coeffs(const dmuon_ns_cfg_t* cfg) {
+  const std::vector<int> cuts = gram_cuts(cfg);
+  for (size_t w = 0; w + 1 < cuts.size(); ++w) {
+    double bound = 1.0;
+    for (int k = cuts[w]; k < cuts[w + 1]; ++k) {
+      const float* c = cfg->coeffs ? cfg->coeffs + 3 * k : kQuintic;
+      double mx = 0.0;
+      for (int j = 0; j <= 1000; ++j) {
+        const double l = 1.25 * j / 1000.0;
+        mx = std::max(mx, std::fabs((double)c[0] + (double)c[1] * l + (double)c[2] * l * l));
+      }
+      bound *= mx;
+    }
+    if (!(bound <= 48.0))
+      return fail(DMUON_E_UNSUPPORTED,
+                  "cfg: Gram-space NS with fp16 operands: the coefficients of window " +
+                      std::to_string(w) + " can grow Q to " + std::to_string(bound) +
+                      ", beyond the fp16 range of its scaled form (48)");
+  }
+  return DMUON_OK;
+}
+
 // Backend and restart list (also needed by the workspace-size query).
 dmuon_status_t check_backend(const dmuon_ns_cfg_t* cfg) {
   if (cfg->backend != DMUON_NS_DIRECT && cfg->backend != DMUON_NS_GRAM)
@@ -235,9 +277,10 @@ dmuon_status_t check_backend(const dmuon_ns_cfg_t* cfg) {
     return fail(DMUON_E_INVALID, "cfg: restarts must hold nrestarts entries");
   for (int i = 0; i < cfg->nrestarts; ++i)
     if (cfg->restarts[i] < 0) return fail(DMUON_E_INVALID, "cfg: negative restart index");
-  if (cfg->backend == DMUON_NS_GRAM && cfg->prec != DMUON_NS_F32 && cfg->prec != DMUON_NS_AUTO)
+  if (cfg->backend == DMUON_NS_GRAM && cfg->prec != DMUON_NS_F32 &&
+      cfg->prec != DMUON_NS_AUTO && cfg->prec != DMUON_NS_F16)
     return fail(DMUON_E_UNSUPPORTED,
-                "cfg: Gram-space NS runs with fp32 operands only (prec F32 or AUTO)");
+                "cfg: Gram-space NS runs with fp32 (prec F32 or AUTO) or fp16 (F16) operands");
   return DMUON_OK;
 }
 
@@ -253,7 +296,10 @@ dmuon_status_t check_cfg(const dmuon_ns_cfg_t* cfg) {
     for (int i = 0; i < 3 * cfg->ns_steps; ++i)
       if (!std::isfinite(cfg->coeffs[i]))
         return fail(DMUON_E_INVALID, "cfg: non-finite coefficient");
-  return check_backend(cfg);
+  dmuon_status_t st = check_backend(cfg);
+  if (!st && cfg->backend == DMUON_NS_GRAM && cfg->prec == DMUON_NS_F16)
+    st = check_gram16_coeffs(cfg);
+  return st;
 }
 
 dmuon_status_t same_shapes(const dmuon_batch_t* a, const dmuon_batch_t* b, const char* an,
@@ -340,6 +386,10 @@ struct Plan {
   int local = 0;
   size_t in_off = 0, norm_off = 0, fin_off = 0;
   int nmat = 0, in_tiles = 0, fin_blocks = 0;
+  // Gram-space NS with fp16 operands: the X conversion after the norm
+  size_t x16_off = 0;
+  int x16_tiles = 0;
+  double x16_bytes = 0;
   double in_bytes = 0, norm_bytes = 0, fin_bytes = 0;
   std::vector<GemmLaunch> gemms;  // SYRK launches, then POLY, then UPDX
   ~Plan() {
@@ -378,12 +428,20 @@ bool vec_ok(const void* p, int dtype, int64_t n) {
   return p && reinterpret_cast<uintptr_t>(p) % need == 0 && n % 4 == 0;
 }
 
-// Gram-space NS launch groups (fp32 operands), appended to `gtasks`: one
-// group per (product, buffers), split by tile class like the direct kinds.
+// Gram-space NS launch groups, appended to `gtasks`: one group per
+// (product, buffers), split by tile class like the direct kinds.  fp32
+// operands, or (h16) fp16 ones: X as normalized by gram16_x_kernel, A and
+// P A stored times kA16, P and Q times kB16 (the direct fp16 mode's A and B
+// scales, which its SYRK, polynomial and X-update epilogues apply), fp32
+// accumulation, and the fp32 A beside its fp16 form for the polynomial's
+// linear term.
+constexpr float kA16 = 4096.f, kB16 = 1024.f;
 void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, Plan* plan,
                        std::vector<GemmTab>& gtasks,
                        std::vector<std::pair<size_t, size_t>>& ranges) {
   const int n = (int)L.g.size();
+  const bool h16 = !L.f32_ops;
+  const double e = h16 ? 2.0 : 4.0;  // operand bytes
   auto none = [](GemmTab& t) {
     t.L = t.R0 = t.R1 = t.fbuf = t.out0 = t.out1 = t.out2 = t.scale = t.xlo = t.ahl = t.sink =
         t.dst = kRefNone;
@@ -407,7 +465,8 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
         t.tri = 1;
         t.tile_count = nt * (nt + 1) / 2;
         t.K = t.kper = (int)G.P;
-        t.ldl = t.ldr = t.ld0 = t.ld_f = (int32_t)G.ld_a32;
+        t.ldl = t.ldr = t.ld0 = (int32_t)(h16 ? G.ld_aop : G.ld_a32);
+        t.ld_f = (int32_t)G.ld_a32;
         fill(t, G, i, tile, flops, bytes, bytes_fin);
         t.tile_begin = acc;
         acc += t.tile_count;
@@ -421,43 +480,57 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
     }
   };
   using D = double;
-  // A = X X^T (scaled by 1/(||u||+eps)^2 on the first window)
+  // A = X X^T (fp32 operands: scaled by 1/(||u||+eps)^2 on the first
+  // window; fp16: X is normalized already)
   add_group(GG_SYRK, KIND_SYRK, [&](GemmTab& t, const Geom& G, int, int, D& f, D& b, D&) {
-    t.L = t.R0 = t.R1 = wsr(G.xm);
-    t.ldl = t.ldr = (int32_t)G.ld_xm;
+    t.L = t.R0 = t.R1 = wsr(h16 ? G.xb : G.xm);
+    t.ldl = t.ldr = (int32_t)(h16 ? G.ld_xb : G.ld_xm);
     t.K = t.kper = (int)G.Q;
     t.fbuf = wsr(G.a32);
+    if (h16) t.out0 = wsr(G.aop);
     const D p = (D)G.p, q = (D)G.q;
     f += p * (p + 1) * q;
-    b += 4 * p * q + 4 * p * p;
+    // fp16: X in; A's fp16 form and its fp32 upper triangle out
+    b += h16 ? 2 * p * q + 2 * p * p + 2 * p * (p + 1) : 4 * p * q + 4 * p * p;
   });
   // P = a I + b A + c A^2 (reads A as both operands and for the b A term)
   for (int g : {GG_P_QA, GG_P_PM})
     add_group(g, KIND_POLY, [&](GemmTab& t, const Geom& G, int, int, D& f, D& b, D&) {
-      t.L = t.R0 = t.R1 = wsr(G.a32);
+      t.L = t.R0 = t.R1 = wsr(h16 ? G.aop : G.a32);
       t.fbuf = wsr(G.a32);
       t.out0 = wsr(g == GG_P_QA ? G.qa : G.pm);
       t.add_diag = 1;
       const D p = (D)G.p;
       f += p * p * (p + 1);
-      b += 8 * p * p;
+      b += h16 ? 2 * p * p + 2 * p * (p + 1) + 2 * p * p : 8 * p * p;
     });
-  // symmetric products C = L R (all operands commuting polynomials in A)
-  struct Mul { int group; size_t Geom::*l; size_t Geom::*r; size_t Geom::*out; };
-  const Mul muls[] = {{GG_PA_QA, &Geom::qa, &Geom::a32, &Geom::pa},
-                      {GG_PA_PM, &Geom::pm, &Geom::a32, &Geom::pa},
-                      {GG_A_QA, &Geom::qa, &Geom::pa, &Geom::a32},
-                      {GG_A_PM, &Geom::pm, &Geom::pa, &Geom::a32},
-                      {GG_Q_AB, &Geom::pm, &Geom::qa, &Geom::qb},
-                      {GG_Q_BA, &Geom::pm, &Geom::qb, &Geom::qa}};
+  // symmetric products C = L R (all operands commuting polynomials in A);
+  // `a_out`: the product is the next A (fp16: its fp32 copy too)
+  struct Mul { int group; size_t Geom::*l; size_t Geom::*r; bool a_out; size_t Geom::*out; };
+  const Mul muls[] = {{GG_PA_QA, &Geom::qa, nullptr, false, &Geom::pa},
+                      {GG_PA_PM, &Geom::pm, nullptr, false, &Geom::pa},
+                      {GG_A_QA, &Geom::qa, &Geom::pa, true, nullptr},
+                      {GG_A_PM, &Geom::pm, &Geom::pa, true, nullptr},
+                      {GG_Q_AB, &Geom::pm, &Geom::qa, false, &Geom::qb},
+                      {GG_Q_BA, &Geom::pm, &Geom::qb, false, &Geom::qa}};
   for (const Mul& mu : muls)
     add_group(mu.group, KIND_GRAMMUL, [&](GemmTab& t, const Geom& G, int, int, D& f, D& b, D&) {
+      const size_t a_op = h16 ? G.aop : G.a32;  // A as an operand
       t.L = wsr(G.*mu.l);
-      t.R0 = t.R1 = wsr(G.*mu.r);
-      t.out0 = wsr(G.*mu.out);
+      t.R0 = t.R1 = wsr(mu.r ? G.*mu.r : a_op);
+      t.out0 = wsr(mu.a_out ? a_op : G.*mu.out);
       const D p = (D)G.p;
       f += p * p * (p + 1);
-      b += 12 * p * p;
+      if (h16) {
+        // L is P (times kB16); R is A or P A (kA16) or Q (kB16)
+        const bool r_is_q = mu.group == GG_Q_AB || mu.group == GG_Q_BA;
+        t.g_in = 1.f / (kB16 * (r_is_q ? kB16 : kA16));
+        t.g_out = r_is_q ? kB16 : kA16;
+        if (mu.a_out) t.fbuf = wsr(G.a32);
+        b += 6 * p * p + (mu.a_out ? 2 * p * (p + 1) : 0.0);
+      } else {
+        b += 12 * p * p;
+      }
     });
   // X = Q X at a window's end (the X update with a = 0); the last window
   // writes the caller's matrix
@@ -467,15 +540,20 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
       t.L = wsr(g == GG_QX_QA ? G.qa : G.qb);
       t.R0 = wsr(G.xt0);
       t.R1 = wsr(G.xt1);
-      t.ldl = (int32_t)G.ld_a32;
+      t.ldl = (int32_t)(h16 ? G.ld_aop : G.ld_a32);
       t.ldr = (int32_t)G.ld_xt;
       t.K = t.kper = (int)G.P;
       t.tiles_m = (int)G.P / tile;
       t.tiles_n = (int)G.Q / tile;
       t.tri = 0;
       t.tile_count = t.tiles_m * t.tiles_n;
-      t.fbuf = wsr(G.xm);
+      t.fbuf = G.hilo ? kRefNone : wsr(G.xm);
       t.ld_f = (int32_t)G.ld_xm;
+      if (h16) {  // fp16 X copy and, below 256-wide tiles, its remainder
+        t.out0 = wsr(G.xb);
+        t.ld0 = (int32_t)G.ld_xb;
+        t.xlo = G.hilo ? wsr(G.xlo) : kRefNone;
+      }
       t.out1 = wsr(G.xt0);
       t.out2 = wsr(G.xt1);
       t.ld1 = (int32_t)G.ld_xt;
@@ -487,8 +565,11 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
       t.sink = wsr(L.sink_off);
       const D p = (D)G.p, q = (D)G.q;
       f += 2 * p * p * q;
-      const D in = 4 * p * p + 8 * p * q;  // Q, X^T, and X (read for the a X term)
-      b += in + 8 * p * q;
+      // Q, X^T, and the master X (read for the a X term); then the master X
+      // (fp16: 4 bytes as hi + remainder, or fp32 + fp16 copy) and X^T out
+      const D master_in = h16 ? 4.0 : 4.0, master_out = h16 ? (G.hilo ? 4.0 : 6.0) : 4.0;
+      const D in = e * p * p + p * q * (e + master_in);
+      b += in + p * q * (e + master_out);
       bfin += in + p * q * esize(dst->dtype) * (ns_only ? 1.0 : 2.0);
     });
 }
@@ -561,6 +642,39 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
       plan->fin_bytes += 8.0 * (double)G.p * (double)G.p;
     }
     plan->fin_blocks = blk;
+  }
+
+  // Gram-space NS with fp16 operands: the conversion of the normalized X
+  // (oriented, padded P x Q) into the fp16 operand layout; its X^T goes to
+  // xt1, the buffer the first window's X update reads (iteration 1).
+  std::vector<EwTab> tx16;
+  if (L.gram && !L.f32_ops) {
+    int blk = 0;
+    for (int i = 0; i < n; ++i) {
+      const Geom& G = L.g[i];
+      EwTab t{};
+      t.m = (int32_t)G.P;
+      t.n = (int32_t)G.Q;
+      t.rows = (int32_t)G.P;
+      t.cols = (int32_t)G.Q;
+      t.tiles_c = t.cols / EW_TILE;
+      t.tile_begin = blk;
+      t.tile_count = (t.rows / EW_TILE) * t.tiles_c;
+      t.ldx = (int32_t)G.ld_xm;
+      t.ldxb = (int32_t)G.ld_xb;
+      t.ldt = (int32_t)G.ld_xt;
+      t.src = t.buf = t.partial = kRefNone;
+      t.xm = G.hilo ? kRefNone : wsr(G.xm);
+      t.xb = wsr(G.xb);
+      t.xlo = G.hilo ? wsr(G.xlo) : kRefNone;
+      t.xt = wsr(G.xt1);
+      t.scale = scale(i);
+      blk += t.tile_count;
+      tx16.push_back(t);
+      // master in (4 bytes); master (4, or fp32 + fp16 copy: 6) and fp16 X^T out
+      plan->x16_bytes += (double)G.p * (double)G.q * (4.0 + (G.hilo ? 4.0 : 6.0) + 2.0);
+    }
+    plan->x16_tiles = blk;
   }
 
   // GEMM tasks, grouped by (kind, tile class).
@@ -708,6 +822,7 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   plan->in_off = place(sizeof(EwTab) * n);
   plan->norm_off = place(sizeof(NormTab) * n);
   plan->fin_off = place(sizeof(FinTab) * tfin.size());
+  plan->x16_off = place(sizeof(EwTab) * tx16.size());
   const size_t g_off = place(sizeof(GemmTab) * gtasks.size());
   for (size_t k = 0; k < plan->gemms.size(); ++k)
     plan->gemms[k].off = g_off + sizeof(GemmTab) * ranges[k].first;
@@ -717,6 +832,8 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
   std::memcpy(host.data() + plan->norm_off, tnorm.data(), sizeof(NormTab) * n);
   if (!tfin.empty())
     std::memcpy(host.data() + plan->fin_off, tfin.data(), sizeof(FinTab) * tfin.size());
+  if (!tx16.empty())
+    std::memcpy(host.data() + plan->x16_off, tx16.data(), sizeof(EwTab) * tx16.size());
   if (!gtasks.empty())
     std::memcpy(host.data() + g_off, gtasks.data(), sizeof(GemmTab) * gtasks.size());
   if (!upload) {
@@ -835,7 +952,7 @@ thread_local Prof g_prof;
 
 const char* kKindNames[KIND_COUNT] = {"momentum", "input", "norm", "syrk", "poly",
                                       "update_x", "clip_norm", "clip_scale", "adamw",
-                                      "gram_mul"};
+                                      "gram_mul", "gram_x"};
 
 template <class F>
 hipError_t timed(int kind, double flops, double bytes, hipStream_t s, F&& launch) {
@@ -871,8 +988,10 @@ dmuon_status_t gram_group(const Plan& plan, int gid, const IterArgs& args, Bases
     if (gl.group != gid) continue;
     const GemmTab* tasks = reinterpret_cast<const GemmTab*>(tab + gl.off);
     const double bytes = args.fin != FIN_NONE ? gl.bytes_fin : gl.bytes;
+    const int h = plan.f32_ops ? 0 : 1;  // fp16 operands
     const hipError_t e = timed(gl.kind, gl.flops, bytes, s, [&] {
-      return launch_gemm(gl.kind, gl.tile, 1, gl.bk, 0, 0, tasks, gl.ntasks, gl.total, args, b, s);
+      return launch_gemm(gl.kind, gl.tile, plan.f32_ops, gl.bk, h, h, tasks, gl.ntasks, gl.total,
+                         args, b, s);
     });
     if (e != hipSuccess)
       return fail(DMUON_E_HIP, std::string("Gram NS product launch: ") + hipGetErrorString(e));
@@ -880,11 +999,18 @@ dmuon_status_t gram_group(const Plan& plan, int gid, const IterArgs& args, Bases
   return DMUON_OK;
 }
 
+// The iteration index the kernels see for window w.  Iteration 0 applies
+// the norm's scale (the SYRK by 1/(||u||+eps)^2, the X update by
+// 1/(||u||+eps)) and its X update reads X^T from xt0; with fp16 operands X
+// is normalized before the first window (gram16_x_kernel, which leaves X^T
+// in xt1), so the windows count from 1.
+int gram_iter(const Plan& plan, int w) { return plan.f32_ops ? w : w + 1; }
+
 // A = X X^T at the start of window w (window 0 scales by 1/(||u||+eps)^2
 // through the norm's scale, which is 1 for a shard until the group sum).
 dmuon_status_t gram_syrk(const Plan& plan, int w, Bases b, hipStream_t s) {
   IterArgs base{};
-  base.iter = w;
+  base.iter = gram_iter(plan, w);
   return gram_group(plan, GG_SYRK, base, b, s);
 }
 
@@ -895,7 +1021,7 @@ dmuon_status_t gram_window(const Plan& plan, const dmuon_ns_cfg_t* cfg,
                            const std::vector<int>& cuts, int w, int fin, float lr, float decay,
                            Bases b, hipStream_t s) {
   IterArgs base{};
-  base.iter = w;  // window 0's X update applies 1/(||u||+eps); X^T ping-pong
+  base.iter = gram_iter(plan, w);  // window 0's X update applies 1/(||u||+eps); X^T ping-pong
   dmuon_status_t st;
   bool q_in_a = true;  // the window's Q lives in Q_a
   for (int k = cuts[w]; k < cuts[w + 1]; ++k) {
@@ -928,6 +1054,15 @@ dmuon_status_t run_gram(const Plan& plan, const dmuon_ns_cfg_t* cfg, bool ns_onl
   const std::vector<int> cuts = gram_cuts(cfg);
   const int windows = (int)cuts.size() - 1;
   dmuon_status_t st;
+  if (!plan.f32_ops) {
+    const EwTab* tx = reinterpret_cast<const EwTab*>(static_cast<const char*>(plan.dtab) +
+                                                     plan.x16_off);
+    const hipError_t e = timed(KIND_GRAM_X, 0, plan.x16_bytes, s, [&] {
+      return launch_gram16_x(tx, plan.nmat, plan.x16_tiles, b, s);
+    });
+    if (e != hipSuccess)
+      return fail(DMUON_E_HIP, std::string("Gram fp16 X launch: ") + hipGetErrorString(e));
+  }
   for (int w = 0; w < windows; ++w) {
     if ((st = gram_syrk(plan, w, b, s))) return st;
     const int fin = w == windows - 1 ? (ns_only ? FIN_OUTPUT : FIN_UPDATE) : FIN_NONE;
@@ -1128,6 +1263,9 @@ dmuon_status_t check_local(const dmuon_ns_cfg_t* cfg, int32_t transposed) {
   if (cfg->backend != DMUON_NS_GRAM)
     return fail(DMUON_E_INVALID, "cfg: the shard entry points run Gram-space NS "
                                  "(backend DMUON_NS_GRAM)");
+  if (cfg->prec == DMUON_NS_F16)
+    return fail(DMUON_E_UNSUPPORTED, "cfg: Gram-space NS on shards runs with fp32 operands "
+                                     "(prec F32 or AUTO)");
   return DMUON_OK;
 }
 
@@ -1724,7 +1862,8 @@ int64_t dmuon_plan_builds(void) {
 }
 
 const char* dmuon_backend_info(void) {
-  return "direct NS (SYRK + symmetric poly + update-X) or Gram-space NS . gfx950 MFMA "
+  return "direct NS (SYRK + symmetric poly + update-X) or Gram-space NS (fp32 or fp16 "
+         "operands) . gfx950 MFMA "
          "bf16/fp16 32x32x16 (tiles 64/128/256) / fp32 32x32x2 (tiles 32/64/128) . "
          "fp32-grade master X . update fused into the last X product";
 }

@@ -22,7 +22,10 @@ enum Kind : int {
   KIND_CLIP_SCALE,    // gradient clipping: g <- g * factor
   KIND_ADAMW,         // AdamW update of non-Muon parameters
   KIND_GRAMMUL,       // Gram-space NS: a product of two commuting symmetric
-                      // p x p matrices (P A, P (P A), P Q), fp32 operands
+                      // p x p matrices (P A, P (P A), P Q), fp32 or fp16
+                      // operands
+  KIND_GRAM_X,        // Gram-space NS with fp16 operands: X normalized into
+                      // the fp16 operand layout
   KIND_COUNT
 };
 
@@ -109,7 +112,9 @@ struct GemmTaskT {
   A<uint16_t> xlo;         // UPDX, bf16 operands: X - bf16 X (stride ld0)
   A<const uint16_t> ahl;   // POLY with split A: A as [hi | lo | ...] rows
   int32_t ld_ahl;          // its row stride
-  int32_t pad0_;
+  // GRAMMUL with fp16 operands: the product is multiplied by g_in (undoing
+  // the operands' power-of-two scales) and stored times g_out
+  float g_in;
   A<void> sink;            // 16 writable, never-read bytes (see updx_final)
   // UPDX, last iteration: the caller's param (step) or output (NS only).
   // Oriented element (r, c), r < pv, c < qv, sits at dst[r*qv + c], or at
@@ -120,6 +125,8 @@ struct GemmTaskT {
   int32_t dst_dtype;
   int32_t add_diag;        // POLY (Gram-space P): add the iteration's a on the diagonal
   int32_t win;             // full product: tiles in column windows (see win_decode)
+  float g_out;
+  int32_t pad1_;
 };
 using GemmTask = GemmTaskT<Ptr>;
 using GemmTab = GemmTaskT<RefOf>;
@@ -250,12 +257,19 @@ hipError_t launch_gram_finalize(const FinTab* tasks, int ntasks, int nblocks, fl
                                 Bases b, hipStream_t s);
 hipError_t launch_norm(const NormTab* tasks, int ntasks, float eps, Bases b,
                        hipStream_t s);
-// kind in {KIND_SYRK, KIND_POLY, KIND_UPDX}; tile in {64, 128, 256}
+// Gram-space NS with fp16 operands, after the norm: the master X (bf16 hi +
+// remainder, or fp32) becomes X / (||u|| + eps) in the fp16 layout, with
+// its fp16 copy (xb) and fp16 X^T (xt).  Tiles of 64 x 64 over the oriented
+// padded P x Q.
+hipError_t launch_gram16_x(const EwTab* tasks, int ntasks, int total_tiles, Bases b,
+                           hipStream_t s);
+// kind in {KIND_SYRK, KIND_POLY, KIND_UPDX, KIND_GRAMMUL}; tile in {64, 128, 256}
 // (16-bit operands) or {64, 128} (fp32 operands); bk, the K depth of a
 // 16-bit main-loop stage: 64, or 128 for the 64-wide SYRK and polynomial
 // (every task's K then a multiple of 128).  h: operand format of the
 // products (0 bf16, 1 fp16); hn: format of the X copies an X update writes
-// for the next iteration (h, or 1 after a bf16 first iteration).
+// for the next iteration (h, or 1 after a bf16 first iteration).  GRAMMUL
+// with 16-bit operands: fp16 only (h = hn = 1).
 hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk, int h, int hn,
                        const GemmTab* tasks, int ntasks, int total_tiles,
                        const IterArgs& args, Bases b, hipStream_t s);

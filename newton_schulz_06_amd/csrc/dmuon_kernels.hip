@@ -275,6 +275,76 @@ __global__ __launch_bounds__(256) void norm_kernel(const NormTab* __restrict__ t
   }
 }
 
+// Gram-space NS with fp16 operands, once the norm is known: one 64 x 64
+// tile of the oriented, padded X per block.  Reads the master X as the input
+// pass left it (bf16 X + bf16 remainder, or fp32), scales it by
+// 1/(||u|| + eps), and writes it back as the fp16 operands read it: the
+// master as fp16 X + fp16 remainder times 2^11 (or fp32 beside an fp16
+// copy), and fp16 X^T through LDS.  The window products then see X in
+// fp16's normal range from the first SYRK on.
+__global__ __launch_bounds__(EW_THREADS) void gram16_x_kernel(const EwTab* __restrict__ tasks,
+                                                              int ntasks, int total_tiles,
+                                                              Bases bases) {
+  __shared__ float tile[EW_TILE][EW_TILE + 1];
+  const int gt = blockIdx.x;
+  if (gt >= total_tiles) return;
+  const EwTask T = resolve(tasks[find_task(tasks, ntasks, gt)], bases);
+  const int lt = gt - T.tile_begin;
+  const int r0 = (lt / T.tiles_c) * EW_TILE;
+  const int c0 = (lt % T.tiles_c) * EW_TILE;
+  const int tid = threadIdx.x;
+  const int cx = (tid & 15) * 4;
+  const int ry = tid >> 4;
+  const float s = ld_f32(T.scale);
+  const bool hilo = T.xlo != nullptr;
+  constexpr int RK = EW_TILE / 16;
+  constexpr float ls = Op16<1>::kLoScale;
+  f32x4 x[RK];
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
+    const size_t row = (size_t)(r0 + ry + 16 * k);
+    if (hilo) {
+      const f32x4 h = unpack_bf16x4(ld_u32x2(T.xb + row * T.ldxb + c0 + cx));
+      const f32x4 l = unpack_bf16x4(ld_u32x2(T.xlo + row * T.ldxb + c0 + cx));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[k][e] = h[e] + l[e];
+    } else {
+      x[k] = ld_f32x4(T.xm + row * T.ldx + c0 + cx);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
+    const int r = ry + 16 * k;
+    const size_t row = (size_t)(r0 + r);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = x[k][e] * s;
+      tile[r][cx + e] = v[e];
+    }
+    const u32x2 h4 = pack4<1>(v[0], v[1], v[2], v[3]);
+    st_u32x2(T.xb + row * T.ldxb + c0 + cx, h4);
+    if (hilo) {
+      const f32x4 hf = unpack4<1>(h4);
+      st_u32x2(T.xlo + row * T.ldxb + c0 + cx,
+               pack4<1>((v[0] - hf[0]) * ls, (v[1] - hf[1]) * ls, (v[2] - hf[2]) * ls,
+                        (v[3] - hf[3]) * ls));
+    } else {
+      st_f32x4(T.xm + row * T.ldx + c0 + cx, v);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
+    const int oc = ry + 16 * k;  // column of the tile = row of X^T
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = tile[cx + e][oc];
+    st_u32x2(static_cast<uint16_t*>(T.xt) + (size_t)(c0 + oc) * T.ldt + r0 + cx,
+             pack4<1>(v[0], v[1], v[2], v[3]));
+  }
+}
+
 // Gram NS on a shard, after the group sum: inv = 1/(sqrt(sumsq) + eps) as in
 // norm_kernel, A *= inv^2 (the same fp32 factor the SYRK epilogue applies
 // when the norm is known up front), and the scales for the X update.
@@ -493,11 +563,30 @@ __device__ __forceinline__ void sym_epilogue(const GemmTask& G, f32x16 (&acc)[NT
           }
         } else if constexpr (KIND == KIND_GRAMMUL) {
           // C = L R^T (L, R symmetric and commuting, so C is symmetric)
-          float* o0 = static_cast<float*>(G.out0);
-          const int ld0 = G.ld0;
+          if constexpr (F32) {
+            float* o0 = static_cast<float*>(G.out0);
+            const int ld0 = G.ld0;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) st_f32(o0 + (size_t)(gi + rr) * ld0 + gj, v[rr]);
-          if (mirror) st_f32x4(o0 + (size_t)gj * ld0 + gi, v);
+            for (int rr = 0; rr < 4; ++rr) st_f32(o0 + (size_t)(gi + rr) * ld0 + gj, v[rr]);
+            if (mirror) st_f32x4(o0 + (size_t)gj * ld0 + gi, v);
+          } else {
+            // fp16 operands: unscale; the fp32 C (upper tiles, for the
+            // polynomial's linear term) when asked for, and the fp16
+            // operand form times g_out, mirrored
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) v[rr] *= G.g_in;
+            if (F) {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) st_f32(F + (size_t)(gi + rr) * ldf + gj, v[rr]);
+            }
+            uint16_t* o0 = static_cast<uint16_t*>(G.out0);
+            const int ld0 = G.ld0;
+            const float go = G.g_out;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) st_u16(o0 + (size_t)(gi + rr) * ld0 + gj, Op16<H>::to(v[rr] * go));
+            if (mirror)
+              st_u32x2(o0 + (size_t)gj * ld0 + gi, pack4<H>(v[0] * go, v[1] * go, v[2] * go, v[3] * go));
+          }
         } else {  // KIND_POLY
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) v[rr] = fmaf(cb, av[j][g][rr], cc * v[rr]);
@@ -1504,6 +1593,13 @@ hipError_t launch_norm(const NormTab* tasks, int ntasks, float eps, Bases b, hip
   return hipGetLastError();
 }
 
+hipError_t launch_gram16_x(const EwTab* tasks, int ntasks, int total_tiles, Bases b,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(gram16_x_kernel, dim3(total_tiles), dim3(EW_THREADS), 0, s, tasks, ntasks,
+                     total_tiles, b);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk, int h, int hn,
                        const GemmTab* tasks, int ntasks, int total_tiles, const IterArgs& A,
                        Bases b, hipStream_t s) {
@@ -1517,8 +1613,11 @@ hipError_t launch_gemm(int kind, int tile, int f32_ops, int bk, int h, int hn,
     case KIND_UPDX:
       return launch_gemm_k<KIND_UPDX>(tile, f32_ops, bk, h, hn, tasks, ntasks, total_tiles, A, b,
                                       s);
-    case KIND_GRAMMUL:  // fp32 operands only
-      if (!f32_ops) return hipErrorInvalidValue;
+    case KIND_GRAMMUL:
+      if (!f32_ops) {  // fp16 operands only
+        if (h != 1 || hn != 1) return hipErrorInvalidValue;
+        return launch_gemm_h<KIND_GRAMMUL, 1, 1>(tile, bk, tasks, ntasks, total_tiles, A, b, s);
+      }
       if (tile == 64)
         return launch_gemm_f32<KIND_GRAMMUL, 64>(tasks, ntasks, total_tiles, A, b, s);
       if (tile == 128)

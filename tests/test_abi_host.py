@@ -105,6 +105,27 @@ def _expected_ws(shapes, prec):
     return a(4 * tiles) + a(16 * len(shapes)) + a(16) + a(24 * len(shapes)) + sum(per)
 
 
+def test_workspace_size_gram_fp16():
+    """Gram-space layout with fp16 operands: the direct fp16 layout's head
+    and per-matrix X buffers (master X: bf16 hi + remainder below 256-wide
+    tiles, else fp32 beside the 16-bit copy; two 16-bit X^T; fp32 A), then
+    five 16-bit P x P buffers (A's operand form, P, P A and the Q pair)."""
+    a = lambda x: _pad(x, 256)  # noqa: E731
+    shapes = [(1024, 256), (256, 1024), (100, 37), (700, 900), (4096, 1024)]
+    tiles, per = 0, 0
+    for m, n in shapes:
+        p, q = min(m, n), max(m, n)
+        t = _tile(p, "f16")
+        P, Q = _pad(p, max(t, 64)), _pad(q, max(t, 64))
+        tiles += (P // 64) * (Q // 64)
+        master = 2 * a(2 * P * _ld(Q, 2)) if t < 256 else a(2 * P * _ld(Q, 2)) + a(4 * P * _ld(Q, 4))
+        per += master + 2 * a(2 * Q * _ld(P, 2)) + a(4 * P * _ld(P, 4)) + 5 * a(2 * P * _ld(P, 2))
+    want = a(4 * tiles) + a(16 * len(shapes)) + a(16) + a(24 * len(shapes)) + per
+    assert dm.workspace_size(shapes, "f16", backend="gram") == want
+    assert dm.workspace_size(shapes, "f16", backend="gram") != dm.workspace_size(shapes, "f32",
+                                                                                  backend="gram")
+
+
 def test_workspace_size_gram():
     """Gram-space layout (fp32 operands): partials, scales, sink, pointer
     slots, then per
@@ -172,13 +193,51 @@ def _cfg_with(**fields):
     return cfg
 
 
-def test_gram_needs_fp32_operands():
+def test_gram_needs_fp32_or_fp16_operands():
     g, k1 = _mats([(64, 96, FAKE_G)])
     o, k2 = _mats([(64, 96, FAKE_O)])
-    for prec in ("bf16", "bf16_split", "bf16_split_a", "f16"):
+    for prec in ("bf16", "bf16_split", "bf16_split_a"):
         cfg = _keep_cfg(prec=prec, backend="gram")
         assert _call_ns(g, o, cfg) == dm.DMUON_E_UNSUPPORTED, _err()
-        assert "fp32" in _err()
+        assert "fp32" in _err() and "fp16" in _err()
+    # fp16 operands pass validation: the first HIP call is reached
+    cfg = _keep_cfg(prec="f16", backend="gram")
+    assert _call_ns(g, o, cfg) == dm.DMUON_E_HIP, _err()
+
+
+def test_gram_fp16_coefficient_bound():
+    """fp16 Gram NS stores P and Q times 2^10: coefficient tables whose
+    per-window bound on |Q| over eigenvalues in [0, 1.25] exceeds 48 are
+    rejected before any device work; the quintic (3.4445 per step, 40.9
+    over a three-step window) passes."""
+    g, k1 = _mats([(64, 96, FAKE_G)])
+    o, k2 = _mats([(64, 96, FAKE_O)])
+    quintic = [(3.4445, -4.7750, 2.0315)] * 5
+    cfg = _keep_cfg(prec="f16", backend="gram", coefficients=quintic)
+    assert _call_ns(g, o, cfg) == dm.DMUON_E_HIP, _err()
+    # four steps in one window: 3.4445^4 = 140.8 > 48
+    cfg = _keep_cfg(prec="f16", backend="gram", coefficients=quintic[:4], restart_iterations=[])
+    assert _call_ns(g, o, cfg) == dm.DMUON_E_UNSUPPORTED, _err()
+    assert "window 0" in _err()
+    # the same table split into windows of two: 11.9 each
+    cfg = _keep_cfg(prec="f16", backend="gram", coefficients=quintic[:4],
+                    restart_iterations=[2])
+    assert _call_ns(g, o, cfg) == dm.DMUON_E_HIP, _err()
+    # two quintic steps (11.9), then three steps of the constant 4 (64 > 48):
+    # only the second window trips
+    late = quintic[:2] + [(4.0, 0.0, 0.0)] * 3
+    cfg = _keep_cfg(prec="f16", backend="gram", coefficients=late)
+    assert _call_ns(g, o, cfg) == dm.DMUON_E_UNSUPPORTED, _err()
+    assert "window 1" in _err()
+    # 1 + 40 l (1 - l), 11 at l = 1/2 and -11.5 at l = 1.25: 11.5^2 = 132 > 48
+    # in window 0
+    bump = [(1.0, 40.0, -40.0)] * 5
+    cfg = _keep_cfg(prec="f16", backend="gram", coefficients=bump)
+    assert _call_ns(g, o, cfg) == dm.DMUON_E_UNSUPPORTED, _err()
+    assert "window 0" in _err()
+    # fp32 Gram NS takes any finite table
+    cfg = _keep_cfg(prec="f32", backend="gram", coefficients=bump)
+    assert _call_ns(g, o, cfg) == dm.DMUON_E_HIP, _err()
 
 
 def test_valid_call_reaches_the_device():
@@ -527,6 +586,7 @@ LOCAL_BAD = {
     "transposed 2": (dict(transposed=2), dm.DMUON_E_INVALID),
     "direct backend": (dict(cfg=dict(prec="f32")), dm.DMUON_E_INVALID),
     "bf16 operands": (dict(cfg=dict(prec="bf16", backend="gram")), dm.DMUON_E_UNSUPPORTED),
+    "fp16 operands": (dict(cfg=dict(prec="f16", backend="gram")), dm.DMUON_E_UNSUPPORTED),
     "window -1": (dict(fn="advance", window=-1), dm.DMUON_E_INVALID),
     "window past the last": (dict(fn="advance", window=2), dm.DMUON_E_INVALID),
     "one window only": (dict(fn="advance", window=1,
