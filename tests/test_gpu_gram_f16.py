@@ -75,16 +75,41 @@ def test_gram_f16_single_terms(table):
 
 
 @pytest.mark.parametrize("restarts", [None, [1, 3], [1, 2, 3, 4]])
-def test_gram_f16_quintic_matches_oracle(restarts):
+@pytest.mark.parametrize("coef", ["quintic", "you"])
+def test_gram_f16_matches_oracle(restarts, coef):
+    """Both coefficient tables (the YOU table's window bounds: 16.1 and 30.5
+    under the default restart).  Emulated with the YOU table: rectangular
+    shapes at most 1.9e-3, square ones up to 2.3e-2 with the default
+    restart and 2.8e-3 with [1, 3]."""
+    table = None if coef == "quintic" else oracle.YOU_COEFFICIENTS
     shapes = RECT + SQUARE
     gs_np = [_gen(s, 10 + i) for i, s in enumerate(shapes)]
-    gin, outs = _gram16(gs_np, restart_iterations=restarts)
+    gin, outs = _gram16(gs_np, coefficients=table, restart_iterations=restarts)
     for s, g, o in zip(shapes, gin, outs):
-        want = oracle.gram_newton_schulz(g, restart_iterations=restarts)
+        want = oracle.gram_newton_schulz(g, coefficients=table, restart_iterations=restarts)
         e = rel_frobenius(o, want)
         bound = 3e-2 if (s in SQUARE and restarts is None) else 1e-2
-        _say(f"restarts {restarts} {s}: relF {e:.2e} (bound {bound})")
-        assert e <= bound, (s, restarts, e)
+        _say(f"{coef} restarts {restarts} {s}: relF {e:.2e} (bound {bound})")
+        assert e <= bound, (s, restarts, coef, e)
+
+
+def test_gram_f16_edge_cases():
+    """A zero matrix (O = 0), one NS step (a single window with no factor
+    products), 16 steps (six windows under restarts every third step), and
+    an empty batch."""
+    g = torch.zeros(64, 200, device="cuda")
+    (o,) = dm.ns_orthogonalize([g], prec="f16", backend="gram")
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0
+    gs_np = [_gen(s, 60 + i) for i, s in enumerate([(100, 300), (520, 1100)])]
+    for steps, restarts in [(1, None), (16, [3, 6, 9, 12, 15])]:
+        gin, outs = _gram16(gs_np, ns_steps=steps, restart_iterations=restarts)
+        for g64, o64 in zip(gin, outs):
+            want = oracle.gram_newton_schulz(g64, steps=steps, restart_iterations=restarts)
+            e = rel_frobenius(o64, want)
+            _say(f"{steps} steps, restarts {restarts} {g64.shape}: relF {e:.2e}")
+            assert e <= 1e-2, (steps, e)
+    assert dm.ns_orthogonalize([], prec="f16", backend="gram") == []
 
 
 STAND_INS = [("gauss", (2048, 512), 8e-3), ("lowrank", (1024, 3584), 2.5e-2),
