@@ -9,8 +9,8 @@ the largest single-GPU batch, the 70B-class MLP matrices (4 of 28672 x 8192,
 2 of 8192 x 28672, bf16, Nesterov); ``--config 2`` runs the 4-layer TinyMLP
 of DMuon's Quick Start (d=512, ff=2048), ``--config 3`` the Llama-8B
 projections, ``--config 4`` the 512-matrix NS-only batch and ``--config 1``
-the fp32 TinyMLP.  ``--ns-backend gram``
-runs the Gram-space iteration with restarts instead (fp32 operands); the
+the fp32 TinyMLP.  ``--ns-backend gram`` runs the Gram-space iteration
+with restarts instead (fp32 operands, or fp16 with ``--ns-prec f16``); the
 value stays the direct method's algorithmic flops per second, so the two
 backends compare on the same work.
 

@@ -241,12 +241,13 @@ dmuon_status_t check_batch(const dmuon_batch_t* b, const char* name, bool need_p
 std::vector<int> gram_cuts(const dmuon_ns_cfg_t* cfg);
 
 // Gram-space NS with fp16 operands stores P times 2^10 and Q (a product of
-// a window's P's) times 2^10, so both must stay below 64 in magnitude.  The
-// eigenvalues of A stay within [0, 1.25] for NS coefficient schedules
-// (each step maps an eigenvalue l to l p(l)^2 of the contracting
-// polynomial), so max over that interval of |p_k(l)| bounds ||P_k|| and
-// the product over a window's steps bounds ||Q||.  Reject tables whose
-// bound exceeds 48 (the quintic: 3.44 per step, 41 over three steps).
+// a window's P's) times 2^10, so both must stay below 64 in magnitude.  A
+// starts with eigenvalues in [0, 1] (X is normalized by its Frobenius norm),
+// and a step maps an eigenvalue l to l p(l)^2, which NS schedules keep
+// within about [0, 1.2].  Over l in [0, 1.25], max |p_k(l)| then bounds
+// ||P_k||, and the product over a window's steps bounds ||Q||.  Tables whose
+// bound exceeds 48 are rejected (the quintic: 3.44 per step, 41 over three
+// steps).
 dmuon_status_t check_gram16_coeffs(const dmuon_ns_cfg_t* cfg) {
   const std::vector<int> cuts = gram_cuts(cfg);
   for (size_t w = 0; w + 1 < cuts.size(); ++w) {
@@ -431,11 +432,10 @@ bool vec_ok(const void* p, int dtype, int64_t n) {
 // Gram-space NS launch groups, appended to `gtasks`: one group per
 // (product, buffers), split by tile class like the direct kinds.  fp32
 // operands, or (h16) fp16 ones: X as normalized by gram16_x_kernel, A and
-// P A stored times kA16, P and Q times kB16 (the direct fp16 mode's A and B
-// scales, which its SYRK, polynomial and X-update epilogues apply), fp32
-// accumulation, and the fp32 A beside its fp16 form for the polynomial's
-// linear term.
-constexpr float kA16 = 4096.f, kB16 = 1024.f;
+// P A stored times kF16AScale, P and Q times kF16BScale (the direct fp16
+// mode's A and B scales, which its SYRK, polynomial and X-update epilogues
+// apply), fp32 accumulation, and the fp32 A beside its fp16 form for the
+// polynomial's linear term.
 void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, Plan* plan,
                        std::vector<GemmTab>& gtasks,
                        std::vector<std::pair<size_t, size_t>>& ranges) {
@@ -522,10 +522,12 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
       const D p = (D)G.p;
       f += p * p * (p + 1);
       if (h16) {
-        // L is P (times kB16); R is A or P A (kA16) or Q (kB16)
+        // L is P (times kF16BScale); R is A or P A (kF16AScale) or Q
+        // (kF16BScale)
         const bool r_is_q = mu.group == GG_Q_AB || mu.group == GG_Q_BA;
-        t.g_in = 1.f / (kB16 * (r_is_q ? kB16 : kA16));
-        t.g_out = r_is_q ? kB16 : kA16;
+        const float r_scale = r_is_q ? kF16BScale : kF16AScale;
+        t.g_in = 1.f / (kF16BScale * r_scale);
+        t.g_out = r_scale;
         if (mu.a_out) t.fbuf = wsr(G.a32);
         b += 6 * p * p + (mu.a_out ? 2 * p * (p + 1) : 0.0);
       } else {
@@ -565,10 +567,11 @@ void build_gram_groups(const Layout& L, const dmuon_batch_t* dst, bool ns_only, 
       t.sink = wsr(L.sink_off);
       const D p = (D)G.p, q = (D)G.q;
       f += 2 * p * p * q;
-      // Q, X^T, and the master X (read for the a X term); then the master X
-      // (fp16: 4 bytes as hi + remainder, or fp32 + fp16 copy) and X^T out
-      const D master_in = h16 ? 4.0 : 4.0, master_out = h16 ? (G.hilo ? 4.0 : 6.0) : 4.0;
-      const D in = e * p * p + p * q * (e + master_in);
+      // Q, X^T, and the master X (read for the a X term: fp32, or fp16 hi +
+      // remainder, 4 bytes either way); then the master X (fp16 operands:
+      // hi + remainder, or fp32 + fp16 copy) and X^T out
+      const D master_out = h16 ? (G.hilo ? 4.0 : 6.0) : 4.0;
+      const D in = e * p * p + p * q * (e + 4.0);
       b += in + p * q * (e + master_out);
       bfin += in + p * q * esize(dst->dtype) * (ns_only ? 1.0 : 2.0);
     });

@@ -54,6 +54,11 @@ constexpr int kSlotsPerMat = 3;
 template <class T> using Ptr = T*;
 template <class T> using RefOf = Ref;
 
+// Power-of-two scales of the fp16 operand forms (the kernels' Op16<1>): A
+// (and, in Gram-space NS, P A) is stored times kF16AScale, B (Gram-space: P
+// and Q) times kF16BScale; the consumers' epilogues divide them out, exactly.
+constexpr float kF16AScale = 4096.f, kF16BScale = 1024.f;
+
 // Element-wise tile size (original-layout tiles of EW_TILE x EW_TILE).
 constexpr int EW_TILE = 64;
 constexpr int EW_THREADS = 256;

@@ -21,6 +21,9 @@
 namespace dmuon {
 namespace {
 
+static_assert(Op16<1>::kAScale == kF16AScale && Op16<1>::kBScale == kF16BScale,
+              "the host's fp16 operand scales are the kernels'");
+
 // --------------------------------------------------------------------------
 // Launch tables hold Refs (see Bases): resolved once per block.
 template <class T>
