@@ -40,8 +40,10 @@ if not torch.cuda.is_available():
 
 import newton_schulz_06_amd as dm  # noqa: E402
 
+# 64-wide tiles up to p = 520, 128-wide at p = 800, 256-wide at p = 1000
+# (padded to 1024)
 RECT = [(100, 300), (300, 100), (1, 7), (7, 1), (257, 700), (700, 257), (520, 1100),
-        (800, 1200)]
+        (800, 1200), (3000, 1000)]
 SQUARE = [(64, 64), (33, 33), (129, 129)]
 
 
