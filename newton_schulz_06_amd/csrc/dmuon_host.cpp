@@ -36,15 +36,15 @@ size_t esize(int dtype) { return dtype == DMUON_F32 ? 4 : 2; }
 // GEMM tile classes (square T x T output tiles).  16-bit operands: the
 // largest of 256 (min side >= 1024) / 128 (>= 768) whose padding of the
 // min side stays within 1/8, else 64 -- small matrices are latency-bound and
-// want many small tiles.  fp32 operands: 32 up to 256 (direct NS only: the
-// 32-wide kernel splits K over its waves), 64 up to 512, 128 above.
+// want many small tiles.  fp32 operands: 16 up to 256 (direct NS only: the
+// 16-wide kernel splits K over its waves), 64 up to 512, 128 above.
 // Matrices are padded to multiples of max(T, 64) (the element-wise passes
 // work on 64 x 64 tiles).
-constexpr int kTiles[4] = {32, 64, 128, 256};
-int tile_index(int tile) { return tile == 32 ? 0 : tile == 64 ? 1 : tile == 128 ? 2 : 3; }
+constexpr int kTiles[4] = {16, 64, 128, 256};
+int tile_index(int tile) { return tile == 16 ? 0 : tile == 64 ? 1 : tile == 128 ? 2 : 3; }
 
 int tile_class(int64_t p, bool f32_ops, bool gram = false) {
-  if (f32_ops) return p <= 256 && !gram ? 32 : p <= 512 ? 64 : 128;
+  if (f32_ops) return p <= 256 && !gram ? 16 : p <= 512 ? 64 : 128;
   auto fits = [p](int64_t t) { return round_up(p, t) * 8 <= p * 9; };
   if (p >= 1024 && fits(256)) return 256;
   if (p >= 768 && fits(128)) return 128;
@@ -110,7 +110,7 @@ dmuon_status_t make_layout(const dmuon_batch_t* b, int prec, int backend, Layout
   L.local = local;
   // Gram-space NS: fp32 operands, or fp16 with DMUON_NS_F16 (not on shards)
   L.f32_ops = (prec == DMUON_NS_F32) || (L.gram && (prec != DMUON_NS_F16 || local));
-  // bits: tile_index (the 32-wide class has fp32 operands only)
+  // bits: tile_index (the 16-wide class has fp32 operands only)
   L.f16 = L.f32_ops ? 0 : prec == DMUON_NS_F16 ? 0xe : prec == DMUON_NS_AUTO ? 0x6 : 0;
   const int n = b->count;
   L.g.resize(n);
@@ -701,10 +701,10 @@ dmuon_status_t build_plan(const Layout& L, const dmuon_batch_t* src, const dmuon
         }
         if (deep) bk = 128;
       }
-      // The 32-wide class speeds the SYRK and polynomial (K split over the
+      // The 16-wide class speeds the SYRK and polynomial (K split over the
       // block's waves); its X updates run on 64-wide tiles (P and Q are
       // multiples of 64 for every class).
-      const int ltile = (kind == KIND_UPDX && tile == 32) ? 64 : tile;
+      const int ltile = (kind == KIND_UPDX && tile < 64) ? 64 : tile;
       const size_t begin = gtasks.size();
       int acc = 0;
       double flops = 0, bytes = 0, bytes_fin = 0;

@@ -269,7 +269,8 @@ hipError_t launch_norm(const NormTab* tasks, int ntasks, float eps, Bases b,
 hipError_t launch_gram16_x(const EwTab* tasks, int ntasks, int total_tiles, Bases b,
                            hipStream_t s);
 // kind in {KIND_SYRK, KIND_POLY, KIND_UPDX, KIND_GRAMMUL}; tile in {64, 128, 256}
-// (16-bit operands) or {64, 128} (fp32 operands); bk, the K depth of a
+// (16-bit operands) or {16 (SYRK and polynomial only), 64, 128} (fp32
+// operands); bk, the K depth of a
 // 16-bit main-loop stage: 64, or 128 for the 64-wide SYRK and polynomial
 // (every task's K then a multiple of 128).  h: operand format of the
 // products (0 bf16, 1 fp16); hn: format of the X copies an X update writes

@@ -1184,24 +1184,26 @@ __global__ __launch_bounds__(256) void gemm_reg_kernel(const GemmTab* __restrict
   epilogue<KIND, T, F32, NT>(G, acc, tm, tn, wr, wc, lane, A, nullptr);
 }
 
-// fp32 products of small matrices (direct NS, min side <= 256): 32 x 32
-// output tiles, so a launch has four times the blocks of 64-wide tiles (the
-// TinyMLP d=256 SYRK: 108 instead of 30 on 256 CUs; each 64-wide block is
-// bound by one CU's fp32 MFMA rate).  The block's 4 waves each take a
-// quarter of K, straight from global memory (the operands are L2-resident
-// at these sizes), and add their 32 x 32 partials through LDS in wave
-// order -- a fixed order, inside the block, so no device-scope
-// synchronization -- before wave 0 runs the tile's epilogue.  fp32 MFMA
-// 32x32x2: lane half h supplies k = k0 + 4h + t to instruction t of a
-// group of 4 (both operands, so the sum over k is complete).  K (the
-// task's padded extent, a multiple of 64) splits into 4 x 16-aligned
-// quarters.
+// fp32 SYRK and polynomial of small matrices (direct NS, min side <= 256)
+// on 16 x 16 output tiles, so a launch of a few small matrices spreads over
+// all CUs (the fp32 TinyMLP d=256: 408 blocks, against 30 of 64 x 64 and 108
+// of 32 x 32; each block is bound by one CU's fp32 MFMA rate).  The block's
+// 4 waves each take a quarter of K, straight from global memory (the
+// operands are L2-resident at these sizes), and add their partials through
+// LDS in wave order -- a fixed order, inside the block, so no device-scope
+// synchronization -- before wave 0 writes the tile.  fp32 MFMA 16x16x4:
+// lane quarter q supplies k = k0 + 4q + t to instruction t of a group of 4
+// (both operands); the output holds rows 4q + i (i < 4) of column lane %
+// 16.  K (the task's padded extent, a multiple of 64) splits into 4 x
+// 16-aligned quarters.  The SYRK writes the fp32 A (scaled on iteration 0)
+// and the polynomial B = b A + c A A^T, both mirrored on off-diagonal tiles.
 template <int KIND>
 __global__ __launch_bounds__(256) void gemm_f32_small_kernel(const GemmTab* __restrict__ tasks,
-                                                         int ntasks, int total_tiles, IterArgs A,
-                                                         Bases bases) {
-  constexpr int T = 32;
-  __shared__ f32x16 part[3][64];
+                                                        int ntasks, int total_tiles, IterArgs A,
+                                                        Bases bases) {
+  static_assert(KIND == KIND_SYRK || KIND == KIND_POLY, "SYRK and polynomial only");
+  constexpr int T = 16;
+  __shared__ f32x4 part[3][64];
   const int vb = xcd_remap(blockIdx.x, gridDim.x, total_tiles);
   if (vb >= total_tiles) return;
   const GemmTask G = resolve(tasks[find_task(tasks, ntasks, vb)], bases);
@@ -1214,29 +1216,51 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(const GemmTab* __re
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 31, h = lane >> 5;
+  const int r = lane & 15, q = lane >> 4;
   const float* lrow =
-      static_cast<const float*>(G.L) + ((size_t)tm * T + r) * G.ldl + 4 * h;
+      static_cast<const float*>(G.L) + ((size_t)tm * T + r) * G.ldl + 4 * q;
   const float* rrow = static_cast<const float*>((A.iter & 1) ? G.R1 : G.R0) +
-                      ((size_t)tn * T + r) * G.ldr + 4 * h;
+                      ((size_t)tn * T + r) * G.ldr + 4 * q;
   const int kq = G.K / 4;
   const int kper = G.kper;
-  f32x16 acc;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int k0 = wave * kq; k0 < (wave + 1) * kq; k0 += 8) {
+  for (int k0 = wave * kq; k0 < (wave + 1) * kq; k0 += 16) {
     const f32x4 a = ld_f32x4(lrow + k0);
     const f32x4 b = ld_f32x4(rrow + k0 % kper);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc, 0, 0, 0);
+    for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc, 0, 0, 0);
   }
   if (wave > 0) part[wave - 1][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
-  f32x16 tot[1][1];
-  tot[0][0] = ((acc + part[0][lane]) + part[1][lane]) + part[2][lane];
-  epilogue<KIND, T, true, 1>(G, tot, tm, tn, 0, 0, lane, A, nullptr);
+  f32x4 v = ((acc + part[0][lane]) + part[1][lane]) + part[2][lane];
+  const int row0 = tm * T + 4 * q;  // rows row0 .. row0 + 3
+  const int col = tn * T + r;
+  const bool mirror = G.tri && tm != tn;
+  float* F = G.fbuf;
+  const int ldf = G.ld_f;
+  float* dst = F;
+  int ld = ldf;
+  if constexpr (KIND == KIND_SYRK) {
+    const float s = A.iter == 0 ? G.scale[1] : 1.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= s;
+  } else {
+    f32x4 av;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av[i] = ld_f32(F + (size_t)(row0 + i) * ldf + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = fmaf(A.b, av[i], A.c * v[i]);
+      if (G.add_diag && row0 + i == col) v[i] += A.a;
+    }
+    dst = static_cast<float*>(G.out0);
+    ld = G.ld0;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st_f32(dst + (size_t)(row0 + i) * ld + col, v[i]);
+  if (mirror) st_f32x4(dst + (size_t)col * ld + row0, v);
 }
 
 // bf16 main loop fed by direct global->LDS loads (global_load_lds_dwordx4):
@@ -1515,11 +1539,14 @@ template <int KIND>
 hipError_t launch_gemm_k(int tile, int f32_ops, int bk, int h, int hn, const GemmTab* tasks,
                          int ntasks, int total_tiles, const IterArgs& A, Bases b, hipStream_t s) {
   if (f32_ops) {
-    if (tile == 32) {
-      const int grid = (total_tiles + 7) / 8 * 8;
-      hipLaunchKernelGGL((gemm_f32_small_kernel<KIND>), dim3(grid), dim3(256), 0, s, tasks,
-                         ntasks, total_tiles, A, b);
-      return hipGetLastError();
+    if (tile == 16) {
+      if constexpr (KIND == KIND_SYRK || KIND == KIND_POLY) {
+        const int grid = (total_tiles + 7) / 8 * 8;
+        hipLaunchKernelGGL((gemm_f32_small_kernel<KIND>), dim3(grid), dim3(256), 0, s, tasks,
+                           ntasks, total_tiles, A, b);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;
     }
     if (tile == 64) return launch_gemm_f32<KIND, 64>(tasks, ntasks, total_tiles, A, b, s);
     if (tile == 128) return launch_gemm_f32<KIND, 128>(tasks, ntasks, total_tiles, A, b, s);

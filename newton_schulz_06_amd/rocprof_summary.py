@@ -31,9 +31,9 @@ def short_name(name: str) -> str:
     m = re.search(r"dmuon::\(anonymous namespace\)::(\w+)(<[^>]*>)?", name)
     if m:
         kern, targs = m.group(1), m.group(2) or ""
-        if kern == "gemm_f32_small_kernel":  # <KIND>: 32 x 32 fp32 tiles
+        if kern == "gemm_f32_small_kernel":  # <KIND>: 16 x 16 fp32 tiles
             k = re.match(r"<(\d+)", targs)
-            return f"{KINDS.get(k.group(1), k.group(1))}[{kern}<T=32>]" if k else kern
+            return f"{KINDS.get(k.group(1), k.group(1))}[{kern}<T=16>]" if k else kern
         t = re.match(r"<(\d+), (\d+)(?:, (\d+))?(?:, (\d+), (\d+))?", targs)
         if t and kern.startswith("gemm"):
             bk = f",BK={t.group(3)}" if kern == "gemm_bf16_kernel" and t.group(3) not in (None, "64") else ""

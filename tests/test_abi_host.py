@@ -60,7 +60,7 @@ def _ld(n, esz):
 
 def _tile(p, prec, gram=False):
     if prec == "f32":
-        return 32 if p <= 256 and not gram else 64 if p <= 512 else 128
+        return 16 if p <= 256 and not gram else 64 if p <= 512 else 128
 
     def fits(t):
         return _pad(p, t) * 8 <= p * 9

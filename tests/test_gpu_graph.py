@@ -144,7 +144,7 @@ def test_graph_outlives_table_eviction():
 
 def test_gram_backend_graph_replays_bitwise():
     """A recorded Gram-space NS call (fp32 operands, restart windows) and a
-    recorded fp32 step on 32-wide tiles replay bit for bit what the direct
+    recorded fp32 step on 16-wide tiles replay bit for bit what the direct
     calls compute."""
     shapes = [(300, 120), (120, 500)]
     gs = [to_dev(workloads.grad_np("gauss", m, n, 74, 0, i), "f32") for i, (m, n) in enumerate(shapes)]

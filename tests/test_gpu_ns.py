@@ -257,7 +257,7 @@ def test_deep_stage_full_table():
 
 
 @pytest.mark.parametrize("shapes,prec,dtype,tol", [
-    # fp32 TinyMLP d=256: 30 SYRK and polynomial tiles per launch
+    # fp32 TinyMLP d=256: 408 SYRK and polynomial tiles of 16 x 16 per launch
     ([(1024, 256), (1024, 256), (256, 1024)], "f32", "f32", 1e-4),
     # one TinyMLP d=512 matrix, automatic precision
     ([(2048, 512)], "auto", "bf16", 2e-2),
