@@ -1867,7 +1867,8 @@ int64_t dmuon_plan_builds(void) {
 const char* dmuon_backend_info(void) {
   return "direct NS (SYRK + symmetric poly + update-X) or Gram-space NS (fp32 or fp16 "
          "operands) . gfx950 MFMA "
-         "bf16/fp16 32x32x16 (tiles 64/128/256) / fp32 32x32x2 (tiles 32/64/128) . "
+         "bf16/fp16 32x32x16 (tiles 64/128/256) / fp32 32x32x2 (tiles 64/128) and 16x16x4 "
+         "(tiles 16) . "
          "fp32-grade master X . update fused into the last X product";
 }
 
